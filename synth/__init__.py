@@ -1,0 +1,287 @@
+"""Seeded synthetic inputs for the routed MoE FFN layer.
+
+Shared by the tests, ``bench.py`` and ``__graft_entry__.smoke()``; imported by
+neither the oracle nor the HIP library.  It holds none of the layer's
+arithmetic: it draws random numbers, lays random bits into the byte fields of
+the two weight codecs, and builds the per-expert router bias that sets expert
+popularity.  Everything is a pure function of (seed, layer, tag), so the CPU
+can regenerate any expert of a GPU-resident layer bit for bit.
+
+Workloads (shapes of the model on the pages: 512 routed experts, 10 active,
+48 layers -- "Avalon" README, opening paragraphs; prefill chunks of 8192 and
+9536 tokens -- the speed tables of "Single RX 7900 XTX ..." section 5.1 and of
+the "Avalon" README, "Speed"):
+
+* tiny    H=256, E=16, k=2, I=128, no shared expert, T=4; router logits
+          given (fp32 N(0,1), distinct within a row); expert weights fp32
+          N(0, 0.02) to be encoded by a round-to-nearest quantiser.
+* decode  H=3072, E=512, k=10, I=512, one bf16 shared expert (I_s=512),
+          T in {1, 3, 8}; router W_r bf16 N(0, 0.02) [E][H] plus a per-expert
+          bias giving Zipf(1.0) popularity; experts by seeded code sampling.
+* stack   48 decode-shaped layers, T=3, RMSNorm gain N(1, 0.1), eps 1e-6.
+* prefill T=8192, decode shapes; Zipf(1.0) bias or no bias (uniform).
+
+Code sampling (how expert bytes are drawn at real shape): every byte of an
+expert record is a counter-hash output, then the fields that must hold a
+particular range are overwritten bit-wise --
+  Q3S-256 block: index bytes [0,96) stay uniform random (every bit pattern is
+  a valid index stream); d (bytes 96..97) = 0x2000 | 10 random bits, i.e. a
+  binary16 in [2^-7, 2^-6), the scale a round-to-nearest encoding of
+  N(0, 0.02) weights produces; sub-scale bytes 98..101 get nibbles 4..7
+  ("rtn" mode, the range round-to-nearest gives) or any nibble ("full" mode,
+  negative sub-scales included); bytes 102..103 = 0.
+  NL4-32 block: d (bytes 0..1) = 0x2800 | 10 random bits, a binary16 in
+  [2^-5, 2^-4); index bytes uniform random.
+The counter hash is MurmurHash3's 32-bit finaliser (fmix32, Austin Appleby,
+public domain), applied twice with per-(seed, layer, expert) keys.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+# --------------------------------------------------------------------------
+# shapes
+# --------------------------------------------------------------------------
+
+Q3S_BLOCK_BYTES = 104     # field widths of the codecs (byte layout only)
+NL4_BLOCK_BYTES = 18
+
+# Router-bias strength.  b_e = -ZIPF_ALPHA * s * ln(rank_e).  Chosen once by
+# bisection on the 8192-token prefill workload (seed 3, s = 1.0) so that the
+# hottest expert receives about 100x the tokens of the coldest; see the design
+# notes for the measured histogram.
+ZIPF_ALPHA = 0.40
+
+
+@dataclass(frozen=True)
+class Shape:
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+    shared_inter: int          # 0 = no shared expert
+
+    @property
+    def upgate_bytes(self):
+        return 2 * self.inter * (self.hidden // 256) * Q3S_BLOCK_BYTES
+
+    @property
+    def down_bytes(self):
+        return self.hidden * (self.inter // 32) * NL4_BLOCK_BYTES
+
+    @property
+    def expert_bytes(self):
+        return self.upgate_bytes + self.down_bytes
+
+
+TINY = Shape(hidden=256, inter=128, n_experts=16, top_k=2, shared_inter=0)
+REAL = Shape(hidden=3072, inter=512, n_experts=512, top_k=10, shared_inter=512)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: Shape
+    tokens: tuple
+    layers: int = 1
+    zipf_s: float = 1.0
+    seed: int = 0
+    note: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", TINY, (4,), seed=1, zipf_s=0.0,
+                     note="logits given; RTN-quantised N(0,0.02) experts"),
+    "decode": Workload("decode", REAL, (1, 3, 8), seed=2),
+    "stack": Workload("stack", REAL, (3,), layers=48, seed=4),
+    "prefill": Workload("prefill", REAL, (8192,), seed=3),
+    "prefill_uniform": Workload("prefill_uniform", REAL, (8192,), seed=3, zipf_s=0.0),
+}
+
+
+# --------------------------------------------------------------------------
+# counter hash (MurmurHash3 fmix32) on int64 tensors holding 32-bit values
+# --------------------------------------------------------------------------
+
+_M32 = 0xFFFFFFFF
+
+
+def _mul32(a, c):
+    """(a * c) mod 2^32 for int64 tensors a < 2^32 and a constant c < 2^32,
+    split in 16-bit halves so no intermediate leaves int64 range."""
+    lo = a * (c & 0xFFFF)
+    hi = ((a * (c >> 16)) & 0xFFFF) << 16
+    return (lo + hi) & _M32
+
+
+def fmix32(x):
+    x = x & _M32
+    x = x ^ (x >> 16)
+    x = _mul32(x, 0x85EBCA6B)
+    x = x ^ (x >> 13)
+    x = _mul32(x, 0xC2B2AE35)
+    return x ^ (x >> 16)
+
+
+def _fmix32_int(x):
+    return int(fmix32(torch.tensor([x & _M32], dtype=torch.int64))[0])
+
+
+def key(seed, layer, tag):
+    """32-bit key of (seed, layer, tag)."""
+    k = _fmix32_int(seed * 0x9E3779B9 + 0x7F4A7C15)
+    k = _fmix32_int(k ^ (layer * 0x632BE59B + 0x1B873593))
+    return _fmix32_int(k ^ (tag * 0xCC9E2D51 + 0x2545F491))
+
+
+def hash_words(k1, k2, n, device="cpu", start=0):
+    """n 32-bit words fmix32(fmix32(i + k1) ^ k2), i = start .. start+n-1,
+    as an int64 tensor."""
+    i = torch.arange(start, start + n, dtype=torch.int64, device=device)
+    return fmix32(fmix32(i + k1) ^ k2)
+
+
+def hash_bytes(k1, k2, nbytes, device="cpu"):
+    """nbytes pseudo-random bytes (little-endian words of hash_words)."""
+    nw = (nbytes + 3) // 4
+    w = hash_words(k1, k2, nw, device).to(torch.int32)   # wraps to int32
+    return w.view(torch.uint8)[:nbytes]
+
+
+# --------------------------------------------------------------------------
+# expert records by code sampling
+# --------------------------------------------------------------------------
+
+def _fix_q3s_fields(blk, mode):
+    """blk: uint8 [n, 104] view; set d, sub-scale and reserved fields."""
+    blk[:, 97] = (blk[:, 97] & 0x03) | 0x20
+    if mode == "rtn":
+        blk[:, 98:102] = (blk[:, 98:102] & 0x33) | 0x44
+    elif mode != "full":
+        raise ValueError("mode must be 'rtn' or 'full'")
+    blk[:, 102:104] = 0
+
+
+def _fix_nl4_fields(blk):
+    blk[:, 1] = (blk[:, 1] & 0x03) | 0x28
+
+
+def expert_record(shape, seed, layer, e, device="cpu", mode="rtn"):
+    """Packed bytes (uint8 [expert_bytes]) of expert e of a layer."""
+    k1 = key(seed, layer, 2 * e + 1)
+    k2 = key(seed, layer, 2 * e + 2)
+    rec = hash_bytes(k1, k2, shape.expert_bytes, device).clone()
+    _fix_q3s_fields(rec[:shape.upgate_bytes].view(-1, Q3S_BLOCK_BYTES), mode)
+    _fix_nl4_fields(rec[shape.upgate_bytes:].view(-1, NL4_BLOCK_BYTES))
+    return rec
+
+
+def expert_bank(shape, seed, layer, device="cpu", mode="rtn", chunk=64):
+    """All E expert records of a layer: uint8 [E][expert_bytes] on `device`.
+    Rows are generated in chunks of experts to bound temporary memory."""
+    E, nb = shape.n_experts, shape.expert_bytes
+    out = torch.empty((E, nb), dtype=torch.uint8, device=device)
+    for e in range(E):
+        out[e] = expert_record(shape, seed, layer, e, device, mode)
+    return out
+
+
+# --------------------------------------------------------------------------
+# dense inputs
+# --------------------------------------------------------------------------
+
+def _gen(seed, layer, tag):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(key(seed, layer, 1_000_000 + tag))
+    return g
+
+
+def normal_bf16(rows, cols, std, seed, layer, tag):
+    """bf16 tensor [rows][cols] ~ N(0, std^2), drawn in fp32 on the CPU and
+    converted by torch (round to nearest even)."""
+    g = _gen(seed, layer, tag)
+    return (torch.randn((rows, cols), generator=g, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def tokens_bf16(T, hidden, seed, layer=0, tag=0):
+    """Activations x: bf16 [T][H] ~ N(0,1)."""
+    return normal_bf16(T, hidden, 1.0, seed, layer, 10 + tag)
+
+
+def unique_logits(T, E, seed, layer=0):
+    """fp32 [T][E] ~ N(0,1) with all values of a row distinct (a row with a
+    repeat is drawn again)."""
+    g = _gen(seed, layer, 20)
+    out = torch.empty((T, E), dtype=torch.float32)
+    for t in range(T):
+        while True:
+            row = torch.randn(E, generator=g, dtype=torch.float32)
+            if torch.unique(row).numel() == E:
+                out[t] = row
+                break
+    return out
+
+
+def router_weight(shape, seed, layer):
+    """W_r: bf16 [E][H] ~ N(0, 0.02)."""
+    return normal_bf16(shape.n_experts, shape.hidden, 0.02, seed, layer, 30)
+
+
+def zipf_bias(E, s, seed, layer, alpha=ZIPF_ALPHA):
+    """fp32 [E]: b_e = -alpha * s * ln(rank_e), ranks a seeded permutation
+    of 1..E (so the hot experts are not the low indices that ties favour)."""
+    if s == 0.0:
+        return torch.zeros(E, dtype=torch.float32)
+    rng = np.random.default_rng(key(seed, layer, 40))
+    rank = rng.permutation(E) + 1
+    return torch.from_numpy((-alpha * s * np.log(rank)).astype(np.float32))
+
+
+def shared_weights(shape, seed, layer):
+    """Shared expert: (up|gate bf16 [2 I_s][H], down bf16 [H][I_s]) ~ N(0, 0.02)."""
+    ug = normal_bf16(2 * shape.shared_inter, shape.hidden, 0.02, seed, layer, 50)
+    dn = normal_bf16(shape.hidden, shape.shared_inter, 0.02, seed, layer, 51)
+    return ug, dn
+
+
+def norm_gain(hidden, seed, layer):
+    """RMSNorm gain gamma: fp32 [H] ~ N(1, 0.1)."""
+    g = _gen(seed, layer, 60)
+    return 1.0 + 0.1 * torch.randn(hidden, generator=g, dtype=torch.float32)
+
+
+def tiny_expert_weights(shape, seed, layer=0):
+    """fp32 N(0, 0.02) expert weights of the tiny workload, to be encoded by a
+    round-to-nearest quantiser: (up|gate [E][2I][H], down [E][H][I])."""
+    g = _gen(seed, layer, 70)
+    ug = torch.randn((shape.n_experts, 2 * shape.inter, shape.hidden), generator=g) * 0.02
+    dn = torch.randn((shape.n_experts, shape.hidden, shape.inter), generator=g) * 0.02
+    return ug, dn
+
+
+@dataclass
+class Layer:
+    """One layer's inputs (torch tensors on one device)."""
+    shape: Shape
+    experts: torch.Tensor                 # uint8 [E][expert_bytes]
+    router_w: torch.Tensor = None         # bf16 [E][H]
+    router_b: torch.Tensor = None         # fp32 [E]
+    shared_ug: torch.Tensor = None        # bf16 [2 I_s][H]
+    shared_down: torch.Tensor = None      # bf16 [H][I_s]
+    seed: int = 0
+    layer: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+def real_layer(shape, seed, layer, zipf_s=1.0, device="cpu", mode="rtn", experts=True):
+    """A real-shape layer: code-sampled experts, router, Zipf bias, shared expert."""
+    ex = expert_bank(shape, seed, layer, device, mode) if experts else None
+    ug, dn = shared_weights(shape, seed, layer) if shape.shared_inter else (None, None)
+    return Layer(shape=shape, experts=ex,
+                 router_w=router_weight(shape, seed, layer).to(device),
+                 router_b=zipf_bias(shape.n_experts, zipf_s, seed, layer).to(device),
+                 shared_ug=None if ug is None else ug.to(device),
+                 shared_down=None if dn is None else dn.to(device),
+                 seed=seed, layer=layer)
