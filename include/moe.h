@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the routed, block-quantized Mixture-of-Experts
+ * FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources: "Avalon" README, opening paragraphs -- each token goes to
+ * 10 of 512 experts, 48 layers; "Qwen3.8-Flash-Next - Avalon GGUF" model card,
+ * "Files / Main model" -- routers and shared experts in the dense part, routed
+ * up/gate in a 3.25-bpw type with a scale per 256-weight block and per-32
+ * sub-scales, down in a 4-bit non-linear 32-weight type, experts packed
+ * up | gate | down; "Betelgeuse" post (2026-11-01) -- every routed expert is
+ * computed exactly, no gate pruning):
+ *
+ *   L[t][e]  = sum_h x[t][h] * W_r[e][h] + b[e]                 (router)
+ *   ids[t]   = the k largest L[t][.], by (value desc, index asc)
+ *   w[t][j]  = softmax over the k selected logits
+ *   a        = bf16_rne( silu(W_gate x) * (W_up x) )              (per slot)
+ *   o        = W_down a                                           (per slot)
+ *   y[t]     = sum_j w[t][j] * o[t,j]  +  shared_expert(x[t])
+ *
+ * Conventions for every function below
+ *   - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *     allocates and frees every buffer, the workspace included; the library
+ *     never allocates or frees device memory and keeps no state except a cache
+ *     of device properties.  Calls are re-entrant; concurrent calls need
+ *     distinct workspaces and outputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on it; no call synchronises the host.
+ *   - All argument checks (null pointers, shapes, formats, alignment,
+ *     workspace size, device architecture) run on the host BEFORE any launch.
+ *     On failure the call returns a non-zero moe_status, launches nothing and
+ *     leaves every output untouched; moe_last_error() then holds a message.
+ *     A failed launch returns MOE_ERR_HIP.  Faults inside a kernel are
+ *     asynchronous and surface at the caller's next synchronisation.
+ *   - Element types: bf16 and fp16 are passed as uint16_t bit patterns.
+ *   - Preconditions not checked on the device: expert ids given to
+ *     moe_permute lie in [0, E); logits are not NaN; weight scales d are
+ *     finite; activations x satisfy |x| <= 65504 (the matrix-core path takes
+ *     x as fp16; bf16 values in that range convert exactly down to 2^-17 and
+ *     lose at most 2^-25 absolute below it).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,       /* a required pointer is NULL                     */
+    MOE_ERR_SHAPE = 2,      /* a size is out of the supported range           */
+    MOE_ERR_FORMAT = 3,     /* unknown or unsupported weight format           */
+    MOE_ERR_ALIGN = 4,      /* a pointer or stride is not 16-byte aligned     */
+    MOE_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required        */
+    MOE_ERR_DEVICE = 6,     /* current device is not gfx950                   */
+    MOE_ERR_HIP = 7         /* a HIP runtime call or kernel launch failed     */
+} moe_status;
+
+/* Weight formats.
+ *  MOE_FMT_BF16    plain bf16, row-major [out][in].
+ *  MOE_FMT_Q3S256  3.25-bpw super-blocks of 256 weights, 104 bytes each:
+ *                  bytes [0,96) 256 3-bit codebook indices as one little-endian
+ *                  bit stream (weight i at bits 3i..3i+2); [96,98) fp16 scale d
+ *                  (little-endian, any finite value, subnormals included);
+ *                  [98,102) eight signed 4-bit sub-scales s_j (bits 4j..4j+3
+ *                  of that little-endian u32, two's complement); [102,104)
+ *                  reserved (ignored).  w_i = d * s_{i/32} * C3[q_i] / 128 with
+ *                  C3 = {-127,-67,-31,0,23,48,78,127}.  (Model card, "Files /
+ *                  Main model": 3.25 bpw, a scale per 256-weight block,
+ *                  sub-scales per 32 weights.)
+ *  MOE_FMT_NL4_32  4-bit non-linear 32-weight blocks, 18 bytes each: [0,2)
+ *                  fp16 d; [2,18) 32 4-bit indices, even weight in the low
+ *                  nibble.  w_i = d * T4[q_i] / 128 with T4 = {-127,-88,-66,
+ *                  -50,-36,-23,-11,0,10,20,31,43,56,71,91,127}.  (Model card,
+ *                  "Files / Main model": IQ4_NL down tensors.)
+ * Matrices are stored [out rows][in] with blocks along the input dimension. */
+typedef enum {
+    MOE_FMT_BF16 = 1,
+    MOE_FMT_Q3S256 = 2,
+    MOE_FMT_NL4_32 = 3
+} moe_format;
+
+/* Layer shape.  Supported: hidden % 256 == 0 (and <= 16384); inter % 64 == 0
+ * (and <= 4096); 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
+ * shared_inter == 0 (no shared expert) or shared_inter % 64 == 0 (<= 4096);
+ * upgate_fmt == MOE_FMT_Q3S256 and down_fmt == MOE_FMT_NL4_32 for the routed
+ * experts (the shared expert and the router are always bf16). */
+typedef struct {
+    int32_t hidden;        /* H                                              */
+    int32_t inter;         /* I, routed expert intermediate size             */
+    int32_t n_experts;     /* E                                              */
+    int32_t top_k;         /* k                                              */
+    int32_t shared_inter;  /* I_s, 0 = no shared expert                      */
+    int32_t upgate_fmt;    /* moe_format of the routed up|gate matrices      */
+    int32_t down_fmt;      /* moe_format of the routed down matrices         */
+} moe_layer_desc;
+
+/* Layer weights (device pointers).  Each routed expert e is one record at
+ * experts + e*expert_stride: its up|gate matrix [2I][H] (rows 0..I-1 = up,
+ * I..2I-1 = gate; model card: "up | gate | down contiguous"), immediately
+ * followed by its down matrix [H][I].  `experts` and `expert_stride` must be
+ * 16-byte aligned and expert_stride >= the record size. */
+typedef struct {
+    const void*  experts;        /* E packed records                           */
+    int64_t      expert_stride;  /* bytes between records                      */
+    const void*  router_w;       /* bf16 [E][H], or NULL if logits are given   */
+    const float* router_b;       /* fp32 [E], or NULL (no bias)                */
+    const void*  shared_upgate;  /* bf16 [2*I_s][H] (up rows, then gate rows)  */
+    const void*  shared_down;    /* bf16 [H][I_s]                              */
+} moe_layer_weights;
+
+/* Bytes of workspace moe_layer_forward / moe_expert_ffn / moe_permute need for
+ * any T <= T_max.  Host-only, pure; returns 0 for an invalid desc/T_max. */
+size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max);
+
+/* Router logits (A1): logits[t][e] = sum_h x[t][h] * W_r[e][h] + b[e], fp32
+ * accumulation.  x bf16 [T][H], w_r bf16 [E][H], b fp32 [E] or NULL, logits
+ * fp32 [T][E].  Same kernels moe_layer_forward runs.  Needs ws (>=
+ * moe_workspace_size with the same H, E and T).
+ * Reading: the pages place "routers" in the dense part (model card, "Files /
+ * Main model") and give no formula; a linear router with a per-expert bias. */
+moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
+                             const uint16_t* w_r, const float* b, float* logits,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Top-k routing (A2).  logits fp32 [T][E] -> topk_ids int32 [T][k] (by
+ * descending logit, ties to the lower index) and topk_w fp32 [T][k] = softmax
+ * of the selected logits.  No capacity limit, nothing dropped ("Betelgeuse":
+ * every one of the routed experts is computed).  1 <= k <= min(E, 32),
+ * E <= 1024, T >= 1. */
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Counting-sort permutation (A3).  topk_ids int32 [T][k] (values in [0,E)) ->
+ * offsets int32 [E+1] (expert e owns permuted rows offsets[e]..offsets[e+1]-1,
+ * offsets[E] = T*k), perm int32 [T*k] (permuted row p holds flat slot
+ * f = t*k + j; stable: ascending f within an expert) and inv_perm int32 [T*k]
+ * (inv_perm[perm[p]] = p).  Bit-exact and deterministic. */
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs (A4-A7).  For every permuted row p of expert e (token
+ * t = perm[p] / k): y_perm[p] = W_down[e] bf16_rne(silu(W_gate[e] x[t]) *
+ * W_up[e] x[t]), unweighted, fp32 [T*k][H].  If shared_y is not NULL and
+ * desc->shared_inter > 0 the shared expert's output for every token is
+ * written to shared_y fp32 [T][H].  x bf16 [T][H]; offsets/perm as produced by
+ * moe_permute (the library also rebuilds its internal tile list from them). */
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                          const uint16_t* x, int32_t T, const int32_t* offsets,
+                          const int32_t* perm, float* y_perm, float* shared_y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine (A8): y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k+j]]
+ * (+ shared_y[t] if not NULL), summed in j order, fp32 [T][H]. */
+moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       int32_t T, int32_t k, int32_t H, const float* shared_y,
+                       float* y, void* stream);
+
+/* The whole layer (A1-A8): y fp32 [T][H] from x bf16 [T][H].  If
+ * logits_or_null is given (fp32 [T][E]) the router is skipped.  Optional
+ * outputs: topk_ids_out int32 [T][k], topk_w_out fp32 [T][k].  Tokens T <= 16
+ * take the bandwidth path (matrix-core GEMV, weights streamed once), larger T
+ * the grouped-GEMM path; both compute the same function. */
+moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                             const uint16_t* x, int32_t T, const float* logits_or_null,
+                             float* y, int32_t* topk_ids_out, float* topk_w_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Helper, not the method: dequantize n_weights weights of one format (a whole
+ * number of blocks, contiguous) to fp32 `out`, with the same device decoders
+ * the FFN kernels inline.  Exact: equal bit for bit to d*s*c/128 (Q3S256) or
+ * d*t/128 (NL4_32).  blocks must be 16-byte aligned. */
+moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
+                          void* stream);
+
+/* Helper for stacked layers (A9, pre-norm residual): if delta is not NULL,
+ * h += delta; then, if gamma and normed_bf16_out are not NULL,
+ * normed[t] = bf16_rne(gamma * h[t] / sqrt(mean(h[t]^2) + eps)).  h fp32 [T][H]
+ * (updated in place), delta fp32 [T][H], gamma fp32 [H], normed bf16 [T][H]. */
+moe_status moe_rmsnorm_residual(float* h, const float* delta, const float* gamma, float eps,
+                                int32_t T, int32_t H, uint16_t* normed_bf16_out, void* stream);
+
+/* Static description of a status code (host). */
+const char* moe_status_string(moe_status s);
+/* Detail of the last failure on the calling thread (host; "" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

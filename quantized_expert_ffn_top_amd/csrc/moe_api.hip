@@ -1,0 +1,399 @@
+// C ABI of libmoe.so (declared in include/moe.h): argument checks, workspace
+// carving and the enqueue order of the kernels.  No call allocates device
+// memory, frees it, or synchronises the host.
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+// ---- device check (cached per device id)
+std::mutex g_dev_mu;
+int g_dev_ok[64];   // 0 unknown, 1 gfx950, 2 other
+
+moe_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device id out of range");
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess)
+            return fail(MOE_ERR_HIP, "hipGetDeviceProperties failed");
+        g_dev_ok[dev] = (std::string(p.gcnArchName).rfind("gfx950", 0) == 0) ? 1 : 2;
+    }
+    if (g_dev_ok[dev] != 1) return fail(MOE_ERR_DEVICE, "current device is not gfx950");
+    return MOE_OK;
+}
+
+moe_status launched(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return MOE_OK;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int kMaxT = 1 << 18;
+
+size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ---- workspace layout for one (shape, T)
+struct Ws {
+    size_t x16, part, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm, y_sh,
+        hist, total;
+    int max_tiles;
+};
+
+int max_tiles_for(int T, int E, int k) {
+    const int n = T * k;
+    if (T <= kDecMaxT) return n < E ? n : E;
+    return (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
+}
+
+Ws layout(int H, int I, int E, int k, int Is, int T) {
+    Ws s{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += a256(bytes);
+        return o;
+    };
+    const size_t n = (size_t)T * k;
+    const int tdec = T < kDecMaxT ? T : kDecMaxT;
+    s.max_tiles = max_tiles_for(T, E, k);
+    s.x16 = take((size_t)T * H * 2);
+    s.part = take((size_t)(H / kRouterKChunk) * tdec * E * 4);
+    s.logits = take((size_t)T * E * 4);
+    s.ids = take(n * 4);
+    s.w = take(n * 4);
+    s.offsets = take((size_t)(E + 1) * 4);
+    s.perm = take(n * 4);
+    s.inv = take(n * 4);
+    s.tiles = take((size_t)s.max_tiles * 12);
+    s.ntiles = take(4);
+    s.a16 = take(n * I * 2);
+    s.a_sh = take((size_t)T * (Is > 0 ? Is : 1) * 2);
+    s.y_perm = take(n * H * 4);
+    s.y_sh = take((size_t)T * H * 4);
+    s.hist = take((size_t)((T + 63) / 64) * E * 4);
+    s.total = off;
+    return s;
+}
+
+moe_status check_desc(const moe_layer_desc* d) {
+    if (!d) return fail(MOE_ERR_NULL, "desc is NULL");
+    if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256)
+        return fail(MOE_ERR_SHAPE, "hidden must be a multiple of 256 in [256, 8192]");
+    if (d->inter < 64 || d->inter > 4096 || d->inter % 64)
+        return fail(MOE_ERR_SHAPE, "inter must be a multiple of 64 in [64, 4096]");
+    if (d->n_experts < 1 || d->n_experts > 1024)
+        return fail(MOE_ERR_SHAPE, "n_experts must be in [1, 1024]");
+    if (d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts)
+        return fail(MOE_ERR_SHAPE, "top_k must be in [1, min(n_experts, 32)]");
+    if (d->shared_inter < 0 || d->shared_inter > 4096 || d->shared_inter % 64)
+        return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64 <= 4096");
+    if (d->upgate_fmt != MOE_FMT_Q3S256 || d->down_fmt != MOE_FMT_NL4_32)
+        return fail(MOE_ERR_FORMAT, "routed experts must be Q3S256 up|gate and NL4_32 down");
+    return MOE_OK;
+}
+
+int64_t record_bytes(const moe_layer_desc* d) {
+    return (int64_t)2 * d->inter * (d->hidden / 256) * 104 + (int64_t)d->hidden * (d->inter / 32) * 18;
+}
+
+moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w, bool need_router,
+                         bool need_shared) {
+    if (!w) return fail(MOE_ERR_NULL, "weights is NULL");
+    if (!w->experts) return fail(MOE_ERR_NULL, "weights->experts is NULL");
+    if (!al16(w->experts) || (w->expert_stride & 15))
+        return fail(MOE_ERR_ALIGN, "experts and expert_stride must be 16-byte aligned");
+    if (w->expert_stride < record_bytes(d))
+        return fail(MOE_ERR_SHAPE, "expert_stride is smaller than one expert record");
+    if (need_router) {
+        if (!w->router_w) return fail(MOE_ERR_NULL, "router_w is NULL and no logits given");
+        if (!al16(w->router_w)) return fail(MOE_ERR_ALIGN, "router_w must be 16-byte aligned");
+        if (w->router_b && !al4(w->router_b)) return fail(MOE_ERR_ALIGN, "router_b misaligned");
+    }
+    if (need_shared) {
+        if (!w->shared_upgate || !w->shared_down)
+            return fail(MOE_ERR_NULL, "shared_inter > 0 but shared weights are NULL");
+        if (!al16(w->shared_upgate) || !al16(w->shared_down))
+            return fail(MOE_ERR_ALIGN, "shared weights must be 16-byte aligned");
+    }
+    return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+size_t permute_ws_bytes(int T, int k, int E) {
+    if (T <= kDecMaxT) return 0;
+    const int mt = max_tiles_for(T, E, k);
+    return a256((size_t)((T + 63) / 64) * E * 4) + a256((size_t)mt * 12) + 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "null pointer";
+        case MOE_ERR_SHAPE: return "unsupported shape";
+        case MOE_ERR_FORMAT: return "unsupported weight format";
+        case MOE_ERR_ALIGN: return "misaligned pointer or stride";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_DEVICE: return "device is not gfx950";
+        case MOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max) {
+    if (check_desc(desc) != MOE_OK || T_max < 1 || T_max > kMaxT) return 0;
+    return layout(desc->hidden, desc->inter, desc->n_experts, desc->top_k, desc->shared_inter, T_max).total;
+}
+
+moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
+                             const uint16_t* w_r, const float* b, float* logits, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!x || !w_r || !logits) return fail(MOE_ERR_NULL, "x, w_r and logits must be non-NULL");
+    if (T < 1 || T > kMaxT || H < 256 || H > 8192 || H % 256 || E < 1 || E > 1024)
+        return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, H % 256 == 0 in [256, 8192], 1 <= E <= 1024");
+    if (!al16(x) || !al16(w_r) || !al4(logits) || (b && !al4(b)))
+        return fail(MOE_ERR_ALIGN, "x and w_r must be 16-byte aligned");
+    const size_t need = (T <= kDecMaxT) ? (size_t)(H / kRouterKChunk) * T * E * 4 : 0;
+    if (need && (!ws || ws_bytes < need)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (T <= kDecMaxT) {
+        launch_router_partial(x, T, H, E, w_r, (float*)ws, st);
+        launch_router_reduce((const float*)ws, H / kRouterKChunk, T, E, b, logits, st);
+    } else {
+        launch_gemm_router(x, T, H, E, w_r, b, logits, st);
+    }
+    return launched("moe_router_logits");
+}
+
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                     float* topk_w, void* stream) {
+    g_last_error.clear();
+    if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_NULL, "null argument");
+    if (T < 1 || T > kMaxT || E < 1 || E > 1024 || k < 1 || k > 32 || k > E)
+        return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, 1 <= E <= 1024, 1 <= k <= min(E, 32)");
+    if (!al4(logits) || !al4(topk_ids) || !al4(topk_w)) return fail(MOE_ERR_ALIGN, "misaligned");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    launch_topk(logits, T, E, k, topk_ids, topk_w, nullptr, nullptr, (hipStream_t)stream);
+    return launched("moe_route");
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                       int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!topk_ids || !offsets || !perm || !inv_perm) return fail(MOE_ERR_NULL, "null argument");
+    if (T < 1 || T > kMaxT || E < 1 || E > 1024 || k < 1 || k > 32 || k > E)
+        return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, 1 <= E <= 1024, 1 <= k <= min(E, 32)");
+    if (!al4(topk_ids) || !al4(offsets) || !al4(perm) || !al4(inv_perm))
+        return fail(MOE_ERR_ALIGN, "misaligned");
+    const size_t need = permute_ws_bytes(T, k, E);
+    if (need && (!ws || ws_bytes < need)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (T <= kDecMaxT) {
+        launch_permute_small(topk_ids, T, E, k, offsets, perm, inv_perm, nullptr, nullptr, st);
+    } else {
+        const size_t hist_b = a256((size_t)((T + 63) / 64) * E * 4);
+        const int mt = max_tiles_for(T, E, k);
+        int32_t* hist = at<int32_t>(ws, 0);
+        int32_t* tiles = at<int32_t>(ws, hist_b);
+        int32_t* nt = at<int32_t>(ws, hist_b + a256((size_t)mt * 12));
+        launch_permute_large(topk_ids, T, k, E, kGemmBM, hist, offsets, perm, inv_perm, tiles, nt, st);
+    }
+    return launched("moe_permute");
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                          const uint16_t* x, int32_t T, const int32_t* offsets,
+                          const int32_t* perm, float* y_perm, float* shared_y, void* ws,
+                          size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    moe_status s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    const bool do_sh = shared_y && desc->shared_inter > 0;
+    s = check_weights(desc, wts, false, do_sh);
+    if (s != MOE_OK) return s;
+    if (!x || !offsets || !perm || !y_perm) return fail(MOE_ERR_NULL, "null argument");
+    if (T < 1 || T > kMaxT) return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18");
+    if (!al16(x) || !al4(offsets) || !al4(perm) || !al4(y_perm) || (shared_y && !al4(shared_y)))
+        return fail(MOE_ERR_ALIGN, "x must be 16-byte aligned");
+    const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k,
+              Is = desc->shared_inter;
+    const Ws L = layout(H, I, E, k, Is, T);
+    if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    s = check_device();
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* ex = (const uint8_t*)wts->experts;
+    const uint16_t* sug = do_sh ? (const uint16_t*)wts->shared_upgate : nullptr;
+    const uint16_t* sdn = do_sh ? (const uint16_t*)wts->shared_down : nullptr;
+    int32_t* tiles = at<int32_t>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.ntiles);
+    uint16_t* x16 = at<uint16_t>(ws, L.x16);
+    uint16_t* a16 = at<uint16_t>(ws, L.a16);
+    uint16_t* ash = at<uint16_t>(ws, L.a_sh);
+    launch_to_f16(x, x16, (int64_t)T * H, st);
+    if (T <= kDecMaxT) {
+        launch_build_tiles(offsets, E, kDecMaxT, tiles, nt, st);
+        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, x, T, H, I,
+                          sug, Is, a16, ash, st);
+        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, sdn, ash, Is,
+                        y_perm, shared_y, st);
+    } else {
+        launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
+        if (do_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, shared_y, st);
+        launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
+        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, y_perm, st);
+    }
+    return launched("moe_expert_ffn");
+}
+
+moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
+                       int32_t T, int32_t k, int32_t H, const float* shared_y, float* y,
+                       void* stream) {
+    g_last_error.clear();
+    if (!y_perm || !inv_perm || !topk_w || !y) return fail(MOE_ERR_NULL, "null argument");
+    if (T < 1 || T > kMaxT || k < 1 || k > 32 || H < 4 || H % 4)
+        return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, 1 <= k <= 32, H % 4 == 0");
+    if (!al16(y_perm) || !al16(y) || (shared_y && !al16(shared_y)) || !al4(inv_perm) || !al4(topk_w))
+        return fail(MOE_ERR_ALIGN, "y_perm, shared_y and y must be 16-byte aligned");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    launch_combine(y_perm, inv_perm, topk_w, T, k, H, shared_y, y, (hipStream_t)stream);
+    return launched("moe_combine");
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                             const uint16_t* x, int32_t T, const float* logits_or_null, float* y,
+                             int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+    g_last_error.clear();
+    moe_status s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    const bool has_sh = desc->shared_inter > 0;
+    s = check_weights(desc, wts, logits_or_null == nullptr, has_sh);
+    if (s != MOE_OK) return s;
+    if (!x || !y) return fail(MOE_ERR_NULL, "x and y must be non-NULL");
+    if (T < 1 || T > kMaxT) return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18");
+    if (!al16(x) || !al16(y) || (logits_or_null && !al4(logits_or_null)) ||
+        (topk_ids_out && !al4(topk_ids_out)) || (topk_w_out && !al4(topk_w_out)))
+        return fail(MOE_ERR_ALIGN, "x and y must be 16-byte aligned");
+    const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k,
+              Is = desc->shared_inter;
+    const Ws L = layout(H, I, E, k, Is, T);
+    if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    s = check_device();
+    if (s != MOE_OK) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* ex = (const uint8_t*)wts->experts;
+    const uint16_t* sug = has_sh ? (const uint16_t*)wts->shared_upgate : nullptr;
+    const uint16_t* sdn = has_sh ? (const uint16_t*)wts->shared_down : nullptr;
+    uint16_t* x16 = at<uint16_t>(ws, L.x16);
+    float* part = at<float>(ws, L.part);
+    float* lg = at<float>(ws, L.logits);
+    int32_t* ids = at<int32_t>(ws, L.ids);
+    float* wv = at<float>(ws, L.w);
+    int32_t* offs = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* inv = at<int32_t>(ws, L.inv);
+    int32_t* tiles = at<int32_t>(ws, L.tiles);
+    int32_t* nt = at<int32_t>(ws, L.ntiles);
+    uint16_t* a16 = at<uint16_t>(ws, L.a16);
+    uint16_t* ash = at<uint16_t>(ws, L.a_sh);
+    float* yp = at<float>(ws, L.y_perm);
+    float* ysh = at<float>(ws, L.y_sh);
+    int32_t* hist = at<int32_t>(ws, L.hist);
+
+    if (T <= kDecMaxT) {
+        if (!logits_or_null)
+            launch_router_partial(x, T, H, E, (const uint16_t*)wts->router_w, part, st);
+        launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, x16, T, E,
+                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt, st);
+        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, x, T, H, I,
+                          sug, Is, a16, ash, st);
+        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, sdn, ash, Is,
+                        yp, ysh, st);
+    } else {
+        const float* L_use = logits_or_null;
+        if (!L_use) {
+            launch_gemm_router(x, T, H, E, (const uint16_t*)wts->router_w, wts->router_b, lg, st);
+            L_use = lg;
+        }
+        launch_topk(L_use, T, E, k, ids, wv, topk_ids_out, topk_w_out, st);
+        launch_to_f16(x, x16, (int64_t)T * H, st);
+        launch_permute_large(ids, T, k, E, kGemmBM, hist, offs, perm, inv, tiles, nt, st);
+        if (has_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, ysh, st);
+        launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
+        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, yp, st);
+    }
+    launch_combine(yp, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+    return launched("moe_layer_forward");
+}
+
+moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
+                          void* stream) {
+    g_last_error.clear();
+    if (!blocks || !out) return fail(MOE_ERR_NULL, "null argument");
+    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32)
+        return fail(MOE_ERR_FORMAT, "moe_dequantize supports Q3S256 and NL4_32");
+    const int64_t unit = fmt == MOE_FMT_Q3S256 ? 256 : 32;
+    if (n_weights < unit || n_weights % unit)
+        return fail(MOE_ERR_SHAPE, "n_weights must be a positive multiple of the block size");
+    if (!al16(blocks) || !al4(out)) return fail(MOE_ERR_ALIGN, "blocks must be 16-byte aligned");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    launch_dequant(fmt, blocks, n_weights, out, (hipStream_t)stream);
+    return launched("moe_dequantize");
+}
+
+moe_status moe_rmsnorm_residual(float* h, const float* delta, const float* gamma, float eps,
+                                int32_t T, int32_t H, uint16_t* normed_bf16_out, void* stream) {
+    g_last_error.clear();
+    if (!h) return fail(MOE_ERR_NULL, "h is NULL");
+    if ((gamma == nullptr) != (normed_bf16_out == nullptr))
+        return fail(MOE_ERR_NULL, "gamma and normed_bf16_out must both be given or both NULL");
+    if (T < 1 || T > kMaxT || H < 1 || H > 65536)
+        return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, 1 <= H <= 65536");
+    if (!(eps >= 0.f)) return fail(MOE_ERR_SHAPE, "eps must be >= 0");
+    if (!al4(h) || (delta && !al4(delta)) || (gamma && !al4(gamma)))
+        return fail(MOE_ERR_ALIGN, "misaligned");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    launch_rmsnorm(h, delta, gamma, eps, T, H, normed_bf16_out, (hipStream_t)stream);
+    return launched("moe_rmsnorm_residual");
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+// Device-side helpers shared by the libmoe kernels (gfx950 only).
+//
+// Block codecs decoded here (model card "Qwen3.8-Flash-Next - Avalon GGUF",
+// "Files / Main model": routed up/gate at 3.25 bpw with a scale per
+// 256-weight block and sub-scales per 32 weights; routed down in a 4-bit
+// non-linear 32-weight type).  Byte layouts (a reading; the page gives none):
+//   Q3S-256, 104 B: [0,96) 3-bit indices, LSB-first stream; [96,98) fp16 d;
+//                   [98,102) eight signed nibbles s_j; [102,104) reserved.
+//                   w = d * s_j * C3[q] / 128.
+//   NL4-32,   18 B: [0,2) fp16 d; [2,18) 4-bit indices, even weight in the
+//                   low nibble.  w = d * T4[q] / 128.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Codebooks (value = entry / 128): int8 levels at normal quantiles, sorted,
+// asymmetric with an exact zero.
+__constant__ const int8_t kC3[8] = {-127, -67, -31, 0, 23, 48, 78, 127};
+__constant__ const int8_t kT4[16] = {-127, -88, -66, -50, -36, -23, -11, 0,
+                                     10, 20, 31, 43, 56, 71, 91, 127};
+
+constexpr int kQ3Bytes = 104;
+constexpr int kQ3Weights = 256;
+constexpr int kNL4Bytes = 18;
+constexpr int kNL4Weights = 32;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Two fp16 halves packed into one dword.
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) {
+    return (lo & 0xffffu) | (hi << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32: lane l holds A[l%16][8(l/16) .. 8(l/16)+7], B[same k][l%16];
+// D lane l holds D[4(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// 32x32x16: lane l holds A[l%32][8(l/32) .. +7], B[same k][l%32];
+// D lane l, register r holds D[8(r/4) + 4(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- loads
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ uint32_t ld4(const void* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+}
+// Streaming (read-once) 16-byte load: bypass-friendly cache policy.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// ---------------------------------------------------------------- top-k key
+// Total order used by the routing: larger logit first, then lower expert
+// index.  -0.0 is folded onto +0.0 so equal values compare equal.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)k << 32) | (uint32_t)(~(uint32_t)e);
+}
+__device__ __forceinline__ int topk_key_index(uint64_t key) {
+    return (int)(~(uint32_t)key);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+    uint32_t k = (uint32_t)(key >> 32);
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Exact top-k of one row of E logits by one wave64 (E <= 1024, k <= 32).
+// Lane j < k returns (id_j, L_j) in selection order; other lanes return
+// (-1, 0).  `get(e)` yields the fp32 logit of expert e.
+template <typename Get>
+__device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, float& out_val) {
+    const int lane = __lane_id();
+    uint64_t keys[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int e = lane + 64 * i;
+        keys[i] = (e < E) ? topk_key(get(e), e) : 0ull;
+    }
+    out_id = -1;
+    out_val = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) best = keys[i] > best ? keys[i] : best;
+        uint64_t win = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (keys[i] == win) keys[i] = 0ull;      // keys are unique (index part)
+        if (lane == j) {
+            out_id = topk_key_index(win);
+            out_val = topk_key_value(win);
+        }
+    }
+}
+
+// Softmax over the k selected logits held by lanes 0..k-1 (lane 0 = max).
+__device__ __forceinline__ float wave_softmax_selected(float v, int k) {
+    const int lane = __lane_id();
+    float m = __shfl(v, 0, 64);
+    float ex = (lane < k) ? expf(v - m) : 0.f;
+    float s = wave_sum_f32(ex);
+    return ex / s;
+}
+
+// ---------------------------------------------------------------- decoders
+// Q3S-256 tail (bytes 96..103 of a block, loaded as one 8-byte word):
+// d = bits 0..15, s_j = bits 16+4j .. 19+4j (signed).
+__device__ __forceinline__ float q3_tail_d(uint64_t tail) {
+    return f16_bits_to_f32((uint32_t)(tail & 0xffffu));
+}
+__device__ __forceinline__ int q3_tail_s(uint64_t tail, int j) {
+    int nib = (int)((tail >> (16 + 4 * j)) & 0xfu);
+    return (nib ^ 8) - 8;
+}
+// 3-bit index i (0..31) of a sub-block whose 12 index bytes are w0,w1,w2.
+__device__ __forceinline__ int q3_index(uint32_t w0, uint32_t w1, uint32_t w2, int i) {
+    uint64_t lo = ((uint64_t)w1 << 32) | w0;
+    int bit = 3 * i;
+    if (bit <= 61) return (int)((lo >> bit) & 7u);
+    if (bit == 63) return (int)(((w1 >> 31) & 1u) | ((w2 & 3u) << 1));
+    return (int)((w2 >> (bit - 64)) & 7u);
+}
+// Exact fp32 value d * s * c / 128 (d*s exact in 15 bits, *c in 22 bits, /128
+// a power of two).
+__device__ __forceinline__ float q3_value(float d, int s, int q) {
+    return (d * (float)s) * (float)kC3[q] * 0.0078125f;
+}
+__device__ __forceinline__ float nl4_value(float d, int q) {
+    return d * (float)kT4[q] * 0.0078125f;
+}
+
+}  // namespace moe

@@ -1,0 +1,67 @@
+// Host-side launchers of the libmoe kernels (one per kernel family), called
+// by the C ABI in moe_api.hip.  Every launcher only enqueues on `st`.
+#pragma once
+
+#include "moe_common.hpp"
+
+namespace moe {
+
+// Work sizes shared by host and device code.
+constexpr int kDecMaxT = 16;          // tokens handled by the bandwidth path
+constexpr int kRouterKChunk = 256;    // K per router partial (bandwidth path)
+constexpr int kGemmBM = 128;          // rows per grouped-GEMM tile
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 64;
+
+// ---- small kernels (moe_kernels_small.hip)
+void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, hipStream_t st);
+void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st);
+void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                 int32_t* ids2, float* w2, hipStream_t st);
+void launch_router_reduce(const float* part, int nkc, int T, int E, const float* bias,
+                          float* logits, hipStream_t st);
+void launch_route_small(const float* part, int nkc, const float* bias, const float* given,
+                        const uint16_t* x, int H, uint16_t* x16, int T, int E, int k,
+                        int32_t* ids, float* w, int32_t* ids_out, float* w_out,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
+                        int32_t* ntiles, hipStream_t st);
+void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* ntiles,
+                          hipStream_t st);
+void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32_t* hist,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
+                          int32_t* ntiles, hipStream_t st);
+void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, int32_t* ntiles,
+                        hipStream_t st);
+void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
+                    const float* shared, float* y, hipStream_t st);
+void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
+                    uint16_t* normed, hipStream_t st);
+
+// ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT
+void launch_router_partial(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
+                           float* part, hipStream_t st);
+void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
+                       const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
+                       const uint16_t* x16, const uint16_t* x, int T, int H, int I,
+                       const uint16_t* sh_ug, int Is, uint16_t* a16_perm, uint16_t* a_sh,
+                       hipStream_t st);
+void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
+                     const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T,
+                     int H, int I, const uint16_t* sh_down, const uint16_t* a_sh, int Is,
+                     float* y_perm, float* y_sh, hipStream_t st);
+
+// ---- grouped-GEMM path (moe_kernels_gemm.hip)
+void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
+                        const float* bias, float* logits, hipStream_t st);
+void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
+                        const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
+                        const uint16_t* x16, int H, int I, uint16_t* a16_perm, hipStream_t st);
+void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
+                      const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
+                      int I, float* y_perm, hipStream_t st);
+void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
+                        const uint16_t* sh_down, int Is, uint16_t* a_sh, float* y_sh,
+                        hipStream_t st);
+
+}  // namespace moe

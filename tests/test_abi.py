@@ -1,0 +1,113 @@
+"""The C ABI library on the CPU: it loads, exports every function include/moe.h
+declares, and rejects bad arguments on the host before touching a GPU (every
+check runs before any launch, so these need no device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_ffn_top_amd as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+# fake, 256-aligned device addresses: never dereferenced by a failing check
+P = 0x10000000
+P2 = 0x20000000
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Q.load()
+    decl = _declared()
+    assert set(decl) == set(Q.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = Q.load()
+    for s in range(8):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(5) == b"workspace missing or too small"
+
+
+def test_workspace_size_monotone_and_rejects_bad_desc():
+    d = Q.desc(3072, 512, 512, 10, 512)
+    sizes = [Q.moe_workspace_size(d, T) for T in (1, 3, 8, 16, 17, 64, 8192)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    bad = Q.desc(3000, 512, 512, 10, 512)
+    assert Q.moe_workspace_size(bad, 4) == 0
+    assert Q.moe_workspace_size(d, 0) == 0
+
+
+def _fwd(d, w, T=4, ws_bytes=1 << 30, x=P, y=P2, logits=None):
+    lib = Q.load()
+    return lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), x, T, logits, y, None, None,
+                                 P, ws_bytes, None)
+
+
+def _w(experts=P, stride=45056, router=P, shared=(None, None)):
+    return Q.LayerWeights(experts, stride, router, None, shared[0], shared[1])
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(hidden=100), 2), (dict(hidden=256 * 33 + 0, inter=96), 2), (dict(inter=32), 2),
+    (dict(n_experts=0), 2), (dict(top_k=17, n_experts=16), 2), (dict(shared_inter=100), 2),
+    (dict(upgate_fmt=1), 3), (dict(down_fmt=2), 3),
+])
+def test_layer_forward_rejects_bad_shapes(case, status):
+    base = dict(hidden=256, inter=128, n_experts=16, top_k=2, shared_inter=0, upgate_fmt=2,
+                down_fmt=3)
+    base.update(case)
+    d = Q.LayerDesc(**base)
+    assert _fwd(d, _w()) == status
+    assert Q.load().moe_last_error()
+
+
+def test_layer_forward_error_paths():
+    d = Q.desc(256, 128, 16, 2, 0)
+    lib = Q.load()
+    assert lib.moe_layer_forward(ctypes.byref(d), None, P, 4, None, P2, None, None, P, 1 << 30,
+                                 None) == 1
+    assert _fwd(d, _w(experts=None)) == 1                  # null experts
+    assert _fwd(d, _w(experts=P + 8)) == 4                 # misaligned experts
+    assert _fwd(d, _w(stride=45056 + 8)) == 4              # misaligned stride
+    assert _fwd(d, _w(stride=45056 - 16)) == 2             # stride smaller than a record
+    assert _fwd(d, _w(router=None)) == 1                   # no router and no logits
+    assert _fwd(d, _w(), x=P + 2) == 4                     # misaligned x
+    assert _fwd(d, _w(), T=0) == 2
+    assert _fwd(d, _w(), ws_bytes=16) == 5                 # workspace too small
+    d2 = Q.desc(256, 128, 16, 2, 64)
+    assert _fwd(d2, _w()) == 1                             # shared_inter > 0, no shared weights
+
+
+def test_stage_error_paths():
+    lib = Q.load()
+    assert lib.moe_route(None, 4, 16, 2, P, P2, None) == 1
+    assert lib.moe_route(P, 4, 16, 17, P, P2, None) == 2
+    assert lib.moe_route(P, 4, 2000, 2, P, P2, None) == 2
+    assert lib.moe_permute(P, 100, 2, 16, P, P, P, None, 0, None) == 5   # needs workspace
+    assert lib.moe_combine(P, P, P, 4, 2, 254, None, P2, None) == 2      # H % 4
+    assert lib.moe_combine(P + 4, P, P, 4, 2, 256, None, P2, None) == 4
+    assert lib.moe_dequantize(1, P, 256, P2, None) == 3
+    assert lib.moe_dequantize(2, P, 100, P2, None) == 2
+    assert lib.moe_dequantize(3, P + 8, 32, P2, None) == 4
+    assert lib.moe_rmsnorm_residual(P, None, P, 1e-6, 4, 256, None, None) == 1
+    assert lib.moe_router_logits(P, 4, 250, 16, P, None, P2, P, 1 << 20, None) == 2
+    assert lib.moe_router_logits(P, 4, 256, 16, P, None, P2, None, 0, None) == 5
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    import quantized_expert_ffn_top_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libmoe.so")
+    with pytest.raises(RuntimeError):
+        L.load()

@@ -1,0 +1,146 @@
+"""GPU parity of the whole layer (moe_layer_forward) against the oracle.
+
+Both regimes are covered on both sides of the switch (T <= 16: bandwidth
+path; T >= 17: grouped-GEMM path), at the tiny shape (fully compared) and at
+the real shape: decode batches fully compared, the 8192-token prefill on
+sampled tokens (the oracle computes those tokens one by one) plus properties
+that hold for every token (valid top-k ids, finite outputs).
+
+Routing: with given logits the ids must match bit for bit.  With the router
+on, GPU logits (fp32) and oracle logits (fp64) can order a near-tie
+differently; the GPU's selection must then be a valid top-k within
+1e-5 * max|L| and the oracle continues with it (none is expected).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_expert_ffn_top_amd as Q
+import synth
+from oracle import moe as OM
+from tests._helpers import (ExpertCache, assert_close, bf16_np, dev, ids_valid_topk,
+                            real_shared_np, tiny_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(d, wts, x, logits=None):
+    T = x.shape[0]
+    y = torch.empty((T, d.hidden), dtype=torch.float32, device=dev())
+    ids = torch.empty((T, d.top_k), dtype=torch.int32, device=dev())
+    w = torch.empty((T, d.top_k), dtype=torch.float32, device=dev())
+    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+    Q.moe_layer_forward(d, wts, x, y, ws, logits=logits, topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 17, 64, 300])
+def test_tiny_layer(T):
+    sh, recs, x, logits = tiny_inputs(seed=1, T=T)
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, 0)
+    ex = torch.from_numpy(recs).to(dev())
+    wts = Q.weights(ex, sh.expert_bytes)
+    y, ids, w = _run_layer(d, wts, x.to(dev()), logits=logits.to(dev()))
+    ref = OM.layer_forward(bf16_np(x), sh.top_k, ExpertCache(sh, lambda e: recs[e]),
+                           sh.n_experts, logits=logits.double().numpy())
+    assert np.array_equal(ids, ref["ids"])
+    assert np.abs(w - ref["w"]).max() <= 1e-6
+    assert_close(y, ref["y"], "tiny T=%d" % T)
+
+
+def _real_case(T, seed, zipf_s=1.0, sample=None):
+    sh = synth.REAL
+    lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev())
+    x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    y, ids, w = _run_layer(d, wts, x)
+    xs = bf16_np(x)
+    L = OM.router_logits(xs, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+    ref_ids = OM.topk_ids_fast(L, sh.top_k)
+    assert ids_valid_topk(ids, L, sh.top_k)
+    mism = np.where((np.sort(ids, axis=1) != np.sort(ref_ids, axis=1)).any(axis=1))[0]
+    assert len(mism) <= max(1, T // 1000), "routing differs on %d tokens" % len(mism)
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    cache = ExpertCache(sh, lambda e: synth.expert_record(sh, seed, 0, e).numpy())
+    ref = OM.layer_forward(xs[rows], sh.top_k, cache, sh.n_experts, logits=L[rows],
+                           shared=real_shared_np(lay), force_ids=ids[rows])
+    assert np.abs(w[rows] - ref["w"]).max() <= 1e-5
+    assert_close(y[rows], ref["y"], "real T=%d" % T)
+    assert np.all(np.isfinite(y))
+    return y, ids
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+def test_real_decode_layer(T):
+    _real_case(T, seed=2)
+
+
+@pytest.mark.parametrize("T", [17, 64])
+def test_real_small_gemm_layer(T):
+    _real_case(T, seed=7)
+
+
+def test_real_prefill_zipf_sampled():
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(8192, size=6, replace=False))
+    sample[-1] = 8191                                   # the ragged end of the last tile
+    _real_case(8192, seed=3, zipf_s=1.0, sample=sample)
+
+
+def test_real_prefill_uniform_sampled():
+    rng = np.random.default_rng(1)
+    sample = np.sort(rng.choice(2048, size=5, replace=False))
+    _real_case(2048, seed=3, zipf_s=0.0, sample=sample)
+
+
+def test_layer_deterministic():
+    sh, recs, x, logits = tiny_inputs(seed=4, T=300)
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, 0)
+    ex = torch.from_numpy(recs).to(dev())
+    wts = Q.weights(ex, sh.expert_bytes)
+    a = _run_layer(d, wts, x.to(dev()), logits=logits.to(dev()))
+    b = _run_layer(d, wts, x.to(dev()), logits=logits.to(dev()))
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_stack_three_layers_teacher_forced():
+    """Pre-norm residual stack (RMSNorm eps 1e-6, gamma ~ N(1, 0.1)), T = 3:
+    each layer's GPU output is compared with the oracle fed the GPU's layer
+    input; the end-to-end error is reported through the same tolerance."""
+    sh = synth.REAL
+    T, seed = 3, 4
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    h = synth.tokens_bf16(T, sh.hidden, seed).float().to(dev())
+    h_ref = h.double().cpu().numpy()
+    normed = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=dev())
+    y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev())
+    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+    for l in range(3):
+        lay = synth.real_layer(sh, seed, l, zipf_s=1.0, device=dev())
+        gamma = synth.norm_gain(sh.hidden, seed, l).to(dev())
+        Q.moe_rmsnorm_residual(h, None, gamma, 1e-6, normed)
+        wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                        lay.shared_down)
+        ids = torch.empty((T, sh.top_k), dtype=torch.int32, device=dev())
+        Q.moe_layer_forward(d, wts, normed, y, ws, topk_ids_out=ids)
+        torch.cuda.synchronize()
+        xin = bf16_np(normed)
+        L = OM.router_logits(xin, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+        cache = ExpertCache(sh, lambda e, l=l: synth.expert_record(sh, seed, l, e).numpy())
+        ref = OM.layer_forward(xin, sh.top_k, cache, sh.n_experts, logits=L,
+                               shared=real_shared_np(lay), force_ids=ids.cpu().numpy())
+        assert ids_valid_topk(ids.cpu().numpy(), L, sh.top_k)
+        assert_close(y.cpu().numpy(), ref["y"], "stack layer %d" % l)
+        # oracle's own end-to-end stream (not teacher-forced) for the report
+        h_ref = OM.stack_step(h_ref, gamma.cpu().numpy(), 1e-6,
+                              lambda z: OM.layer_forward(z, sh.top_k, cache, sh.n_experts,
+                                                         router_w=bf16_np(lay.router_w),
+                                                         router_b=lay.router_b.cpu().numpy(),
+                                                         shared=real_shared_np(lay))["y"])
+        Q.moe_rmsnorm_residual(h, y, None, 1e-6, None)
+    assert_close(h.cpu().numpy(), h_ref, "stack end-to-end")
