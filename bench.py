@@ -1,0 +1,283 @@
+"""Benchmark of the routed, block-quantized MoE FFN layer on one MI355X.
+
+Workload (the decode-shaped single layer at real shape): H=3072, 512 routed
+experts (up|gate in the 3.25-bpw Q3S-256 codec, down in the 4-bit NL4-32
+codec), top-10 with softmax over the selected logits, one always-on bf16
+shared expert (I_s=512), I=512; router W_r bf16 [512][3072] plus a Zipf(1.0)
+popularity bias; tokens bf16 N(0,1).  A step is one whole layer forward
+(router, top-k, permutation, up|gate + SwiGLU, down, combine) over a batch of
+T tokens, T = 8 for the headline value; T = 1 and 3 are reported beside it,
+and the 8192-token prefill chunk too.  Decode steps rotate through 16
+independently seeded layers (17.7 GB of packed experts) so the 256 MB
+Infinity Cache cannot serve repeated experts; inputs are resident in HBM
+before timing starts.
+
+The roofline object is for the dominant kernel of the headline workload (the
+up|gate kernel of the bandwidth path), its duration measured with HIP events
+recorded by the library around that kernel on the caller's stream; its
+algorithmic bytes are those of the experts the batch actually routes to.
+
+cpu_baseline: the CPU oracle (fp64 NumPy, dequantising from the packed bytes)
+on one T = 8 decode layer of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix cores, vendor figure
+
+# algorithmic bytes / flops (real shape: H=3072, I=512, E=512, k=10, I_s=512)
+H, I, E, K, IS = 3072, 512, 512, 10, 512
+UG_BYTES = 2 * I * (H // 256) * 104            # 1,277,952 packed up|gate bytes per expert
+DN_BYTES = H * (I // 32) * 18                  # 884,736 packed down bytes per expert
+SH_UG_BYTES = 2 * IS * H * 2                   # 6,291,456
+SH_DN_BYTES = H * IS * 2                       # 3,145,728
+ROUTER_BYTES = E * H * 2 + E * 4               # 3,147,776
+FLOP_PER_TOKEN = K * 2 * 3 * H * I + 2 * 3 * H * IS + 2 * H * E   # 106,954,752
+
+
+def upgate_bytes(T, U):
+    """Up|gate kernel (bandwidth path): packed up|gate of the U distinct routed
+    experts + shared up|gate + x (bf16 and its fp16 copy) + a written (fp16
+    routed, bf16 shared)."""
+    return U * UG_BYTES + SH_UG_BYTES + 2 * T * H * 2 + T * K * I * 2 + T * IS * 2
+
+
+def down_bytes(T, U):
+    return U * DN_BYTES + SH_DN_BYTES + T * K * I * 2 + T * IS * 2 + T * K * H * 4 + T * H * 4
+
+
+def layer_bytes(T, U):
+    """Whole layer: every distinct weight byte once + token in/out."""
+    return U * (UG_BYTES + DN_BYTES) + SH_UG_BYTES + SH_DN_BYTES + ROUTER_BYTES + T * (H * 2 + H * 4)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=48)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--layers", type=int, default=16, help="decode layers rotated through")
+    p.add_argument("--prefill-steps", type=int, default=10)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (this build has no multi-GPU path); "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_expert_ffn_top_amd as Q
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    Q.load()
+    sh = synth.REAL
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+
+    t0 = time.time()
+    layers = [synth.real_layer(sh, 2, l, zipf_s=1.0, device=dev) for l in range(args.layers)]
+    wts = [Q.weights(L.experts, sh.expert_bytes, L.router_w, L.router_b, L.shared_ug,
+                     L.shared_down) for L in layers]
+    torch.cuda.synchronize()
+    print("# generated %d layers in %.1f s" % (args.layers, time.time() - t0), file=sys.stderr)
+
+    ws = torch.empty(Q.moe_workspace_size(d, 8192), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def distinct_experts(T, x):
+        us = []
+        ids = torch.empty((T, sh.top_k), dtype=torch.int32, device=dev)
+        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        for l in range(args.layers):
+            Q.moe_layer_forward(d, wts[l], x, y, ws, topk_ids_out=ids)
+            us.append(int(torch.unique(ids).numel()))
+        return us
+
+    def time_steps(T, x, steps, warmup, nlay):
+        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        for i in range(warmup):
+            Q.moe_layer_forward(d, wts[i % nlay], x, y, ws)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            Q.moe_layer_forward(d, wts[i % nlay], x, y, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def time_kernels(T, x, steps, nlay, nev):
+        """Per-kernel durations (ms) from events the library records between
+        its kernels; averaged over `steps` calls."""
+        y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        for row in evs:
+            for ev in row:
+                ev.record(stream)            # materialise the handles
+        torch.cuda.synchronize()
+        n_marks = None
+        for i in range(steps):
+            n_marks = Q.moe_layer_forward_timed(d, wts[i % nlay], x, y, ws,
+                                                [ev.cuda_event for ev in evs[i]])
+        torch.cuda.synchronize()
+        dur = np.zeros(n_marks - 1)
+        for row in evs:
+            for j in range(n_marks - 1):
+                dur[j] += row[j].elapsed_time(row[j + 1])
+        return dur / steps
+
+    results = {"decode": {}, "prefill": None}
+    for T in (1, 3, 8):
+        x = synth.tokens_bf16(T, sh.hidden, 2, 0).to(dev)
+        us = distinct_experts(T, x)
+        ms = time_steps(T, x, args.steps, args.warmup, args.layers)
+        U = float(np.mean(us))
+        lb = layer_bytes(T, U)
+        kd = time_kernels(T, x, max(args.layers, 16), args.layers, 8)
+        names = ["router", "route+permute", "upgate", "down", "combine"]
+        kern = {}
+        for nm, t in zip(names, kd):
+            kern[nm] = {"us": round(t * 1e3, 2)}
+        kern["upgate"]["GBps"] = round(upgate_bytes(T, U) / (kd[2] * 1e-3) / 1e9, 1)
+        kern["down"]["GBps"] = round(down_bytes(T, U) / (kd[3] * 1e-3) / 1e9, 1)
+        results["decode"][T] = {
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "distinct_experts_mean": U, "layer_bytes": int(lb),
+            "layer_GBps": round(lb / (ms * 1e-3) / 1e9, 1),
+            "layer_hbm_frac": round(lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels": kern, "_kd": kd, "_U": U,
+        }
+        print("# decode T=%d: %.4f ms/step, U=%.1f, %.0f GB/s layer, kernels %s" % (
+            T, ms, U, lb / (ms * 1e-3) / 1e9, kern), file=sys.stderr)
+
+    if not args.no_prefill:
+        Tp = 8192
+        x = synth.tokens_bf16(Tp, sh.hidden, 3, 0).to(dev)
+        ms = time_steps(Tp, x, args.prefill_steps, 2, 1)
+        kd = time_kernels(Tp, x, 4, 1, 12)
+        names = ["router", "topk", "to_f16", "permute", "shared", "upgate", "down", "combine"]
+        flops = FLOP_PER_TOKEN * Tp
+        ug_flops = 2.0 * Tp * K * 2 * I * H
+        dn_flops = 2.0 * Tp * K * I * H
+        kern = {nm: {"us": round(t * 1e3, 1)} for nm, t in zip(names, kd)}
+        kern["upgate"]["TFLOPs"] = round(ug_flops / (kd[5] * 1e-3) / 1e12, 1)
+        kern["down"]["TFLOPs"] = round(dn_flops / (kd[6] * 1e-3) / 1e12, 1)
+        results["prefill"] = {
+            "tokens": Tp, "tokens_per_s": round(Tp / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "algorithmic_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "kernels": kern,
+        }
+        print("# prefill T=%d: %.3f ms, %.1f TFLOP/s, kernels %s" % (
+            Tp, ms, flops / (ms * 1e-3) / 1e12, kern), file=sys.stderr)
+
+    # roofline of the dominant kernel of the headline workload (decode T=8)
+    dec8 = results["decode"][8]
+    kd8, U8 = dec8.pop("_kd"), dec8.pop("_U")
+    for T in (1, 3):
+        results["decode"][T].pop("_kd")
+        results["decode"][T].pop("_U")
+    ub = upgate_bytes(8, U8)
+    ach = ub / (kd8[2] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for("k_upgate_dec", ub),
+            "kernel": "k_upgate_dec (up|gate + SwiGLU, routed + shared, T=8)",
+            "bytes_per_launch": int(ub), "us_per_launch": round(kd8[2] * 1e3, 2)}
+
+    cpu = None if args.no_cpu else cpu_baseline(layers[0], sh)
+
+    ms8 = dec8["ms_per_step"]
+    line = {
+        "metric": "MoE-layer tokens/s (decode, T=8)", "value": dec8["tokens_per_s"],
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms8, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q3s/nl4 weights, fp16/bf16 mfma, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "decode-shaped MoE layer: H=3072, E=512 routed (Q3S-256 up|gate, "
+                               "NL4-32 down), top-10 + 1 shared bf16 expert, I=512, T=8 tokens, "
+                               "Zipf(1.0) routing, 16 rotating layers",
+                   "tokens": 8, "layers_rotated": args.layers},
+        "roofline": roof, "cpu_baseline": cpu, "results": results,
+    }
+    print(json.dumps(line))
+
+
+def traffic_for(kernel, algo_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel's file; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+    except Exception:
+        return None
+    src = os.path.join(ROOT, "quantized_expert_ffn_top_amd", "csrc", rec["source"])
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layer, sh):
+    """The oracle as it stands on one decode layer, T = 8 tokens."""
+    import numpy as np
+    import torch
+
+    import synth
+    from oracle import formats as OF
+    from oracle import moe as OM
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                     # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    T = 8
+    x = synth.tokens_bf16(T, sh.hidden, 2, 0)
+    t0 = time.time()
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        def bf(t):
+            return OM.bf16_bits_to_float(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+
+        def get(e, cache={}):
+            if e not in cache:
+                rec = layer.experts[e].cpu().numpy()
+                cache[e] = OF.expert_matrices(rec, sh.hidden, sh.inter)
+            return cache[e]
+
+        ug = bf(layer.shared_ug)
+        shared = (ug[:sh.shared_inter], ug[sh.shared_inter:], bf(layer.shared_down))
+        OM.layer_forward(bf(x), sh.top_k, get, sh.n_experts, router_w=bf(layer.router_w),
+                         router_b=layer.router_b.cpu().numpy().astype(np.float64), shared=shared)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.time() - t0
+    return {"value": round(T / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "one decode layer (T=8 tokens, ~60 routed experts dequantised from their "
+                      "packed bytes + shared expert + router), fp64 NumPy, %.1f s" % dt}
+
+
+if __name__ == "__main__":
+    main()

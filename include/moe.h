@@ -83,7 +83,7 @@ typedef enum {
     MOE_FMT_NL4_32 = 3
 } moe_format;
 
-/* Layer shape.  Supported: hidden % 256 == 0 (and <= 16384); inter % 64 == 0
+/* Layer shape.  Supported: hidden % 256 == 0 (and <= 8192); inter % 64 == 0
  * (and <= 4096); 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
  * shared_inter == 0 (no shared expert) or shared_inter % 64 == 0 (<= 4096);
  * upgate_fmt == MOE_FMT_Q3S256 and down_fmt == MOE_FMT_NL4_32 for the routed
@@ -169,6 +169,21 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
                              const uint16_t* x, int32_t T, const float* logits_or_null,
                              float* y, int32_t* topk_ids_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Instrumented moe_layer_forward, for measurement: identical work, and in
+ * addition events[0] (hipEvent_t, created by the caller) is recorded on
+ * `stream` before the first kernel and events[i] after the i-th kernel, while
+ * i < n_events.  *n_marks receives the number of marks the call wanted
+ * (kernels + 1).  Kernel order -- T <= 16: [router partials (if no logits)],
+ * routing + permutation, up|gate, down, combine; T > 16: [router GEMM (if no
+ * logits)], top-k, fp16 staging, permutation (3 kernels, one mark), [shared
+ * expert GEMMs (2 kernels, one mark)], routed up|gate GEMM, routed down GEMM,
+ * combine. */
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                   const uint16_t* x, int32_t T, const float* logits_or_null,
+                                   float* y, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* events,
+                                   int32_t n_events, int32_t* n_marks);
 
 /* Helper, not the method: dequantize n_weights weights of one format (a whole
  * number of blocks, contiguous) to fp32 `out`, with the same device decoders

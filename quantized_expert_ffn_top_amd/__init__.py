@@ -6,11 +6,12 @@ this package is its Python binding (ctypes) plus the build script.
 
 from ._lib import (EXPORTS, LIB_PATH, MOE_FMT_BF16, MOE_FMT_NL4_32, MOE_FMT_Q3S256, LayerDesc,
                    LayerWeights, MoeError, desc, load, moe_combine, moe_dequantize,
-                   moe_expert_ffn, moe_layer_forward, moe_permute, moe_rmsnorm_residual,
+                   moe_expert_ffn, moe_layer_forward, moe_layer_forward_timed, moe_permute, moe_rmsnorm_residual,
                    moe_route, moe_router_logits, moe_workspace_size, weights)
 
 __all__ = ["EXPORTS", "LIB_PATH", "MOE_FMT_BF16", "MOE_FMT_NL4_32", "MOE_FMT_Q3S256",
            "LayerDesc", "LayerWeights", "MoeError", "desc", "load", "moe_combine",
-           "moe_dequantize", "moe_expert_ffn", "moe_layer_forward", "moe_permute",
+           "moe_dequantize", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed",
+           "moe_permute",
            "moe_rmsnorm_residual", "moe_route", "moe_router_logits", "moe_workspace_size",
            "weights"]

@@ -22,8 +22,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_dequantize",
-           "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
+           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_timed",
+           "moe_dequantize", "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,9 @@ def load():
         "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P, P]),
         "moe_layer_forward": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P,
                                     I32, P, P, P, P, P, SZ, P]),
+        "moe_layer_forward_timed": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                          P, I32, P, P, P, P, P, SZ, P, P, I32,
+                                          ctypes.POINTER(I32)]),
         "moe_dequantize": (I32, [I32, P, I64, P, P]),
         "moe_rmsnorm_residual": (I32, [P, P, P, F, I32, I32, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
@@ -164,6 +167,22 @@ def moe_layer_forward(d, w, x, y, ws, logits=None, topk_ids_out=None, topk_w_out
                                     _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(x)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_timed(d, w, x, y, ws, events, logits=None, topk_ids_out=None,
+                            topk_w_out=None):
+    """events: raw hipEvent_t handles (ints).  Returns the number of marks the
+    call recorded (kernels + 1)."""
+    T = x.shape[0]
+    arr = (ctypes.c_void_p * len(events))(*events)
+    n = ctypes.c_int32(0)
+    _check(load().moe_layer_forward_timed(ctypes.byref(d), ctypes.byref(w), _ptr(x), T,
+                                          _ptr(logits), _ptr(y), _ptr(topk_ids_out),
+                                          _ptr(topk_w_out), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(x), arr,
+                                          len(events), ctypes.byref(n)),
+           "moe_layer_forward_timed")
+    return n.value
 
 
 def moe_dequantize(fmt, blocks, n_weights, out):

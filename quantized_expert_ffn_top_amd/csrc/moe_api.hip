@@ -295,10 +295,27 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
     return launched("moe_combine");
 }
 
-moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* wts,
-                             const uint16_t* x, int32_t T, const float* logits_or_null, float* y,
-                             int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Records events[i] after the i-th kernel of a layer call (events[0] before
+// the first), as long as there are events left.
+struct Marks {
+    void* const* ev;
+    int n;
+    int used;
+    hipStream_t st;
+    void mark() {
+        if (ev && used < n) (void)hipEventRecord((hipEvent_t)ev[used], st);
+        ++used;
+    }
+};
+
+moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                              const uint16_t* x, int32_t T, const float* logits_or_null, float* y,
+                              int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                              size_t ws_bytes, void* stream, Marks* mk) {
     g_last_error.clear();
     moe_status s = check_desc(desc);
     if (s != MOE_OK) return s;
@@ -318,6 +335,7 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
     if (s != MOE_OK) return s;
 
     hipStream_t st = (hipStream_t)stream;
+    mk->st = st;
     const uint8_t* ex = (const uint8_t*)wts->experts;
     const uint16_t* sug = has_sh ? (const uint16_t*)wts->shared_upgate : nullptr;
     const uint16_t* sdn = has_sh ? (const uint16_t*)wts->shared_down : nullptr;
@@ -337,30 +355,75 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
     float* ysh = at<float>(ws, L.y_sh);
     int32_t* hist = at<int32_t>(ws, L.hist);
 
+    mk->mark();
     if (T <= kDecMaxT) {
-        if (!logits_or_null)
+        if (!logits_or_null) {
             launch_router_partial(x, T, H, E, (const uint16_t*)wts->router_w, part, st);
+            mk->mark();
+        }
         launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, x16, T, E,
                            k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt, st);
+        mk->mark();
         launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, x, T, H, I,
                           sug, Is, a16, ash, st);
+        mk->mark();
         launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, sdn, ash, Is,
                         yp, ysh, st);
+        mk->mark();
     } else {
         const float* L_use = logits_or_null;
         if (!L_use) {
             launch_gemm_router(x, T, H, E, (const uint16_t*)wts->router_w, wts->router_b, lg, st);
+            mk->mark();
             L_use = lg;
         }
         launch_topk(L_use, T, E, k, ids, wv, topk_ids_out, topk_w_out, st);
+        mk->mark();
         launch_to_f16(x, x16, (int64_t)T * H, st);
+        mk->mark();
         launch_permute_large(ids, T, k, E, kGemmBM, hist, offs, perm, inv, tiles, nt, st);
-        if (has_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, ysh, st);
+        mk->mark();
+        if (has_sh) {
+            launch_gemm_shared(x, T, H, sug, sdn, Is, ash, ysh, st);
+            mk->mark();
+        }
         launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
+        mk->mark();
         launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, yp, st);
+        mk->mark();
     }
     launch_combine(yp, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+    mk->mark();
     return launched("moe_layer_forward");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                             const uint16_t* x, int32_t T, const float* logits_or_null, float* y,
+                             int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+    Marks mk{nullptr, 0, 0, nullptr};
+    return layer_forward_impl(desc, wts, x, T, logits_or_null, y, topk_ids_out, topk_w_out, ws,
+                              ws_bytes, stream, &mk);
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                   const uint16_t* x, int32_t T, const float* logits_or_null,
+                                   float* y, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                                   size_t ws_bytes, void* stream, void* const* events,
+                                   int32_t n_events, int32_t* n_marks) {
+    if (!events || n_events < 1 || !n_marks) {
+        g_last_error = "events, n_events >= 1 and n_marks are required";
+        return MOE_ERR_NULL;
+    }
+    Marks mk{events, n_events, 0, nullptr};
+    moe_status s = layer_forward_impl(desc, wts, x, T, logits_or_null, y, topk_ids_out, topk_w_out,
+                                      ws, ws_bytes, stream, &mk);
+    *n_marks = mk.used;
+    return s;
 }
 
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
