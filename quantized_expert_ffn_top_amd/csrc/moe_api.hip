@@ -53,8 +53,8 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // ---- workspace layout for one (shape, T)
 struct Ws {
-    size_t x16, part, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm, y_sh,
-        hist, total;
+    size_t x16, part, logits, ids, w, offsets, perm, inv, tiles, ntiles, tok_slot, tok_w, a16,
+        a_sh, y_perm, y_sh, hist, total;
     int max_tiles;
 };
 
@@ -83,8 +83,11 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     s.offsets = take((size_t)(E + 1) * 4);
     s.perm = take(n * 4);
     s.inv = take(n * 4);
-    s.tiles = take((size_t)s.max_tiles * 12);
+    const int gemm_tiles = (int)((n + kGemmBM - 1) / kGemmBM) + (n < (size_t)E ? (int)n : E);
+    s.tiles = take((size_t)(s.max_tiles > gemm_tiles ? s.max_tiles : gemm_tiles) * 12);
     s.ntiles = take(4);
+    s.tok_slot = take((size_t)s.max_tiles * 16 * 4);
+    s.tok_w = take((size_t)s.max_tiles * 16 * 4);
     s.a16 = take(n * I * 2);
     s.a_sh = take((size_t)T * (Is > 0 ? Is : 1) * 2);
     s.y_perm = take(n * H * 4);
@@ -188,7 +191,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     if (T <= kDecMaxT) {
-        launch_router_partial(x, T, H, E, w_r, (float*)ws, st);
+        launch_dec_stage1(x, T, H, E, w_r, (float*)ws, nullptr, 0, nullptr, st);
         launch_router_reduce((const float*)ws, H / kRouterKChunk, T, E, b, logits, st);
     } else {
         launch_gemm_router(x, T, H, E, w_r, b, logits, st);
@@ -223,7 +226,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     if (T <= kDecMaxT) {
-        launch_permute_small(topk_ids, T, E, k, offsets, perm, inv_perm, nullptr, nullptr, st);
+        launch_permute_small(topk_ids, T, E, k, offsets, perm, inv_perm, st);
     } else {
         const size_t hist_b = a256((size_t)((T + 63) / 64) * E * 4);
         const int mt = max_tiles_for(T, E, k);
@@ -253,6 +256,10 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
               Is = desc->shared_inter;
     const Ws L = layout(H, I, E, k, Is, T);
     if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    const int n = T * k;
+    const int gemm_tiles = (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
+    if ((size_t)gemm_tiles * 12 > L.tok_slot - L.tiles)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small for the tile list");
     s = check_device();
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
@@ -265,18 +272,10 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     uint16_t* a16 = at<uint16_t>(ws, L.a16);
     uint16_t* ash = at<uint16_t>(ws, L.a_sh);
     launch_to_f16(x, x16, (int64_t)T * H, st);
-    if (T <= kDecMaxT) {
-        launch_build_tiles(offsets, E, kDecMaxT, tiles, nt, st);
-        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, x, T, H, I,
-                          sug, Is, a16, ash, st);
-        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, sdn, ash, Is,
-                        y_perm, shared_y, st);
-    } else {
-        launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
-        if (do_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, shared_y, st);
-        launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
-        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, y_perm, st);
-    }
+    launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
+    if (do_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, shared_y, st);
+    launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16, st);
+    launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, y_perm, st);
     return launched("moe_expert_ffn");
 }
 
@@ -349,6 +348,8 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     int32_t* inv = at<int32_t>(ws, L.inv);
     int32_t* tiles = at<int32_t>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.ntiles);
+    int32_t* tok_slot = at<int32_t>(ws, L.tok_slot);
+    float* tok_w = at<float>(ws, L.tok_w);
     uint16_t* a16 = at<uint16_t>(ws, L.a16);
     uint16_t* ash = at<uint16_t>(ws, L.a_sh);
     float* yp = at<float>(ws, L.y_perm);
@@ -357,19 +358,22 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
 
     mk->mark();
     if (T <= kDecMaxT) {
-        if (!logits_or_null) {
-            launch_router_partial(x, T, H, E, (const uint16_t*)wts->router_w, part, st);
+        if (!logits_or_null || has_sh) {
+            launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
+                              part, sug, Is, ash, st);
             mk->mark();
         }
         launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, x16, T, E,
-                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt, st);
+                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt,
+                           tok_slot, tok_w, st);
         mk->mark();
-        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, x, T, H, I,
-                          sug, Is, a16, ash, st);
+        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, T, H, I,
+                          a16, st);
         mk->mark();
-        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, sdn, ash, Is,
-                        yp, ysh, st);
+        launch_down_comb_dec(ex, wts->expert_stride, tiles, nt, tok_slot, tok_w, a16, T, H, I, sdn,
+                             ash, Is, y, st);
         mk->mark();
+        return launched("moe_layer_forward");
     } else {
         const float* L_use = logits_or_null;
         if (!L_use) {
