@@ -59,9 +59,9 @@ def upgate_bytes(T, U):
 
 
 def down_bytes(T, U):
-    """Down + combine kernel: packed down of the U experts + shared down + a
-    (routed fp16, shared bf16) read + y written."""
-    return U * DN_BYTES + SH_DN_BYTES + T * K * I * 2 + T * IS * 2 + T * H * 4
+    """Down kernel: packed down of the U experts + shared down + a (routed
+    fp16, shared bf16) read + unweighted outputs (permuted rows, shared) written."""
+    return U * DN_BYTES + SH_DN_BYTES + T * K * I * 2 + T * IS * 2 + T * K * H * 4 + T * H * 4
 
 
 def layer_bytes(T, U):
@@ -161,12 +161,12 @@ def main():
         U = float(np.mean(us))
         lb = layer_bytes(T, U)
         kd = time_kernels(T, x, max(args.layers, 16), args.layers, 8)
-        names = ["stage1", "route", "upgate", "down_combine"]
+        names = ["stage1", "route", "upgate", "down", "combine"]
         kern = {}
         for nm, t in zip(names, kd):
             kern[nm] = {"us": round(t * 1e3, 2)}
         for nm, b, j in (("stage1", stage1_bytes(T), 0), ("upgate", upgate_bytes(T, U), 2),
-                         ("down_combine", down_bytes(T, U), 3)):
+                         ("down", down_bytes(T, U), 3)):
             kern[nm]["GBps"] = round(b / (kd[j] * 1e-3) / 1e9, 1)
             kern[nm]["hbm_frac"] = round(b / (kd[j] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         results["decode"][T] = {

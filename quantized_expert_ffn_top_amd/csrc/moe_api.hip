@@ -53,8 +53,8 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // ---- workspace layout for one (shape, T)
 struct Ws {
-    size_t x16, part, logits, ids, w, offsets, perm, inv, tiles, ntiles, tok_slot, tok_w, a16,
-        a_sh, y_perm, y_sh, hist, total;
+    size_t x16, part, shp, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm,
+        y_sh, hist, total;
     int max_tiles;
 };
 
@@ -77,6 +77,7 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     s.max_tiles = max_tiles_for(T, E, k);
     s.x16 = take((size_t)T * H * 2);
     s.part = take((size_t)(H / kRouterKChunk) * tdec * E * 4);
+    s.shp = take((size_t)(H / kRouterKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
     s.logits = take((size_t)T * E * 4);
     s.ids = take(n * 4);
     s.w = take(n * 4);
@@ -86,8 +87,6 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     const int gemm_tiles = (int)((n + kGemmBM - 1) / kGemmBM) + (n < (size_t)E ? (int)n : E);
     s.tiles = take((size_t)(s.max_tiles > gemm_tiles ? s.max_tiles : gemm_tiles) * 12);
     s.ntiles = take(4);
-    s.tok_slot = take((size_t)s.max_tiles * 16 * 4);
-    s.tok_w = take((size_t)s.max_tiles * 16 * 4);
     s.a16 = take(n * I * 2);
     s.a_sh = take((size_t)T * (Is > 0 ? Is : 1) * 2);
     s.y_perm = take(n * H * 4);
@@ -258,7 +257,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
     const int n = T * k;
     const int gemm_tiles = (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
-    if ((size_t)gemm_tiles * 12 > L.tok_slot - L.tiles)
+    if ((size_t)gemm_tiles * 12 > L.ntiles - L.tiles)
         return fail(MOE_ERR_WORKSPACE, "workspace too small for the tile list");
     s = check_device();
     if (s != MOE_OK) return s;
@@ -340,6 +339,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     const uint16_t* sdn = has_sh ? (const uint16_t*)wts->shared_down : nullptr;
     uint16_t* x16 = at<uint16_t>(ws, L.x16);
     float* part = at<float>(ws, L.part);
+    float* shp = at<float>(ws, L.shp);
     float* lg = at<float>(ws, L.logits);
     int32_t* ids = at<int32_t>(ws, L.ids);
     float* wv = at<float>(ws, L.w);
@@ -348,8 +348,6 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     int32_t* inv = at<int32_t>(ws, L.inv);
     int32_t* tiles = at<int32_t>(ws, L.tiles);
     int32_t* nt = at<int32_t>(ws, L.ntiles);
-    int32_t* tok_slot = at<int32_t>(ws, L.tok_slot);
-    float* tok_w = at<float>(ws, L.tok_w);
     uint16_t* a16 = at<uint16_t>(ws, L.a16);
     uint16_t* ash = at<uint16_t>(ws, L.a_sh);
     float* yp = at<float>(ws, L.y_perm);
@@ -360,20 +358,18 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     if (T <= kDecMaxT) {
         if (!logits_or_null || has_sh) {
             launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
-                              part, sug, Is, ash, st);
+                              part, sug, Is, shp, st);
             mk->mark();
         }
         launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, x16, T, E,
-                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt,
-                           tok_slot, tok_w, st);
+                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt, st);
         mk->mark();
         launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, T, H, I,
-                          a16, st);
+                          a16, has_sh ? shp : nullptr, Is, ash, st);
         mk->mark();
-        launch_down_comb_dec(ex, wts->expert_stride, tiles, nt, tok_slot, tok_w, a16, T, H, I, sdn,
-                             ash, Is, y, st);
+        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, k, sdn, ash,
+                        Is, yp, ysh, st);
         mk->mark();
-        return launched("moe_layer_forward");
     } else {
         const float* L_use = logits_or_null;
         if (!L_use) {

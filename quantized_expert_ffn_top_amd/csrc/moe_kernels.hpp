@@ -24,7 +24,7 @@ void launch_route_small(const float* part, int nkc, const float* bias, const flo
                         const uint16_t* x, int H, uint16_t* x16, int T, int E, int k,
                         int32_t* ids, float* w, int32_t* ids_out, float* w_out,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* ntiles, int32_t* tok_slot, float* tok_w, hipStream_t st);
+                        int32_t* ntiles, hipStream_t st);
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t st);
 void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32_t* hist,
@@ -39,15 +39,15 @@ void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps,
 
 // ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
-                       const uint16_t* sh_ug, int Is, uint16_t* a_sh, hipStream_t st);
+                       const uint16_t* sh_ug, int Is, float* shp, hipStream_t st);
 void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                        const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                        const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                       hipStream_t st);
-void launch_down_comb_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
-                          const int32_t* ntiles, const int32_t* tok_slot, const float* tok_w,
-                          const uint16_t* a16_perm, int T, int H, int I, const uint16_t* sh_down,
-                          const uint16_t* a_sh, int Is, float* y, hipStream_t st);
+                       const float* shp, int Is, uint16_t* a_sh, hipStream_t st);
+void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
+                     const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T, int H,
+                     int I, int k, const uint16_t* sh_down, const uint16_t* a_sh, int Is,
+                     float* y_perm, float* y_sh, hipStream_t st);
 
 // ---- grouped-GEMM path (moe_kernels_gemm.hip)
 void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,

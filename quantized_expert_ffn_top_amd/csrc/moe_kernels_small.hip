@@ -126,17 +126,12 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* lds, int& total)
 }
 
 // Stable counting sort of the n = T*k slots of at most 16 tokens, by one
-// workgroup of 1024 threads.  s_ids / s_w hold the expert and weight of each
-// slot, s_cnt the per-expert counts.  Writes offsets [E+1], perm, inv, the
-// active experts as tiles (expert, first row, rows) in ascending expert
-// order, and -- if tok_slot is given -- the token-major view of each tile:
-// tok_slot[16*a + t] = permuted row of token t in tile a (or -1) and
-// tok_w[16*a + t] = its routing weight (or 0).
-__device__ void small_counting_sort(const int* s_ids, const float* s_w, int* s_cnt,
-                                    int* s_tile, int* s_scan, int T, int E, int k,
-                                    int32_t* offsets, int32_t* perm, int32_t* inv,
-                                    int32_t* tiles, int32_t* ntiles, int32_t* tok_slot,
-                                    float* tok_w) {
+// workgroup of 1024 threads.  s_ids holds the expert of each slot, s_cnt the
+// per-expert counts.  Writes offsets [E+1], perm, inv and (if `tiles`) the
+// active experts as tiles (expert, first row, rows) in ascending expert order.
+__device__ void small_counting_sort(const int* s_ids, int* s_cnt, int* s_scan, int T, int E,
+                                    int k, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                    int32_t* tiles, int32_t* ntiles) {
     const int tid = threadIdx.x;
     int c = (tid < E) ? s_cnt[tid] : 0;
     int tot_c, tot_a;
@@ -144,7 +139,6 @@ __device__ void small_counting_sort(const int* s_ids, const float* s_w, int* s_c
     int aidx = block_excl_scan_1024(c > 0 ? 1 : 0, s_scan, tot_a);
     if (tid < E) {
         offsets[tid] = off;
-        s_tile[tid] = aidx;
         if (c > 0 && tiles) {
             tiles[3 * aidx + 0] = tid;
             tiles[3 * aidx + 1] = off;
@@ -156,11 +150,6 @@ __device__ void small_counting_sort(const int* s_ids, const float* s_w, int* s_c
         if (ntiles) *ntiles = tot_a;
     }
     s_cnt[tid] = off;                          // reuse: first row of each expert
-    if (tok_slot)
-        for (int i = tid; i < tot_a * 16; i += 1024) {
-            tok_slot[i] = -1;
-            tok_w[i] = 0.f;
-        }
     __syncthreads();
     // slot f = t*k + j goes to first(e) + number of earlier tokens routed to e
     // (a token selects an expert at most once)
@@ -172,10 +161,6 @@ __device__ void small_counting_sort(const int* s_ids, const float* s_w, int* s_c
         const int p = s_cnt[e] + rank;
         perm[p] = tid;
         inv[tid] = p;
-        if (tok_slot) {
-            tok_slot[16 * s_tile[e] + t] = p;
-            tok_w[16 * s_tile[e] + t] = s_w[tid];
-        }
     }
 }
 
@@ -190,13 +175,10 @@ __global__ void __launch_bounds__(1024) k_route_small(
     uint16_t* __restrict__ x16, int T, int E, int k,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles,
-    int32_t* __restrict__ tok_slot, float* __restrict__ tok_w) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
     __shared__ float s_log[16 * 1024];
     __shared__ int s_ids[16 * 32];
-    __shared__ float s_w[16 * 32];
     __shared__ int s_cnt[1024];
-    __shared__ int s_tile[1024];
     __shared__ int s_scan[40];
     const int tid = threadIdx.x, lane = __lane_id(), wid = tid >> 6;
 
@@ -216,19 +198,29 @@ __global__ void __launch_bounds__(1024) k_route_small(
     if (given_logits) {
         for (int i = tid; i < nl; i += 1024) s_log[i] = given_logits[i];
     } else {
-        for (int i = tid; i < nl; i += 1024) {
-            // chunks summed in ascending order; loads issued four at a time
-            float acc = 0.f;
-            int c = 0;
-            for (; c + 4 <= nkc; c += 4) {
-                const float a0 = part[(int64_t)(c + 0) * nl + i];
-                const float a1 = part[(int64_t)(c + 1) * nl + i];
-                const float a2 = part[(int64_t)(c + 2) * nl + i];
-                const float a3 = part[(int64_t)(c + 3) * nl + i];
-                acc = (((acc + a0) + a1) + a2) + a3;
+        // every partial of this thread's (up to 16) logits is loaded before any
+        // is summed; chunks are summed in ascending order
+        for (int i0 = 0; i0 < nl; i0 += 4 * 1024) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < nkc; c0 += 8) {
+                float v[4][8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const int i = i0 + u * 1024 + tid;
+                        v[u][c] = (i < nl && c0 + c < nkc) ? part[(int64_t)(c0 + c) * nl + i] : 0.f;
+                    }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[u] += v[u][c];
             }
-            for (; c < nkc; ++c) acc += part[(int64_t)c * nl + i];
-            s_log[i] = bias ? acc + bias[i % E] : acc;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * 1024 + tid;
+                if (i < nl) s_log[i] = bias ? acc[u] + bias[i % E] : acc[u];
+            }
         }
     }
     __syncthreads();
@@ -246,13 +238,11 @@ __global__ void __launch_bounds__(1024) k_route_small(
             if (ids_out) ids_out[t * k + lane] = id;
             if (w_out) w_out[t * k + lane] = wt;
             s_ids[t * k + lane] = id;
-            s_w[t * k + lane] = wt;
             atomicAdd(&s_cnt[id], 1);
         }
     }
     __syncthreads();
-    small_counting_sort(s_ids, s_w, s_cnt, s_tile, s_scan, T, E, k, offsets, perm, inv, tiles,
-                        ntiles, tok_slot, tok_w);
+    small_counting_sort(s_ids, s_cnt, s_scan, T, E, k, offsets, perm, inv, tiles, ntiles);
 }
 
 // Stand-alone counting sort for T <= 16 (same code as the decode routing).
@@ -260,21 +250,17 @@ __global__ void __launch_bounds__(1024) k_permute_small(
     const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
     __shared__ int s_ids[16 * 32];
-    __shared__ float s_w[16 * 32];
     __shared__ int s_cnt[1024];
-    __shared__ int s_tile[1024];
     __shared__ int s_scan[40];
     const int tid = threadIdx.x;
     s_cnt[tid] = 0;
     __syncthreads();
     if (tid < T * k) {
         s_ids[tid] = ids[tid];
-        s_w[tid] = 0.f;
         atomicAdd(&s_cnt[ids[tid]], 1);
     }
     __syncthreads();
-    small_counting_sort(s_ids, s_w, s_cnt, s_tile, s_scan, T, E, k, offsets, perm, inv, nullptr,
-                        nullptr, nullptr, nullptr);
+    small_counting_sort(s_ids, s_cnt, s_scan, T, E, k, offsets, perm, inv, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------- permute
@@ -477,10 +463,9 @@ void launch_route_small(const float* part, int nkc, const float* bias, const flo
                         const uint16_t* x, int H, uint16_t* x16, int T, int E, int k,
                         int32_t* ids, float* w, int32_t* ids_out, float* w_out,
                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* ntiles, int32_t* tok_slot, float* tok_w, hipStream_t st) {
+                        int32_t* ntiles, hipStream_t st) {
     k_route_small<<<1, 1024, 0, st>>>(part, nkc, bias, given, x, H, x16, T, E, k, ids, w,
-                                      ids_out, w_out, offsets, perm, inv, tiles, ntiles, tok_slot,
-                                      tok_w);
+                                      ids_out, w_out, offsets, perm, inv, tiles, ntiles);
 }
 
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
