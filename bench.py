@@ -78,11 +78,21 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="run only the workload read by rocprofv3 counter passes: decode T=8 "
+                        "layers and a 1 GiB device copy (the byte-count calibration)")
+    p.add_argument("--summarize", nargs="+", metavar="CSV",
+                   help="print per-(kernel, grid) tables of rocprofv3 kernel-trace or "
+                        "counter-collection CSV files and exit")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize:
+        for path in args.summarize:
+            summarize_csv(path)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); "
               "got --gpus %d" % args.gpus, file=sys.stderr)
@@ -152,6 +162,20 @@ def main():
             for j in range(n_marks - 1):
                 dur[j] += row[j].elapsed_time(row[j + 1])
         return dur / steps
+
+    if args.traffic_probe:
+        x = synth.tokens_bf16(8, sh.hidden, 2, 0).to(dev)
+        y = torch.empty((8, sh.hidden), dtype=torch.float32, device=dev)
+        for i in range(2 * args.layers):
+            Q.moe_layer_forward(d, wts[i % args.layers], x, y, ws)
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("# traffic probe: %d decode layers at T=8, 4 copies of %d bytes" % (
+            2 * args.layers, src.numel()), file=sys.stderr)
+        return
 
     results = {"decode": {}, "prefill": None}
     for T in (1, 3, 8):
@@ -230,20 +254,75 @@ def main():
     print(json.dumps(line))
 
 
+def summarize_csv(path):
+    """Group a rocprofv3 CSV by (kernel, grid size): dispatch count and mean /
+    min / max duration (kernel trace), or mean value per counter (counter
+    collection).  Kernels of the library only, plus the runtime's copy kernel."""
+    import collections
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    if not rows:
+        print("%s: empty" % path)
+        return
+    cols = rows[0].keys()
+    gcols = [c for c in cols if c.startswith("Grid_Size")]
+
+    def short(name):
+        name = name.split("(")[0]
+        return name.replace("void ", "").replace("moe::", "")
+
+    def keep(name):
+        return "moe::" in name or "copyBuffer" in name
+
+    def grid(r):
+        g = 1
+        for c in gcols:
+            g *= max(int(float(r[c])), 1)
+        return g
+
+    print("### %s" % os.path.basename(path))
+    if "Counter_Name" in cols:
+        agg = collections.defaultdict(list)
+        for r in rows:
+            if keep(r["Kernel_Name"]):
+                agg[(short(r["Kernel_Name"]), grid(r), r["Counter_Name"])].append(
+                    float(r["Counter_Value"]))
+        print("| kernel | grid (work-items) | counter | dispatches | mean per dispatch |")
+        print("|---|---|---|---|---|")
+        for (k, g, c), v in sorted(agg.items()):
+            print("| %s | %d | %s | %d | %.6g |" % (k, g, c, len(v), sum(v) / len(v)))
+    else:
+        agg = collections.defaultdict(list)
+        for r in rows:
+            if keep(r["Kernel_Name"]):
+                agg[(short(r["Kernel_Name"]), grid(r))].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print("| kernel | grid (work-items) | dispatches | mean us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for (k, g), v in sorted(agg.items()):
+            print("| %s | %d | %d | %.2f | %.2f | %.2f |" % (k, g, len(v), sum(v) / len(v),
+                                                            min(v), max(v)))
+    print()
+
+
+def source_digest(files):
+    """sha256 over the named kernel sources, in order (the kernel's identity)."""
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "quantized_expert_ffn_top_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel, algo_bytes):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current source of the kernel's file; else None."""
+    taken on the current source of the kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(path))[kernel]
-    except Exception:
+        sha = source_digest(rec["sources"])
+    except (OSError, KeyError, ValueError):
         return None
-    src = os.path.join(ROOT, "quantized_expert_ffn_top_amd", "csrc", rec["source"])
-    try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except OSError:
-        return None
-    if sha != rec.get("source_sha256"):
+    if sha != rec.get("sources_sha256"):
         return None
     return rec.get("hbm_bytes_per_launch")
 

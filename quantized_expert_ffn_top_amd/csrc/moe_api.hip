@@ -190,7 +190,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     if (T <= kDecMaxT) {
-        launch_dec_stage1(x, T, H, E, w_r, (float*)ws, nullptr, 0, nullptr, st);
+        launch_dec_stage1(x, T, H, E, w_r, (float*)ws, nullptr, 0, nullptr, nullptr, st);
         launch_router_reduce((const float*)ws, H / kRouterKChunk, T, E, b, logits, st);
     } else {
         launch_gemm_router(x, T, H, E, w_r, b, logits, st);
@@ -356,13 +356,14 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
 
     mk->mark();
     if (T <= kDecMaxT) {
-        if (!logits_or_null || has_sh) {
-            launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
-                              part, sug, Is, shp, st);
-            mk->mark();
-        }
-        launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, x16, T, E,
-                           k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt, st);
+        // stage 1 always runs: router partials (no given logits), shared up|gate
+        // partials (shared expert present) and the fp16 copy of x
+        launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
+                          part, sug, Is, shp, x16, st);
+        mk->mark();
+        launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, nullptr,
+                           T, E, k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt,
+                           st);
         mk->mark();
         launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, T, H, I,
                           a16, has_sh ? shp : nullptr, Is, ash, st);

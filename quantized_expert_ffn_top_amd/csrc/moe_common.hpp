@@ -95,31 +95,38 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// ---------------------------------------------------------------- top-k key
+// ---------------------------------------------------------------- top-k
 // Total order used by the routing: larger logit first, then lower expert
-// index.  -0.0 is folded onto +0.0 so equal values compare equal.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+// index.  Logits are compared through an order-preserving u32 key (-0.0 is
+// folded onto +0.0 so equal values compare equal).
+__device__ __forceinline__ uint32_t order_key(float v) {
     uint32_t u = __float_as_uint(v);
     if (u == 0x80000000u) u = 0u;
-    uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)k << 32) | (uint32_t)(~(uint32_t)e);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ int topk_key_index(uint64_t key) {
-    return (int)(~(uint32_t)key);
-}
-__device__ __forceinline__ float topk_key_value(uint64_t key) {
-    uint32_t k = (uint32_t)(key >> 32);
-    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-    return __uint_as_float(u);
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+// Wave-wide max / min of a u32 through DPP row permutations (max over each
+// 16-lane row) and four lane reads; the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));  // xor 1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));  // xor 2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false)); // half mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false)); // mirror
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -130,29 +137,37 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 // Exact top-k of one row of E logits by one wave64 (E <= 1024, k <= 32).
 // Lane j < k returns (id_j, L_j) in selection order; other lanes return
-// (-1, 0).  `get(e)` yields the fp32 logit of expert e.
+// (-1, 0).  `get(e)` yields the fp32 logit of expert e (lane l holds experts
+// l, l+64, ...).  Each round: the largest value key over the wave, then the
+// lowest expert index among the lanes holding that value.
 template <typename Get>
 __device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, float& out_val) {
     const int lane = __lane_id();
-    uint64_t keys[16];
+    uint32_t keys[16];
+    uint32_t alive = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        int e = lane + 64 * i;
-        keys[i] = (e < E) ? topk_key(get(e), e) : 0ull;
+        const int e = lane + 64 * i;
+        keys[i] = (e < E) ? order_key(get(e)) : 0u;
+        alive |= (e < E) ? (1u << i) : 0u;
     }
     out_id = -1;
     out_val = 0.f;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0ull;
+        uint32_t best = 0u, bi = 16u;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) best = keys[i] > best ? keys[i] : best;
-        uint64_t win = wave_max_u64(best);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (keys[i] == win) keys[i] = 0ull;      // keys are unique (index part)
+        for (int i = 0; i < 16; ++i) {
+            const bool take = ((alive >> i) & 1u) && (bi == 16u || keys[i] > best);
+            best = take ? keys[i] : best;
+            bi = take ? (uint32_t)i : bi;
+        }
+        const uint32_t m = wave_max_u32(bi < 16u ? best : 0u);
+        const uint32_t cand = (bi < 16u && best == m) ? (uint32_t)lane + 64u * bi : 0xffffffffu;
+        const uint32_t win = wave_min_u32(cand);
+        if ((int)(win & 63u) == lane) alive &= ~(1u << (win >> 6));
         if (lane == j) {
-            out_id = topk_key_index(win);
-            out_val = topk_key_value(win);
+            out_id = (int)win;
+            out_val = order_key_value(m);
         }
     }
 }
@@ -160,10 +175,9 @@ __device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, fl
 // Softmax over the k selected logits held by lanes 0..k-1 (lane 0 = max).
 __device__ __forceinline__ float wave_softmax_selected(float v, int k) {
     const int lane = __lane_id();
-    float m = __shfl(v, 0, 64);
-    float ex = (lane < k) ? expf(v - m) : 0.f;
-    float s = wave_sum_f32(ex);
-    return ex / s;
+    const float m = __shfl(v, 0, 64);
+    const float ex = (lane < k) ? expf(v - m) : 0.f;
+    return ex / wave_sum_f32(ex);
 }
 
 // ---------------------------------------------------------------- decoders

@@ -39,7 +39,7 @@ void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps,
 
 // ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
-                       const uint16_t* sh_ug, int Is, float* shp, hipStream_t st);
+                       const uint16_t* sh_ug, int Is, float* shp, uint16_t* x16, hipStream_t st);
 void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                        const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                        const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,

@@ -27,14 +27,28 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // Items [n_r, n_r + n_s): shared expert up|gate partials of 16 rows (rows
 // 0..Is-1 up, Is..2Is-1 gate) over one K chunk, shp[kc][t][2 Is]; summed and
 // passed through SwiGLU by the up|gate kernel.  A = tokens (bf16, rows >= T
-// zero), B = bf16 weight rows, 16x16x32 bf16 steps.
+// zero), B = bf16 weight rows, 16x16x32 bf16 steps.  The last H/256 waves
+// write the fp16 copy of the tokens, one 256-wide K chunk each.
 __global__ void __launch_bounds__(512) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
                                                     int E, const uint16_t* __restrict__ w_r,
                                                     float* __restrict__ part, int n_r,
                                                     const uint16_t* __restrict__ sh_ug, int Is,
-                                                    float* __restrict__ shp, int n_s) {
+                                                    float* __restrict__ shp, int n_s,
+                                                    uint16_t* __restrict__ x16) {
     const int lane = __lane_id();
     const int wi = blockIdx.x * 8 + (int)(threadIdx.x >> 6);
+    const int n_x = H / kRouterKChunk;               // waves [n_r + n_s, +n_x): fp16 copy of x
+    if (wi >= n_r + n_s && wi < n_r + n_s + n_x) {
+        const int k0 = (wi - n_r - n_s) * kRouterKChunk;
+        for (int i = lane; i < T * (kRouterKChunk / 4); i += 64) {
+            const int t = i / (kRouterKChunk / 4), c = (i % (kRouterKChunk / 4)) * 4;
+            const uint2 v = *reinterpret_cast<const uint2*>(x + (int64_t)t * H + k0 + c);
+            *reinterpret_cast<uint2*>(x16 + (int64_t)t * H + k0 + c) = make_uint2(
+                pack2(f32_to_f16_bits(bf16_to_f32(v.x & 0xffffu)), f32_to_f16_bits(bf16_to_f32(v.x >> 16))),
+                pack2(f32_to_f16_bits(bf16_to_f32(v.y & 0xffffu)), f32_to_f16_bits(bf16_to_f32(v.y >> 16))));
+        }
+        return;
+    }
     const int r = lane & 15, g = lane >> 4;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bool vt = r < T;
@@ -370,12 +384,14 @@ __global__ void __launch_bounds__(256) k_down_dec(
 // ---------------------------------------------------------------- launchers
 
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
-                       const uint16_t* sh_ug, int Is, float* shp, hipStream_t st) {
+                       const uint16_t* sh_ug, int Is, float* shp, uint16_t* x16, hipStream_t st) {
     const int nkc = H / kRouterKChunk;
     const int n_r = w_r ? ((E + 15) / 16) * nkc : 0;
     const int n_s = (sh_ug && Is > 0) ? (2 * Is / 16) * nkc : 0;
-    if (n_r + n_s == 0) return;
-    k_dec_stage1<<<(n_r + n_s + 7) / 8, 512, 0, st>>>(x, T, H, E, w_r, part, n_r, sh_ug, Is, shp, n_s);
+    const int n_x = x16 ? nkc : 0;
+    if (n_r + n_s + n_x == 0) return;
+    k_dec_stage1<<<(n_r + n_s + n_x + 7) / 8, 512, 0, st>>>(x, T, H, E, w_r, part, n_r, sh_ug, Is,
+                                                            shp, n_s, x16);
 }
 
 template <int GPW, bool FULL>

@@ -126,19 +126,24 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* lds, int& total)
 }
 
 // Stable counting sort of the n = T*k slots of at most 16 tokens, by one
-// workgroup of 1024 threads.  s_ids holds the expert of each slot, s_cnt the
-// per-expert counts.  Writes offsets [E+1], perm, inv and (if `tiles`) the
-// active experts as tiles (expert, first row, rows) in ascending expert order.
-__device__ void small_counting_sort(const int* s_ids, int* s_cnt, int* s_scan, int T, int E,
-                                    int k, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                    int32_t* tiles, int32_t* ntiles) {
+// workgroup of 1024 threads.  s_ids holds the expert of each slot and
+// s_mask[e] the set of tokens (bit t) that selected expert e; a token
+// selects an expert at most once, so the rank of slot (t, j) inside expert e
+// is the number of set bits of s_mask[e] below bit t.  Writes offsets [E+1],
+// perm, inv and (if `tiles`) the active experts as tiles (expert, first row,
+// rows) in ascending expert order.
+__device__ void small_counting_sort(const int* s_ids, const uint32_t* s_mask, int* s_first,
+                                    int* s_scan, int T, int E, int k, int32_t* offsets,
+                                    int32_t* perm, int32_t* inv, int32_t* tiles,
+                                    int32_t* ntiles) {
     const int tid = threadIdx.x;
-    int c = (tid < E) ? s_cnt[tid] : 0;
+    const int c = (tid < E) ? __popc(s_mask[tid]) : 0;
     int tot_c, tot_a;
-    int off = block_excl_scan_1024(c, s_scan, tot_c);
-    int aidx = block_excl_scan_1024(c > 0 ? 1 : 0, s_scan, tot_a);
+    const int off = block_excl_scan_1024(c, s_scan, tot_c);
+    const int aidx = block_excl_scan_1024(c > 0 ? 1 : 0, s_scan, tot_a);
     if (tid < E) {
         offsets[tid] = off;
+        s_first[tid] = off;
         if (c > 0 && tiles) {
             tiles[3 * aidx + 0] = tid;
             tiles[3 * aidx + 1] = off;
@@ -149,16 +154,10 @@ __device__ void small_counting_sort(const int* s_ids, int* s_cnt, int* s_scan, i
         offsets[E] = tot_c;
         if (ntiles) *ntiles = tot_a;
     }
-    s_cnt[tid] = off;                          // reuse: first row of each expert
     __syncthreads();
-    // slot f = t*k + j goes to first(e) + number of earlier tokens routed to e
-    // (a token selects an expert at most once)
-    const int n = T * k;
-    if (tid < n) {
+    if (tid < T * k) {
         const int t = tid / k, e = s_ids[tid];
-        int rank = 0;
-        for (int f2 = 0; f2 < t * k; ++f2) rank += (s_ids[f2] == e) ? 1 : 0;
-        const int p = s_cnt[e] + rank;
+        const int p = s_first[e] + __popc(s_mask[e] & ((1u << t) - 1u));
         perm[p] = tid;
         inv[tid] = p;
     }
@@ -178,13 +177,14 @@ __global__ void __launch_bounds__(1024) k_route_small(
     int32_t* __restrict__ inv, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
     __shared__ float s_log[16 * 1024];
     __shared__ int s_ids[16 * 32];
-    __shared__ int s_cnt[1024];
+    __shared__ uint32_t s_mask[1024];
+    __shared__ int s_first[1024];
     __shared__ int s_scan[40];
     const int tid = threadIdx.x, lane = __lane_id(), wid = tid >> 6;
 
-    s_cnt[tid] = 0;
-    // fp16 copy of x, 8 elements per thread per step (T*H % 8 == 0, 16-byte aligned)
-    const int n8 = T * H / 8;
+    s_mask[tid] = 0u;
+    // fp16 copy of x (when stage 1 did not make it), 8 elements per step
+    const int n8 = x16 ? T * H / 8 : 0;
     for (int i = tid; i < n8; i += 1024) {
         const u32x4 v = ld16(x + 8 * (int64_t)i);
         u32x4 o;
@@ -238,11 +238,11 @@ __global__ void __launch_bounds__(1024) k_route_small(
             if (ids_out) ids_out[t * k + lane] = id;
             if (w_out) w_out[t * k + lane] = wt;
             s_ids[t * k + lane] = id;
-            atomicAdd(&s_cnt[id], 1);
+            atomicOr(&s_mask[id], 1u << t);
         }
     }
     __syncthreads();
-    small_counting_sort(s_ids, s_cnt, s_scan, T, E, k, offsets, perm, inv, tiles, ntiles);
+    small_counting_sort(s_ids, s_mask, s_first, s_scan, T, E, k, offsets, perm, inv, tiles, ntiles);
 }
 
 // Stand-alone counting sort for T <= 16 (same code as the decode routing).
@@ -250,17 +250,19 @@ __global__ void __launch_bounds__(1024) k_permute_small(
     const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
     __shared__ int s_ids[16 * 32];
-    __shared__ int s_cnt[1024];
+    __shared__ uint32_t s_mask[1024];
+    __shared__ int s_first[1024];
     __shared__ int s_scan[40];
     const int tid = threadIdx.x;
-    s_cnt[tid] = 0;
+    s_mask[tid] = 0u;
     __syncthreads();
     if (tid < T * k) {
         s_ids[tid] = ids[tid];
-        atomicAdd(&s_cnt[ids[tid]], 1);
+        atomicOr(&s_mask[ids[tid]], 1u << (tid / k));
     }
     __syncthreads();
-    small_counting_sort(s_ids, s_cnt, s_scan, T, E, k, offsets, perm, inv, nullptr, nullptr);
+    small_counting_sort(s_ids, s_mask, s_first, s_scan, T, E, k, offsets, perm, inv, nullptr,
+                        nullptr);
 }
 
 // ---------------------------------------------------------------- permute
