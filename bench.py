@@ -80,7 +80,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only the workload read by rocprofv3 counter passes: decode T=8 "
-                        "layers and a 1 GiB device copy (the byte-count calibration)")
+                        "layers rotated as in the timed loop")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run only four 1 GiB device-to-device copies (the byte calibration "
+                        "of the rocprofv3 traffic counters)")
     p.add_argument("--summarize", nargs="+", metavar="CSV",
                    help="print per-(kernel, grid) tables of rocprofv3 kernel-trace or "
                         "counter-collection CSV files and exit")
@@ -106,6 +109,14 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("# copy probe: 4 copies of %d bytes" % src.numel(), file=sys.stderr)
+        return
     Q.load()
     sh = synth.REAL
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
@@ -168,13 +179,8 @@ def main():
         y = torch.empty((8, sh.hidden), dtype=torch.float32, device=dev)
         for i in range(2 * args.layers):
             Q.moe_layer_forward(d, wts[i % args.layers], x, y, ws)
-        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
         torch.cuda.synchronize()
-        print("# traffic probe: %d decode layers at T=8, 4 copies of %d bytes" % (
-            2 * args.layers, src.numel()), file=sys.stderr)
+        print("# traffic probe: %d decode layers at T=8" % (2 * args.layers), file=sys.stderr)
         return
 
     results = {"decode": {}, "prefill": None}

@@ -21,8 +21,11 @@ moe_status fail(moe_status s, const std::string& msg) {
 // ---- device check (cached per device id)
 std::mutex g_dev_mu;
 int g_dev_ok[64];   // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[64];  // compute units of each checked device
 
-moe_status check_device() {
+// Checks that the current device is gfx950; `n_cu` (optional) receives its
+// compute-unit count, the grid of the persistent kernels.
+moe_status check_device(int* n_cu = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
     if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device id out of range");
@@ -32,8 +35,10 @@ moe_status check_device() {
         if (hipGetDeviceProperties(&p, dev) != hipSuccess)
             return fail(MOE_ERR_HIP, "hipGetDeviceProperties failed");
         g_dev_ok[dev] = (std::string(p.gcnArchName).rfind("gfx950", 0) == 0) ? 1 : 2;
+        g_dev_cus[dev] = p.multiProcessorCount > 0 ? p.multiProcessorCount : 1;
     }
     if (g_dev_ok[dev] != 1) return fail(MOE_ERR_DEVICE, "current device is not gfx950");
+    if (n_cu) *n_cu = g_dev_cus[dev];
     return MOE_OK;
 }
 
@@ -58,9 +63,15 @@ struct Ws {
     int max_tiles;
 };
 
-int max_tiles_for(int T, int E, int k) {
+// The layer runs the bandwidth path for T <= kDecMaxT tokens when its up|gate
+// kernel can stage two items of the hidden size; otherwise the grouped GEMMs.
+bool dec_path(int T, int H) { return T <= kDecMaxT && upgate_dec_supported(H); }
+
+// tiles of the expert kernels: one per active expert (bandwidth path) or per
+// kGemmBM rows of an expert (grouped GEMM)
+int max_tiles_for(int T, int E, int k, bool dec) {
     const int n = T * k;
-    if (T <= kDecMaxT) return n < E ? n : E;
+    if (dec) return n < E ? n : E;
     return (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
 }
 
@@ -74,7 +85,7 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     };
     const size_t n = (size_t)T * k;
     const int tdec = T < kDecMaxT ? T : kDecMaxT;
-    s.max_tiles = max_tiles_for(T, E, k);
+    s.max_tiles = max_tiles_for(T, E, k, dec_path(T, H));
     s.x16 = take((size_t)T * H * 2);
     s.part = take((size_t)(H / kRouterKChunk) * tdec * E * 4);
     s.shp = take((size_t)(H / kRouterKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
@@ -146,7 +157,7 @@ T* at(void* ws, size_t off) {
 
 size_t permute_ws_bytes(int T, int k, int E) {
     if (T <= kDecMaxT) return 0;
-    const int mt = max_tiles_for(T, E, k);
+    const int mt = max_tiles_for(T, E, k, false);
     return a256((size_t)((T + 63) / 64) * E * 4) + a256((size_t)mt * 12) + 256;
 }
 
@@ -228,7 +239,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
         launch_permute_small(topk_ids, T, E, k, offsets, perm, inv_perm, st);
     } else {
         const size_t hist_b = a256((size_t)((T + 63) / 64) * E * 4);
-        const int mt = max_tiles_for(T, E, k);
+        const int mt = max_tiles_for(T, E, k, false);
         int32_t* hist = at<int32_t>(ws, 0);
         int32_t* tiles = at<int32_t>(ws, hist_b);
         int32_t* nt = at<int32_t>(ws, hist_b + a256((size_t)mt * 12));
@@ -329,7 +340,8 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
               Is = desc->shared_inter;
     const Ws L = layout(H, I, E, k, Is, T);
     if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
-    s = check_device();
+    int n_cu = 0;
+    s = check_device(&n_cu);
     if (s != MOE_OK) return s;
 
     hipStream_t st = (hipStream_t)stream;
@@ -355,7 +367,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     int32_t* hist = at<int32_t>(ws, L.hist);
 
     mk->mark();
-    if (T <= kDecMaxT) {
+    if (dec_path(T, H)) {
         // stage 1 always runs: router partials (no given logits), shared up|gate
         // partials (shared expert present) and the fp16 copy of x
         launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
@@ -366,7 +378,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
                            st);
         mk->mark();
         launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, T, H, I,
-                          a16, has_sh ? shp : nullptr, Is, ash, st);
+                          a16, has_sh ? shp : nullptr, Is, ash, n_cu, st);
         mk->mark();
         launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, k, sdn, ash,
                         Is, yp, ysh, st);

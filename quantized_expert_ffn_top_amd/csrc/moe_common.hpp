@@ -82,6 +82,18 @@ __device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- LDS by address
+// 32-bit LDS addresses, so that table lookups compose their address with
+// integer and/or operations (one v_and_or_b32 per lookup).
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_u32*)p;
+}
+__device__ __forceinline__ uint32_t lds_ld(uint32_t a) {
+    return *(const lds_u32*)(uintptr_t)a;
+}
+
 // ---------------------------------------------------------------- loads
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {

@@ -37,13 +37,15 @@ void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st);
 
-// ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT
+// ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT and
+// upgate_dec_supported(H) (the staged up|gate rows of two items fit in LDS)
+bool upgate_dec_supported(int H);
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
                        const uint16_t* sh_ug, int Is, float* shp, uint16_t* x16, hipStream_t st);
 void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                        const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                        const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                       const float* shp, int Is, uint16_t* a_sh, hipStream_t st);
+                       const float* shp, int Is, uint16_t* a_sh, int n_cu, hipStream_t st);
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                      const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T, int H,
                      int I, int k, const uint16_t* sh_down, const uint16_t* a_sh, int Is,

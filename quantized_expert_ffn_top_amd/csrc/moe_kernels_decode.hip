@@ -13,6 +13,8 @@
 // model card "Qwen3.8-Flash-Next - Avalon GGUF", "Files / Main model"
 // (routers and shared experts in the dense part; routed up/gate 3.25 bpw,
 // down IQ4_NL; expert records packed up | gate | down).
+#include <algorithm>
+
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -20,6 +22,10 @@ namespace moe {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// silu(g) * u from the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g)) * u;
+}
 
 // ---------------------------------------------------------------- stage 1
 // Wave-sized items, no block-level synchronisation.  Items [0, n_r): router
@@ -95,66 +101,285 @@ __global__ void __launch_bounds__(512) k_dec_stage1(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- up|gate
-// Decode table: entry (s, v, c) = (fp16(s*C3[v & 7]), fp16(s*C3[v >> 3])) for
-// sub-scale s in [-8, 7], index pair v, and copy c = lane & 7 (8 copies spread
-// the random lookups over the LDS banks).  Byte address s'*2048 + v*32 + c*4
-// with s' = s + 8, so a pair's six index bits land on the address with one
-// shift and one and-or.
-constexpr int kQ3Lut = 16 * 64 * 8;               // dwords
+// Decode table: entry v = (fp16(C3[v & 7]), fp16(C3[v >> 3])) for an index
+// pair v (two 3-bit codes, the first in the low bits), in 32 copies
+// (copy = lane & 31) so that the random lookups of a half-wave fall in
+// distinct LDS banks.  Byte address v*128 + c*4: a pair's six index bits
+// reach it with one shift and one and-or.  The sub-scale s multiplies the
+// pair afterwards (v_pk_mul_f16; s*c is an exact fp16 integer, |s*c| <= 1016).
+constexpr int kQ3LutCopies = 32;
+constexpr int kQ3LutDw = 64 * kQ3LutCopies;       // 8 KB
+// C3 as int8 bytes (entry q in byte q): the table build needs no memory load.
+constexpr uint64_t kC3Bytes = 0x7F4E301700E1BD81ull;
 
-__device__ __forceinline__ void build_q3_lut(uint32_t* lut, int tid, int nthr) {
-    // one (s, v) entry per step, its 8 copies written as two 16-byte stores
-    for (int sv = tid; sv < 16 * 64; sv += nthr) {
-        const int sp = sv >> 6, v = sv & 63;
-        const float s = (float)(sp - 8);
-        const uint32_t val = pack2(f32_to_f16_bits(s * (float)kC3[v & 7]),
-                                   f32_to_f16_bits(s * (float)kC3[v >> 3]));
-        const u32x4 q = {val, val, val, val};
-        reinterpret_cast<u32x4*>(lut)[2 * sv] = q;
-        reinterpret_cast<u32x4*>(lut)[2 * sv + 1] = q;
-    }
+__device__ __forceinline__ float c3_entry(int q) {
+    return (float)(int8_t)(uint8_t)(kC3Bytes >> (8 * q));
 }
 
-// Byte address (bits 5..10) of the index pair starting at bit P of the
+// Byte address (bits 7..12) of the index pair starting at bit P of the
 // 96-bit index string w[0..2], or-ed onto `base`.
 template <int P>
 __device__ __forceinline__ uint32_t q3_pair_addr(const uint32_t* w, uint32_t base) {
     constexpr int wd = P >> 5, lo = P & 31;
     uint32_t v;
-    if constexpr (lo + 6 > 32) v = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], lo - 5);
-    else if constexpr (lo >= 5) v = w[wd] >> (lo - 5);
-    else if constexpr (wd > 0) v = __builtin_amdgcn_alignbit(w[wd], w[wd - 1], 27 + lo);
-    else v = w[wd] << (5 - lo);
-    return (v & 0x7e0u) | base;
+    if constexpr (lo + 6 > 32) v = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], lo - 7);
+    else if constexpr (lo >= 7) v = w[wd] >> (lo - 7);
+    else if constexpr (wd > 0) v = __builtin_amdgcn_alignbit(w[wd], w[wd - 1], 25 + lo);
+    else v = w[wd] << (7 - lo);
+    return (v & 0x1f80u) | base;
 }
 
-// One block = an item of 8 waves.  Items [0, n_fin): shared expert finish,
-// a_sh[t][o] = bf16(silu(sum_c g) * sum_c u) over the stage-1 chunks (chunk
-// order).  Items [n_fin, ...): (active expert a, 16-column slice): the 16 up
-// rows and the 16 matching gate rows, waves splitting K in groups of 128
-// (4 sub-blocks).  Lane group g of a 16x16x32 step takes one whole 32-weight
-// sub-block (12 index bytes), so the B operand of a step spans 4 sub-blocks
-// of one 256-weight block: B = s*c from the table (exact fp16 integers,
-// |s*c| <= 1016) and the block scale d/128 multiplies the fp32 partial of the
-// group.  Epilogue: a = bf16_rne(silu(g) * u), stored as fp16 (exact).
-template <int GPW, bool FULL>
-__global__ void __launch_bounds__(512) k_upgate_dec(
+// LDS budget of the up|gate kernel besides the table: the partial sums of
+// two items (WAVES x (up, gate) x 64 lanes x 4 floats each) and two staged
+// items of 32 rows at a stride of (row bytes + 8).
+__host__ __device__ constexpr int ug_red_bytes(int waves) { return 2 * waves * 2 * 64 * 16; }
+
+__host__ __device__ constexpr int ug_stage_stride(int H) { return (H / 256) * 104 + 8; }
+// one stage: 32 rows and a 16-byte scratch slot for the loads past the rows
+__host__ __device__ constexpr int ug_stage_bytes(int H) { return 32 * ug_stage_stride(H) + 16; }
+// 12 waves (3 per SIMD) when the H/128 K groups split evenly over them, else 8
+__host__ __device__ constexpr int ug_waves(int H) {
+    return ((H / 128) % 12 == 0 && (H / 128) / 12 <= 2) ? 12 : 8;
+}
+
+// Persistent: one block of WAVES waves per CU; each block owns a contiguous range
+// of items (active expert a, 16-column slice): the 16 up rows and the 16
+// matching gate rows (32 x H/256 packed blocks).  An item's rows are loaded
+// with coalesced CH-byte loads two items ahead into registers, written to an
+// LDS stage when their turn comes (row stride = row bytes + 8, so that the
+// per-lane reads of 16 rows hit distinct banks), and decoded from there.
+// The waves split K in groups of 128 (4 sub-blocks; wave w takes groups
+// w + WAVES*i); lane group g of a
+// 16x16x32 step takes one whole 32-weight sub-block (12 index bytes), so the
+// B operand of a step spans 4 sub-blocks of one 256-weight block:
+// B = s*c (exact fp16 integers) and the block scale d/128 multiplies the
+// fp32 partial of the group.  The A operand holds every token of the batch
+// (row m = token m, rows >= T zero): each item multiplies all tokens and
+// keeps the routed ones.  Epilogue: partials of the waves summed in wave
+// order through LDS, a = bf16_rne(silu(g) * u), stored as fp16 (exact).
+// After the routed items every block finishes its share of the shared
+// expert: a_sh[t][o] = bf16(silu(sum_c g) * sum_c u) over the stage-1 chunks.
+template <int GPW, bool FULL, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const uint8_t* __restrict__ experts, int64_t estride, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ ntiles, const int32_t* __restrict__ perm, int k,
     const uint16_t* __restrict__ x16, int T, int H, int I, uint16_t* __restrict__ a16_perm,
-    const float* __restrict__ shp, int nkc, int Is, int n_fin, uint16_t* __restrict__ a_sh) {
-    __shared__ uint32_t lut[kQ3Lut];
-    __shared__ f32x4 red[8][2][64];
-    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const float* __restrict__ shp, int nkc, int Is, uint16_t* __restrict__ a_sh) {
+    constexpr int NT = 64 * WAVES;                          // threads
+    constexpr int CH = FULL ? 16 : 8;                       // bytes per staging load
+    // chunks per thread: 32 rows of <= 52 * WAVES * GPW bytes
+    constexpr int NCH = (32 * 52 * WAVES * GPW / CH + NT - 1) / NT;
+    __shared__ __attribute__((aligned(8192))) uint32_t lut[kQ3LutDw];  // pair bits OR onto the address
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    f32x4 (*red)[WAVES][2][64] = reinterpret_cast<f32x4 (*)[WAVES][2][64]>(dyn);
+    uint8_t* stage = dyn + ug_red_bytes(WAVES);
 
-    if ((int)blockIdx.x < n_fin) {                 // shared expert: sum partials, SwiGLU
-        const int i = blockIdx.x * 512 + tid;
-        if (i < T * Is) {
+    const int tid = threadIdx.x, lane = __lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int nsl = I / 16;
+    const int n_items = __builtin_amdgcn_readfirstlane(*ntiles) * nsl;
+    const int G = gridDim.x;
+    const int i0 = (int)((int64_t)blockIdx.x * n_items / G);
+    const int i1 = (int)((int64_t)(blockIdx.x + 1) * n_items / G);
+    const int rb = (H / kQ3Weights) * kQ3Bytes;
+    const int RS = rb + 8;
+    const int NG = FULL ? WAVES * GPW : H / 128;
+
+    // table
+    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
+        const int v = i >> 3;
+        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
+        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
+    }
+
+    // A operand: every token of the batch
+    u32x4 av[GPW][4];
+    {
+        const bool vt = r < T;
+        const uint16_t* xr = x16 + (int64_t)(vt ? r : 0) * H + 32 * g;
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+            const int q = w + WAVES * gi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                av[gi][i] = ((FULL || q < NG) && vt) ? ld16(xr + q * 128 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // staging map of this thread (the same for every item): chunk j covers
+    // CH bytes of row `row` (0..15 up, 16..31 gate) at column `col`
+    const int cpr = rb / CH;                                // chunks per row
+    int gofs[NCH], lofs[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = tid + NT * j;
+        const int row = c / cpr, col = (c - row * cpr) * CH;
+        const bool ok = row < 32;
+        gofs[j] = ok ? (row < 16 ? row : I - 16 + row) * rb + col : 0;
+        lofs[j] = ok ? row * RS + col : 32 * RS;           // past the rows: a scratch slot
+    }
+
+    struct Buf {                                            // one item in flight
+        uint32_t v[NCH][CH / 4];
+    };
+    Buf P0, P1;
+    auto issue = [&](int i, Buf& B) {
+        const int ic = min(i, max(0, min(i1, n_items) - 1)), at = ic / nsl, sl = ic - at * nsl;
+        const int e = tiles[3 * at];
+        const uint8_t* base = experts + (int64_t)e * estride + (int64_t)(16 * sl) * rb;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if constexpr (CH == 16) {
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + gofs[c]));
+                B.v[c][0] = t[0]; B.v[c][1] = t[1]; B.v[c][2] = t[2]; B.v[c][3] = t[3];
+            } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + gofs[c]));
+                B.v[c][0] = t[0]; B.v[c][1] = t[1];
+            }
+        }
+    };
+    auto put = [&](int sb, const Buf& B) {                  // registers -> stage sb (8-byte stores)
+        uint8_t* st = stage + sb * ug_stage_bytes(H);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+            for (int h = 0; h < CH / 8; ++h)
+                *reinterpret_cast<uint2*>(st + lofs[c] + 8 * h) = make_uint2(B.v[c][2 * h], B.v[c][2 * h + 1]);
+        }
+    };
+
+    const uint32_t cbase = lds_addr(lut) + (uint32_t)(lane & 31) * 4u;
+    const uint32_t kmag = (65536u + (uint32_t)k - 1u) / (uint32_t)k;   // t = (f * kmag) >> 16 for f < 512
+    const __amdgpu_buffer_rsrc_t a_out =
+        __builtin_amdgcn_make_buffer_rsrc(a16_perm, 0, (int)(T * k * I * 2), 0x00020000);
+    // this lane's bytes in a staged row: group gi at + (WAVES / 2) * 104 * gi
+    const int r_idx = r * RS + (w >> 1) * kQ3Bytes + 12 * (4 * (w & 1) + g);
+    const int r_tail = r * RS + (w >> 1) * kQ3Bytes + 96;
+
+    auto decode = [&](int it, int sb) {                     // sb: stage of item it
+        const int at = it / nsl, sl = it - at * nsl;
+        const int row0 = tiles[3 * at + 1], rows = tiles[3 * at + 2];
+        const uint32_t st = lds_addr(stage + sb * ug_stage_bytes(H));
+        f32x4 acc_u = {0.f, 0.f, 0.f, 0.f}, acc_g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+            const int q = w + WAVES * gi;
+            if (FULL || q < NG) {
+                const uint32_t ou = st + r_idx + (WAVES / 2) * kQ3Bytes * gi, og = ou + 16 * RS;
+                const uint32_t iu[3] = {lds_ld(ou), lds_ld(ou + 4), lds_ld(ou + 8)};
+                const uint32_t ig[3] = {lds_ld(og), lds_ld(og + 4), lds_ld(og + 8)};
+                const uint32_t tu = st + r_tail + (WAVES / 2) * kQ3Bytes * gi, tg = tu + 16 * RS;
+                const uint64_t tlu = ((uint64_t)lds_ld(tu + 4) << 32) | lds_ld(tu);
+                const uint64_t tlg = ((uint64_t)lds_ld(tg + 4) << 32) | lds_ld(tg);
+                const int js = 4 * (q & 1) + g;
+                const _Float16 su = (_Float16)(float)q3_tail_s(tlu, js);
+                const _Float16 sg = (_Float16)(float)q3_tail_s(tlg, js);
+                const h2 su2 = {su, su}, sg2 = {sg, sg};
+                f32x4 pu = {0.f, 0.f, 0.f, 0.f}, pg = {0.f, 0.f, 0.f, 0.f};
+                // all 32 table reads of the group in flight before any is used
+                uint32_t lu[16], lg[16];
+#define MOE_PAIR(I_, P_)                                                        \
+    lu[4 * I_ + P_] = lds_ld(q3_pair_addr<24 * I_ + 6 * P_>(iu, cbase));        \
+    lg[4 * I_ + P_] = lds_ld(q3_pair_addr<24 * I_ + 6 * P_>(ig, cbase));
+#define MOE_STEP(I_) MOE_PAIR(I_, 0) MOE_PAIR(I_, 1) MOE_PAIR(I_, 2) MOE_PAIR(I_, 3)
+                MOE_STEP(0) MOE_STEP(1) MOE_STEP(2) MOE_STEP(3)
+#undef MOE_STEP
+#undef MOE_PAIR
+                __builtin_amdgcn_sched_barrier(0);
+                u32x4 bu[4], bg[4];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    bu[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lu[i]) * su2);
+                    bg[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lg[i]) * sg2);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pu = mfma16_f16(av[gi][i], bu[i], pu);
+                    pg = mfma16_f16(av[gi][i], bg[i], pg);
+                }
+                const float du = q3_tail_d(tlu) * 0.0078125f;
+                const float dg = q3_tail_d(tlg) * 0.0078125f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc_u[i] += pu[i] * du;
+                    acc_g[i] += pg[i] * dg;
+                }
+            }
+        }
+        const int buf = it & 1;
+        red[buf][w][0][lane] = acc_u;
+        red[buf][w][1][lane] = acc_g;
+        __syncthreads();
+        // finish: waves 0-3, thread (slot j, column n); D row m = token tj sits at
+        // lane (m/4)*16 + n, element m%4.  Every thread issues the store (equal
+        // memory-op counts on all paths); those without an output store out of
+        // range, which the buffer unit drops.
+        const int j = tid >> 4, n = tid & 15;
+        uint16_t av16 = 0;
+        if (w < 4) {
+            // slots 4w .. 4w+3 of the tile (scalar loads; past `rows` they are
+            // other tiles' slots or the next workspace array, never used)
+            const int* ps = perm + row0 + 4 * w;
+            const int s0 = ps[0], s1 = ps[1], s2 = ps[2], s3 = ps[3];
+            const int slot = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
+            const int tj = (int)(((uint32_t)(j < rows ? slot : 0) * kmag) >> 16);
+            const float* ru =
+                reinterpret_cast<const float*>(&red[buf][0][0][(tj >> 2) * 16 + n]) + (tj & 3);
+            float u = 0.f, gg = 0.f;
+#pragma unroll
+            for (int v = 0; v < WAVES; ++v) {
+                u += ru[v * 2 * 64 * 4];
+                gg += ru[v * 2 * 64 * 4 + 64 * 4];
+            }
+            av16 = (uint16_t)f32_to_f16_bits(bf16_to_f32(f32_to_bf16(silu_mul_fast(gg, u))));
+        }
+        const bool ok = w < 4 && j < rows;
+        const uint32_t off = ok ? (uint32_t)(((row0 + j) * I + 16 * sl + n) * 2) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b16(av16, a_out, off, 0, 0);
+    };
+
+    // pipeline, one barrier per item: step i writes item i + 1 from its
+    // registers to stage (i + 1 - i0) % 2, loads item i + 3 into those
+    // registers, decodes item i from stage (i - i0) % 2 and writes its partial
+    // sums; after the
+    // barrier waves 0-3 finish item i while the others go on.  Items i + 2
+    // and i + 3 are in flight during the decode of item i (past the end the
+    // last item is loaded again and not used; a block without items loads
+    // item min(i0, n_items - 1)).
+    issue(i0, P0);
+    issue(i0 + 1, P1);
+    __syncthreads();                                        // table written
+    put(0, P0);
+    issue(i0 + 2, P0);
+    __syncthreads();                                        // stage 0 written
+    auto step = [&](int it, Buf& B) {                       // B holds item it + 1
+        put((it + 1 - i0) & 1, B);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(it + 3, B);
+        __builtin_amdgcn_sched_barrier(0);
+        decode(it, (it - i0) & 1);
+    };
+    for (int it = i0; it < i1; it += 6) {
+        step(it, P1);
+        if (it + 1 >= i1) break;
+        step(it + 1, P0);
+        if (it + 2 >= i1) break;
+        step(it + 2, P1);
+        if (it + 3 >= i1) break;
+        step(it + 3, P0);
+        if (it + 4 >= i1) break;
+        step(it + 4, P1);
+        if (it + 5 >= i1) break;
+        step(it + 5, P0);
+    }
+
+    if (shp) {                                              // shared expert: sum partials, SwiGLU
+        for (int i = blockIdx.x * NT + tid; i < T * Is; i += G * NT) {
             const int t = i / Is, o = i - t * Is;
             float u = 0.f, gg = 0.f;
-            for (int c0 = 0; c0 < nkc; c0 += 8) {      // 16 loads in flight, summed in chunk order
+            for (int c0 = 0; c0 < nkc; c0 += 8) {           // 16 loads in flight, summed in chunk order
                 float pu[8], pg[8];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
@@ -169,103 +394,6 @@ __global__ void __launch_bounds__(512) k_upgate_dec(
                 }
             }
             a_sh[i] = (uint16_t)f32_to_bf16(silu_mul(gg, u));
-        }
-        return;
-    }
-    const int nsl = I / 16;
-    const int item = blockIdx.x - n_fin;
-    const int at = item / nsl;
-    const int n0 = (item - at * nsl) * 16;
-    if (at >= *ntiles) return;
-    const int e = tiles[3 * at], row0 = tiles[3 * at + 1], rows = tiles[3 * at + 2];
-
-    const int64_t row_bytes = (int64_t)(H / kQ3Weights) * kQ3Bytes;
-    const uint8_t* W = experts + (int64_t)e * estride;
-    const uint8_t* up = W + (int64_t)(n0 + r) * row_bytes;
-    const uint8_t* gt = W + (int64_t)(I + n0 + r) * row_bytes;
-    // rows >= rows reuse the first row's token: their results are never stored
-    const int t = perm[row0 + (r < rows ? r : 0)] / k;
-    const uint16_t* xr = x16 + (int64_t)t * H + 32 * g;
-    const int NG = FULL ? 8 * GPW : H / 128;
-
-    // all loads of the item first
-    uint32_t iu[GPW][3], ig[GPW][3];
-    uint64_t tu[GPW], tg[GPW];
-    u32x4 av[GPW][4];
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-        const int q = w + 8 * gi;
-        if (q < NG) {
-            const int b = q >> 1, js = 4 * (q & 1) + g;
-            const int off = b * kQ3Bytes + 12 * js;
-            iu[gi][0] = ld4(up + off);
-            iu[gi][1] = ld4(up + off + 4);
-            iu[gi][2] = ld4(up + off + 8);
-            ig[gi][0] = ld4(gt + off);
-            ig[gi][1] = ld4(gt + off + 4);
-            ig[gi][2] = ld4(gt + off + 8);
-            tu[gi] = *reinterpret_cast<const uint64_t*>(up + b * kQ3Bytes + 96);
-            tg[gi] = *reinterpret_cast<const uint64_t*>(gt + b * kQ3Bytes + 96);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[gi][i] = ld16(xr + q * 128 + 8 * i);
-        }
-    }
-    build_q3_lut(lut, tid, 512);
-    __syncthreads();
-
-    const uint8_t* Lb = reinterpret_cast<const uint8_t*>(lut);
-    const uint32_t cbase = (uint32_t)(lane & 7) * 4u;
-    f32x4 acc_u = {0.f, 0.f, 0.f, 0.f}, acc_g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-        const int q = w + 8 * gi;
-        if (q < NG) {
-            const int js = 4 * (q & 1) + g;
-            const uint32_t bu_s = (uint32_t)(q3_tail_s(tu[gi], js) + 8) * 2048u + cbase;
-            const uint32_t bg_s = (uint32_t)(q3_tail_s(tg[gi], js) + 8) * 2048u + cbase;
-            f32x4 pu = {0.f, 0.f, 0.f, 0.f}, pg = {0.f, 0.f, 0.f, 0.f};
-            u32x4 bu[4], bg[4];
-#define MOE_PAIR(I_, P_)                                                                  \
-    bu[I_][P_] = *reinterpret_cast<const uint32_t*>(Lb + q3_pair_addr<24 * I_ + 6 * P_>(iu[gi], bu_s)); \
-    bg[I_][P_] = *reinterpret_cast<const uint32_t*>(Lb + q3_pair_addr<24 * I_ + 6 * P_>(ig[gi], bg_s));
-#define MOE_STEP(I_) MOE_PAIR(I_, 0) MOE_PAIR(I_, 1) MOE_PAIR(I_, 2) MOE_PAIR(I_, 3)
-            MOE_STEP(0) MOE_STEP(1) MOE_STEP(2) MOE_STEP(3)
-#undef MOE_STEP
-#undef MOE_PAIR
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pu = mfma16_f16(av[gi][i], bu[i], pu);
-                pg = mfma16_f16(av[gi][i], bg[i], pg);
-            }
-            const float du = q3_tail_d(tu[gi]) * 0.0078125f;
-            const float dg = q3_tail_d(tg[gi]) * 0.0078125f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc_u[i] += pu[i] * du;
-                acc_g[i] += pg[i] * dg;
-            }
-        }
-    }
-    red[w][0][lane] = acc_u;
-    red[w][1][lane] = acc_g;
-    __syncthreads();
-    if (w == 0) {
-        f32x4 u = red[0][0][lane], gg = red[0][1][lane];
-#pragma unroll
-        for (int v = 1; v < 8; ++v) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u[i] += red[v][0][lane][i];
-                gg[i] += red[v][1][lane][i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * g + i;
-            if (m < rows) {
-                const uint32_t bf = f32_to_bf16(silu_mul(gg[i], u[i]));
-                a16_perm[(int64_t)(row0 + m) * I + n0 + r] = (uint16_t)f32_to_f16_bits(bf16_to_f32(bf));
-            }
         }
     }
 }
@@ -394,38 +522,58 @@ void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w
                                                             shp, n_s, x16);
 }
 
-template <int GPW, bool FULL>
+template <int GPW, bool FULL, int WAVES>
 static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, int64_t estride,
                          const int32_t* tiles, const int32_t* ntiles, const int32_t* perm, int k,
                          const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                         const float* shp, int nkc, int Is, int n_fin, uint16_t* a_sh) {
-    k_upgate_dec<GPW, FULL><<<grid, 512, 0, st>>>(experts, estride, tiles, ntiles, perm, k, x16, T,
-                                                  H, I, a16_perm, shp, nkc, Is, n_fin, a_sh);
+                         const float* shp, int nkc, int Is, uint16_t* a_sh) {
+    const size_t dyn = ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H);
+    static bool attr = false;                      // opt in to more than 64 KB of LDS once
+    if (!attr) {
+        hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kQ3LutDw * 4);
+        attr = true;
+    }
+    k_upgate_dec<GPW, FULL, WAVES><<<grid, 64 * WAVES, dyn, st>>>(
+        experts, estride, tiles, ntiles, perm, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh);
 }
 
 void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                        const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                        const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                       const float* shp, int Is, uint16_t* a_sh, hipStream_t st) {
-    const int n_fin = (shp && Is > 0) ? (T * Is + 511) / 512 : 0;
-    const unsigned grid = (unsigned)(n_fin + max_tiles * (I / 16));
+                       const float* shp, int Is, uint16_t* a_sh, int n_cu, hipStream_t st) {
+    const int max_items = max_tiles * (I / 16);
+    const unsigned grid = (unsigned)std::max(1, std::min(n_cu, max_items));
     const int nkc = H / kRouterKChunk;
-    const int gpw = (H / 128 + 7) / 8;
-    const bool full = (H / 128) == 8 * gpw;
-#define MOE_UG(G)                                                                               \
-    case G:                                                                                     \
-        if (full)                                                                               \
-            upgate_dec_t<G, true>(grid, st, experts, estride, tiles, ntiles, perm, k, x16, T, H, \
-                                  I, a16_perm, shp, nkc, Is, n_fin, a_sh);                      \
-        else                                                                                    \
-            upgate_dec_t<G, false>(grid, st, experts, estride, tiles, ntiles, perm, k, x16, T,  \
-                                   H, I, a16_perm, shp, nkc, Is, n_fin, a_sh);                  \
-        break;
+    // 12 waves (3 per SIMD) when the K groups split evenly over them, else 8
+    const int NG = H / 128;
+    const int waves = ug_waves(H);
+    const int gpw = (NG + waves - 1) / waves;
+    const bool full = NG == waves * gpw;
+    shp = (Is > 0) ? shp : nullptr;
+#define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, tiles, ntiles, perm, k, \
+                                               x16, T, H, I, a16_perm, shp, nkc, Is, a_sh)
+    if (waves == 12) {
+        if (gpw == 1) MOE_UGT(1, true, 12);
+        else MOE_UGT(2, true, 12);
+        return;
+    }
     switch (gpw) {
-        MOE_UG(1) MOE_UG(2) MOE_UG(3) MOE_UG(4) MOE_UG(5) MOE_UG(6) MOE_UG(7) MOE_UG(8)
+#define MOE_UG(G)                          \
+    case G:                                \
+        if (full) MOE_UGT(G, true, 8);     \
+        else MOE_UGT(G, false, 8);         \
+        break;
+        MOE_UG(1) MOE_UG(2) MOE_UG(3) MOE_UG(4)
+#undef MOE_UG
         default: break;
     }
-#undef MOE_UG
+#undef MOE_UGT
+}
+
+bool upgate_dec_supported(int H) {
+    return H / 128 <= 8 * 4 &&
+           kQ3LutDw * 4 + ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H) <= 160 * 1024;
 }
 
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
