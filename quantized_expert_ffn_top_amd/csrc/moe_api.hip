@@ -381,7 +381,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
                           a16, has_sh ? shp : nullptr, Is, ash, n_cu, st);
         mk->mark();
         launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, k, sdn, ash,
-                        Is, yp, ysh, st);
+                        Is, yp, ysh, n_cu, st);
         mk->mark();
     } else {
         const float* L_use = logits_or_null;

@@ -49,7 +49,7 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* t
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                      const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T, int H,
                      int I, int k, const uint16_t* sh_down, const uint16_t* a_sh, int Is,
-                     float* y_perm, float* y_sh, hipStream_t st);
+                     float* y_perm, float* y_sh, int n_cu, hipStream_t st);
 
 // ---- grouped-GEMM path (moe_kernels_gemm.hip)
 void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,

@@ -398,115 +398,211 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     }
 }
 
-// ---------------------------------------------------------------- down + combine
-// One block = 4 waves; wave = 16 output rows.  Items per 64-row slice sl:
-// routed (active expert a, sl) and, if present, the shared expert (sl).
-// Routed: the wave's 16 down rows (16 x 288 bytes per 16-block K chunk) are
-// staged into LDS with coalesced dword loads, then one 16x16x32 step per
-// NL4-32 block (lane group g takes 8 weights = 4 index bytes, B = table
+// ---------------------------------------------------------------- down
+// NL4 decode table: byte v -> (fp16(T4[v & 15]), fp16(T4[v >> 4])), the two
+// weights of one index byte (even weight in the low nibble), in 32 copies
+// (copy = lane & 31): byte address v*128 + c*4, so one shift and one and-or
+// per byte.  32 KB, built once per block.
+constexpr int kNl4LutDw = 256 * 32;
+// T4 as int8 bytes (entry q in byte q of the pair of words).
+constexpr uint64_t kT4Lo = 0x00F5E9DCCEBEA881ull, kT4Hi = 0x7F5B47382B1F140Aull;
+
+__device__ __forceinline__ float t4_entry(int q) {
+    return (float)(int8_t)(uint8_t)((q < 8 ? kT4Lo : kT4Hi) >> (8 * (q & 7)));
+}
+
+constexpr int kDnWaves = 8;
+constexpr int kDnChunkDw = 72;                    // 16 NL4 blocks of a row (288 bytes)
+constexpr int kDnStageDw = kDnChunkDw + 1;        // stage row stride (odd: rows in distinct banks)
+constexpr int kDnLoads = 16 * kDnChunkDw / 64;    // dword loads per lane per staged chunk (18)
+
+// Persistent: blocks of 8 waves; after the table is built every wave works
+// alone.  The waves are dealt to the active experts (2 shares each) and to
+// the shared expert (7 shares, its rows being bf16) in proportion; the waves
+// of one expert split its H/16 slices of 16 output rows.  A wave keeps the
+// A operand of its expert (the routed rows' fp16 activations, <= 16 slots)
+// in registers.  Routed slice: the 16 rows x 16 blocks of a K chunk (4608
+// contiguous bytes) are loaded with coalesced dword loads two units ahead,
+// written to the wave's LDS stage and decoded from there: one 16x16x32 step
+// per NL4 block (lane group g takes 8 weights = 4 index bytes; B = table
 // integers T4[q], exact fp16) and the block scale d/128 multiplies the fp32
-// partial of the step.  M rows = the expert's permuted rows (<= 16).  Output:
-// y_perm (unweighted, permuted rows) or y_sh; the combine kernel sums them.
-constexpr int kDnRowDw = 73;                      // 72 dwords per 16-block row chunk + 1 pad
-
-template <bool FULL16>                            // every K chunk has 16 blocks (I % 512 == 0)
-__global__ void __launch_bounds__(256) k_down_dec(
+// partial of the step.  Output y_perm[slot][h] (unweighted, permuted rows);
+// the combine kernel sums them.  Shared slice: bf16 rows x a_sh (bf16), 16x16x32
+// bf16 steps, output y_sh[t][h].
+template <bool FULL16, bool ONEK>   // I % 512 == 0; I <= 512 (A kept for all slices)
+__global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const uint8_t* __restrict__ experts, int64_t estride, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, int max_tiles, const uint16_t* __restrict__ a16_perm,
-    int T, int H, int I, int k, const uint16_t* __restrict__ sh_down,
-    const uint16_t* __restrict__ a_sh, int Is, float* __restrict__ y_perm,
-    float* __restrict__ y_sh) {
-    __shared__ uint32_t lut[256 * 32];             // byte -> (T4[lo], T4[hi]) fp16, 32 copies
-    __shared__ uint32_t wbuf[4][16 * kDnRowDw];
-    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
+    const int32_t* __restrict__ ntiles, const uint16_t* __restrict__ a16_perm, int T, int H, int I,
+    const uint16_t* __restrict__ sh_down, const uint16_t* __restrict__ a_sh, int Is,
+    float* __restrict__ y_perm, float* __restrict__ y_sh) {
+    __shared__ __attribute__((aligned(32768))) uint32_t lut[kNl4LutDw];   // byte bits OR onto the address
+    __shared__ uint32_t stg[kDnWaves][16 * kDnStageDw];
+    const int tid = threadIdx.x, lane = __lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int nsl = H / 64;
-    const int sl = blockIdx.x % nsl;
-    const int a = blockIdx.x / nsl;               // 0..max_tiles-1 routed, max_tiles = shared
-    const bool is_sh = a == max_tiles;
-    if (is_sh ? sh_down == nullptr : a >= *ntiles) return;
-    const int n0 = sl * 64 + w * 16;
+    for (int i = tid; i < kNl4LutDw / 4; i += 64 * kDnWaves) {   // 16-byte chunk i: 8 per entry
+        const int v = i >> 3;
+        const uint32_t val = pack2(f32_to_f16_bits(t4_entry(v & 15)), f32_to_f16_bits(t4_entry(v >> 4)));
+        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
+    }
+    __syncthreads();
 
-    if (is_sh) {
-        const uint16_t* brow = sh_down + (int64_t)(n0 + r) * Is + 8 * g;
-        const uint16_t* arow = a_sh + (int64_t)(r < T ? r : 0) * Is + 8 * g;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // this wave's expert and slices
+    const int nt = __builtin_amdgcn_readfirstlane(*ntiles);
+    const bool has_sh = sh_down != nullptr;
+    const int total = 2 * nt + (has_sh ? 7 : 0);
+    const int GW = gridDim.x * kDnWaves, gw = blockIdx.x * kDnWaves + w;
+    const int u = (int)((int64_t)gw * total / GW);
+    const int t = u < 2 * nt ? (u >> 1) : nt;               // t == nt: shared expert
+    const int us = 2 * t, ue = t < nt ? 2 * t + 2 : total;
+    const int ws = (int)(((int64_t)us * GW + total - 1) / total);
+    const int we = (int)(((int64_t)ue * GW + total - 1) / total);
+    const int nsl = H / 16;
+    const int s0 = (int)((int64_t)(gw - ws) * nsl / (we - ws));
+    const int s1 = (int)((int64_t)(gw - ws + 1) * nsl / (we - ws));
+    if (s0 >= s1) return;
+
+    if (t == nt) {                                          // shared expert, bf16
+        const bool vt = r < T;
+        const uint16_t* arow = a_sh + (int64_t)(vt ? r : 0) * Is + 8 * g;
+        const __amdgpu_buffer_rsrc_t yo = __builtin_amdgcn_make_buffer_rsrc(y_sh, 0, T * H * 4, 0x00020000);
+        for (int sl = s0; sl < s1; ++sl) {
+            const uint16_t* brow = sh_down + (int64_t)(16 * sl + r) * Is + 8 * g;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int s2 = 0; s2 < Is / 32; ++s2)
-            acc = mfma16_bf16(ld16(arow + 32 * s2), ld16_stream(brow + 32 * s2), acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * g + i;
-            if (m < T) y_sh[(int64_t)m * H + n0 + r] = acc[i];
-        }
-    } else {
-        const int e = tiles[3 * a], row0 = tiles[3 * a + 1], rows = tiles[3 * a + 2];
-        if (tid < 256) {                           // entry tid, its 32 copies as 8 16-byte stores
-            const uint32_t val = pack2(f32_to_f16_bits((float)kT4[tid & 15]),
-                                       f32_to_f16_bits((float)kT4[tid >> 4]));
-            const u32x4 q = {val, val, val, val};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) reinterpret_cast<u32x4*>(lut)[8 * tid + c] = q;
-        }
-        const int nb = I / 32;
-        const int64_t rb = (int64_t)nb * kNL4Bytes;
-        const int64_t ug_bytes = (int64_t)2 * I * (H / kQ3Weights) * kQ3Bytes;
-        const uint8_t* base = experts + (int64_t)e * estride + ug_bytes + (int64_t)n0 * rb;
-        // rows >= rows reuse the first row: their results are never stored
-        const uint16_t* arow = a16_perm + (int64_t)(row0 + (r < rows ? r : 0)) * I + 8 * g;
-        uint32_t* wb = wbuf[w];
-        const uint8_t* Lb = reinterpret_cast<const uint8_t*>(lut);
-        const uint32_t cb = (uint32_t)(lane & 31) * 4u;   // byte b: address b*128 + copy*4
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        __syncthreads();                           // table ready
-        for (int c = 0; c < (nb + 15) / 16; ++c) {  // K chunks of 16 blocks (nb is even)
-            const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
-            const int dpr = FULL16 ? 72 : cbk * kNL4Bytes / 4;   // dwords per row in this chunk
-            uint32_t bw[18];
-#pragma unroll
-            for (int i = 0; i < 18; ++i) {
-                const int j = lane + 64 * i, row = j / dpr, col = j - dpr * row;
-                const bool ok = FULL16 || j < 16 * dpr;
-                bw[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const uint32_t*>(base + (ok ? row : 0) * rb + 288 * c) + (ok ? col : 0));
+            for (int kk = 0; kk < Is / 32; ++kk) {
+                const u32x4 av = vt ? ld16(arow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+                acc = mfma16_bf16(av, ld16_stream(brow + 32 * kk), acc);
             }
-            u32x4 av[16];
 #pragma unroll
-            for (int b = 0; b < 16; ++b) av[b] = ld16(arow + 512 * c + 32 * (b < cbk ? b : 0));
-#pragma unroll
-            for (int i = 0; i < 18; ++i) {
-                const int j = lane + 64 * i, row = j / dpr, col = j - dpr * row;
-                if (FULL16 || j < 16 * dpr) wb[row * kDnRowDw + col] = bw[i];
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i;
+                const uint32_t off = m < T ? (uint32_t)((m * H + 16 * sl + r) * 4) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), yo, off, 0, 0);
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            const uint32_t* wr = wb + r * kDnRowDw;
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                if (b < cbk) {
-                    const int o = 18 * b + 2 + 4 * g;      // index bytes of lane group g
-                    const uint32_t nib = (b & 1) ? wr[o >> 2]
-                                                 : __builtin_amdgcn_alignbit(wr[(o >> 2) + 1], wr[o >> 2], 16);
-                    const uint32_t dw = wr[(18 * b) >> 2];
-                    const float d = f16_bits_to_f32((b & 1) ? (dw >> 16) : (dw & 0xffffu)) * 0.0078125f;
-                    u32x4 bv;
-                    bv[0] = *reinterpret_cast<const uint32_t*>(Lb + (((nib << 7) & 0x7f80u) | cb));
-                    bv[1] = *reinterpret_cast<const uint32_t*>(Lb + (((nib >> 1) & 0x7f80u) | cb));
-                    bv[2] = *reinterpret_cast<const uint32_t*>(Lb + (((nib >> 9) & 0x7f80u) | cb));
-                    bv[3] = *reinterpret_cast<const uint32_t*>(Lb + (((nib >> 17) & 0x7f80u) | cb));
-                    const f32x4 part = mfma16_f16(av[b], bv, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] += part[i] * d;
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * g + i;
-            if (m < rows) y_perm[(int64_t)(row0 + m) * H + n0 + r] = acc[i];
-        }
+        return;
     }
 
+    const int e = tiles[3 * t], row0 = tiles[3 * t + 1], rows = tiles[3 * t + 2];
+    const int nb = I / 32, nkc = (nb + 15) / 16;
+    const int rb = nb * kNL4Bytes;
+    const uint8_t* W = experts + (int64_t)e * estride + (int64_t)2 * I * (H / kQ3Weights) * kQ3Bytes;
+    const uint16_t* arow = a16_perm + (int64_t)(row0 + (r < rows ? r : 0)) * I + 8 * g;
+    const __amdgpu_buffer_rsrc_t yo =
+        __builtin_amdgcn_make_buffer_rsrc(y_perm, 0, (row0 + rows) * H * 4, 0x00020000);
+    const uint32_t cbase = lds_addr(lut) + (uint32_t)(lane & 31) * 4u;
+    uint32_t* st = stg[w];
+
+    // lane's dwords of a staged chunk: (global byte offset | stage dword << 16)
+    uint32_t off[kDnLoads];
+#pragma unroll
+    for (int i = 0; i < kDnLoads; ++i) {
+        const int j = lane + 64 * i, row = j / kDnChunkDw, col = j - row * kDnChunkDw;
+        off[i] = (uint32_t)(row * rb + 4 * col) | ((uint32_t)(row * kDnStageDw + col) << 16);
+    }
+    // A operand of the expert: chunk c, block b -> av[b]
+    u32x4 av[16];
+    auto load_a = [&](int c) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+            av[b] = (16 * c + b < nb) ? ld16(arow + 32 * (16 * c + b)) : u32x4{0u, 0u, 0u, 0u};
+    };
+    if (ONEK) load_a(0);
+
+    struct Buf {
+        uint32_t v[kDnLoads];
+    };
+    Buf P0, P1;
+    // unit q = (slice s0 + q / nkc, chunk q % nkc); past the end the last unit is loaded again
+    const int nu = (s1 - s0) * nkc;
+    auto issue = [&](int q, Buf& B) {
+        q = min(q, nu - 1);
+        const int sl = s0 + q / nkc, c = q - (q / nkc) * nkc;
+        const uint8_t* base = W + (int64_t)(16 * sl) * rb + 288 * c;
+        const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
+        const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
+#pragma unroll
+        for (int i = 0; i < kDnLoads; ++i) {
+            uint32_t go;
+            if (FULL16) {
+                go = off[i] & 0xffffu;
+            } else {
+                const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
+                go = j < 16 * dpr ? (uint32_t)(row * rb + 4 * col) : 0u;
+            }
+            B.v[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + go));
+        }
+    };
+    auto put = [&](int q, const Buf& B) {
+        const int c = min(q, nu - 1) % nkc;
+        const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
+        const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
+#pragma unroll
+        for (int i = 0; i < kDnLoads; ++i) {
+            if (FULL16) {
+                st[off[i] >> 16] = B.v[i];
+            } else {
+                const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
+                if (j < 16 * dpr) st[row * kDnStageDw + col] = B.v[i];
+            }
+        }
+    };
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto decode = [&](int q) {
+        const int sl = s0 + q / nkc, c = q - (q / nkc) * nkc;
+        if (!ONEK) load_a(c);
+        const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
+        const uint32_t* wr = st + r * kDnStageDw;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            if (b < cbk) {
+                const int o = 18 * b + 2 + 4 * g;              // index bytes of lane group g
+                const uint32_t nib = (b & 1) ? wr[o >> 2]
+                                             : __builtin_amdgcn_alignbit(wr[(o >> 2) + 1], wr[o >> 2], 16);
+                const uint32_t dw = wr[(18 * b) >> 2];
+                const float d = f16_bits_to_f32((b & 1) ? (dw >> 16) : (dw & 0xffffu)) * 0.0078125f;
+                u32x4 bv;
+                bv[0] = lds_ld(((nib << 7) & 0x7f80u) | cbase);
+                bv[1] = lds_ld(((nib >> 1) & 0x7f80u) | cbase);
+                bv[2] = lds_ld(((nib >> 9) & 0x7f80u) | cbase);
+                bv[3] = lds_ld(((nib >> 17) & 0x7f80u) | cbase);
+                const f32x4 part = mfma16_f16(av[b], bv, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += part[i] * d;
+            }
+        }
+        if (c == nkc - 1) {                                 // slice done: rows m = 4g + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i;
+                const uint32_t o = m < rows ? (uint32_t)(((row0 + m) * H + 16 * sl + r) * 4) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), yo, o, 0, 0);
+                acc[i] = 0.f;
+            }
+        }
+    };
+
+    // two units in flight while one is decoded
+    issue(0, P0);
+    issue(1, P1);
+    auto step = [&](int q, Buf& B) {
+        put(q, B);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(q + 2, B);
+        __builtin_amdgcn_sched_barrier(0);
+        decode(q);
+    };
+    for (int q = 0; q < nu; q += 4) {
+        step(q, P0);
+        if (q + 1 >= nu) break;
+        step(q + 1, P1);
+        if (q + 2 >= nu) break;
+        step(q + 2, P0);
+        if (q + 3 >= nu) break;
+        step(q + 3, P1);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -579,14 +675,23 @@ bool upgate_dec_supported(int H) {
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                      const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T, int H,
                      int I, int k, const uint16_t* sh_down, const uint16_t* a_sh, int Is,
-                     float* y_perm, float* y_sh, hipStream_t st) {
-    const unsigned grid = (unsigned)((max_tiles + 1) * (H / 64));
-    if (I % 512 == 0)
-        k_down_dec<true><<<grid, 256, 0, st>>>(experts, estride, tiles, ntiles, max_tiles, a16_perm,
-                                               T, H, I, k, sh_down, a_sh, Is, y_perm, y_sh);
-    else
-        k_down_dec<false><<<grid, 256, 0, st>>>(experts, estride, tiles, ntiles, max_tiles, a16_perm,
-                                                T, H, I, k, sh_down, a_sh, Is, y_perm, y_sh);
+                     float* y_perm, float* y_sh, int n_cu, hipStream_t st) {
+    (void)k;
+    // every expert needs at least one wave: 2 shares each, 7 for the shared one
+    const int shares = 2 * max_tiles + 7;
+    const unsigned grid = (unsigned)std::max(n_cu, (shares + kDnWaves - 1) / kDnWaves);
+    if (Is <= 0) sh_down = nullptr;
+#define MOE_DN(F, O)                                                                             \
+    k_down_dec<F, O><<<grid, 64 * kDnWaves, 0, st>>>(experts, estride, tiles, ntiles, a16_perm, T, \
+                                                     H, I, sh_down, a_sh, Is, y_perm, y_sh)
+    if (I % 512 == 0) {
+        if (I == 512) MOE_DN(true, true);
+        else MOE_DN(true, false);
+    } else {
+        if (I < 512) MOE_DN(false, true);
+        else MOE_DN(false, false);
+    }
+#undef MOE_DN
 }
 
 }  // namespace moe
