@@ -186,12 +186,6 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int RS = rb + 8;
     const int NG = FULL ? WAVES * GPW : H / 128;
 
-    // table
-    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
-        const int v = i >> 3;
-        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
-        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
-    }
 
     // A operand: every token of the batch
     u32x4 av[GPW][4];
@@ -350,6 +344,12 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     // item min(i0, n_items - 1)).
     issue(i0, P0);
     issue(i0 + 1, P1);
+    // the table, while the first items load
+    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
+        const int v = i >> 3;
+        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
+        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
+    }
     __syncthreads();                                        // table written
     put(0, P0);
     issue(i0 + 2, P0);
@@ -413,10 +413,10 @@ __device__ __forceinline__ float t4_entry(int q) {
 
 constexpr int kDnWaves = 8;
 constexpr int kDnChunkDw = 72;                    // 16 NL4 blocks of a row (288 bytes)
-constexpr int kDnStageDw = kDnChunkDw + 1;        // stage row stride (odd: rows in distinct banks)
+constexpr int kDnStageDw = kDnChunkDw + 2;        // stage row stride (= 10 mod 32: the 16 rows x 2 lane groups of a half-wave hit distinct banks)
 constexpr int kDnLoads = 16 * kDnChunkDw / 64;    // dword loads per lane per staged chunk (18)
 
-// Persistent: blocks of 8 waves; after the table is built every wave works
+// Persistent: blocks of kDnWaves waves; after the table is built every wave works
 // alone.  The waves are dealt to the active experts (2 shares each) and to
 // the shared expert (7 shares, its rows being bf16) in proportion; the waves
 // of one expert split its H/16 slices of 16 output rows.  A wave keeps the
@@ -440,6 +440,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const int tid = threadIdx.x, lane = __lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
+    const int nt = __builtin_amdgcn_readfirstlane(*ntiles);  // in flight during the table build
     for (int i = tid; i < kNl4LutDw / 4; i += 64 * kDnWaves) {   // 16-byte chunk i: 8 per entry
         const int v = i >> 3;
         const uint32_t val = pack2(f32_to_f16_bits(t4_entry(v & 15)), f32_to_f16_bits(t4_entry(v >> 4)));
@@ -448,7 +449,6 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     __syncthreads();
 
     // this wave's expert and slices
-    const int nt = __builtin_amdgcn_readfirstlane(*ntiles);
     const bool has_sh = sh_down != nullptr;
     const int total = 2 * nt + (has_sh ? 7 : 0);
     const int GW = gridDim.x * kDnWaves, gw = blockIdx.x * kDnWaves + w;
@@ -516,10 +516,13 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     Buf P0, P1;
     // unit q = (slice s0 + q / nkc, chunk q % nkc); past the end the last unit is loaded again
     const int nu = (s1 - s0) * nkc;
+    // the expert's down rows as a buffer: 32-bit lane offsets, the unit's start in a scalar
+    const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(W), 0, H * rb, 0x00020000);
     auto issue = [&](int q, Buf& B) {
         q = min(q, nu - 1);
         const int sl = s0 + q / nkc, c = q - (q / nkc) * nkc;
-        const uint8_t* base = W + (int64_t)(16 * sl) * rb + 288 * c;
+        const int soff = 16 * sl * rb + 288 * c;
         const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
         const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
 #pragma unroll
@@ -531,7 +534,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
                 const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
                 go = j < 16 * dpr ? (uint32_t)(row * rb + 4 * col) : 0u;
             }
-            B.v[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + go));
+            B.v[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, go, soff, 0);
         }
     };
     auto put = [&](int q, const Buf& B) {
@@ -555,22 +558,40 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         if (!ONEK) load_a(c);
         const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
         const uint32_t* wr = st + r * kDnStageDw;
+        // four blocks at a time: their index words and scales, then all 16
+        // table reads, then four independent steps
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            if (b < cbk) {
-                const int o = 18 * b + 2 + 4 * g;              // index bytes of lane group g
-                const uint32_t nib = (b & 1) ? wr[o >> 2]
-                                             : __builtin_amdgcn_alignbit(wr[(o >> 2) + 1], wr[o >> 2], 16);
-                const uint32_t dw = wr[(18 * b) >> 2];
-                const float d = f16_bits_to_f32((b & 1) ? (dw >> 16) : (dw & 0xffffu)) * 0.0078125f;
-                u32x4 bv;
-                bv[0] = lds_ld(((nib << 7) & 0x7f80u) | cbase);
-                bv[1] = lds_ld(((nib >> 1) & 0x7f80u) | cbase);
-                bv[2] = lds_ld(((nib >> 9) & 0x7f80u) | cbase);
-                bv[3] = lds_ld(((nib >> 17) & 0x7f80u) | cbase);
-                const f32x4 part = mfma16_f16(av[b], bv, f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int b0 = 0; b0 < 16; b0 += 4) {
+            if (b0 < cbk) {
+                uint32_t nib[4];
+                float d[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += part[i] * d;
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const int b = b0 + k4;
+                    const int o = 18 * b + 2 + 4 * g;          // index bytes of lane group g
+                    nib[k4] = (b & 1) ? wr[o >> 2] : __builtin_amdgcn_alignbit(wr[(o >> 2) + 1], wr[o >> 2], 16);
+                    const uint32_t dw = wr[(18 * b) >> 2];
+                    d[k4] = f16_bits_to_f32((b & 1) ? (dw >> 16) : (dw & 0xffffu)) * 0.0078125f;
+                }
+                u32x4 bv[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    bv[k4][0] = lds_ld(((nib[k4] << 7) & 0x7f80u) | cbase);
+                    bv[k4][1] = lds_ld(((nib[k4] >> 1) & 0x7f80u) | cbase);
+                    bv[k4][2] = lds_ld(((nib[k4] >> 9) & 0x7f80u) | cbase);
+                    bv[k4][3] = lds_ld(((nib[k4] >> 17) & 0x7f80u) | cbase);
+                }
+                f32x4 part[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4)
+                    part[k4] = mfma16_f16(av[b0 + k4], bv[k4], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    if (FULL16 || b0 + k4 < cbk) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] += part[k4][i] * d[k4];
+                    }
+                }
             }
         }
         if (c == nkc - 1) {                                 // slice done: rows m = 4g + i
