@@ -47,15 +47,19 @@ FLOP_PER_TOKEN = K * 2 * 3 * H * I + 2 * 3 * H * IS + 2 * H * E   # 106,954,752
 
 
 def stage1_bytes(T):
-    """Router partials + shared up|gate: W_r, shared up|gate, x, partial logits
-    written, shared activations written."""
-    return ROUTER_BYTES + SH_UG_BYTES + T * H * 2 + (H // 256) * T * E * 4 + T * IS * 2
+    """Stage 1: W_r and the shared up|gate rows read, x read, the logits, the
+    shared up|gate partials (one per 256-wide K chunk) and the fp16 copy of x
+    written."""
+    return (ROUTER_BYTES + SH_UG_BYTES + T * H * 2 + T * E * 4 + (H // 256) * T * 2 * IS * 4
+            + T * H * 2)
 
 
 def upgate_bytes(T, U):
-    """Routed up|gate kernel (bandwidth path): packed up|gate of the U distinct
-    routed experts + the tokens' fp16 rows + a written (fp16)."""
-    return U * UG_BYTES + T * H * 2 + T * K * I * 2
+    """Up|gate kernel (bandwidth path, routing included): the logits, the packed
+    up|gate of the U distinct routed experts, the tokens' fp16 rows and the
+    shared partials read; a (fp16 routed, bf16 shared) written."""
+    return (T * E * 4 + U * UG_BYTES + T * H * 2 + (H // 256) * T * 2 * IS * 4 + T * K * I * 2
+            + T * IS * 2)
 
 
 def down_bytes(T, U):
@@ -191,12 +195,12 @@ def main():
         U = float(np.mean(us))
         lb = layer_bytes(T, U)
         kd = time_kernels(T, x, max(args.layers, 16), args.layers, 8)
-        names = ["stage1", "route", "upgate", "down", "combine"]
+        names = ["stage1", "upgate", "down", "combine"]
         kern = {}
         for nm, t in zip(names, kd):
             kern[nm] = {"us": round(t * 1e3, 2)}
-        for nm, b, j in (("stage1", stage1_bytes(T), 0), ("upgate", upgate_bytes(T, U), 2),
-                         ("down", down_bytes(T, U), 3)):
+        for nm, b, j in (("stage1", stage1_bytes(T), 0), ("upgate", upgate_bytes(T, U), 1),
+                         ("down", down_bytes(T, U), 2)):
             kern[nm]["GBps"] = round(b / (kd[j] * 1e-3) / 1e9, 1)
             kern[nm]["hbm_frac"] = round(b / (kd[j] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         results["decode"][T] = {
@@ -237,11 +241,11 @@ def main():
         results["decode"][T].pop("_kd")
         results["decode"][T].pop("_U")
     ub = upgate_bytes(8, U8)
-    ach = ub / (kd8[2] * 1e-3) / 1e9
+    ach = ub / (kd8[1] * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for("k_upgate_dec", ub),
             "kernel": "k_upgate_dec (routed up|gate + SwiGLU, T=8)",
-            "bytes_per_launch": int(ub), "us_per_launch": round(kd8[2] * 1e3, 2)}
+            "bytes_per_launch": int(ub), "us_per_launch": round(kd8[1] * 1e3, 2)}
 
     cpu = None if args.no_cpu else cpu_baseline(layers, sh)
 

@@ -118,8 +118,8 @@ size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max);
 
 /* Router logits (A1): logits[t][e] = sum_h x[t][h] * W_r[e][h] + b[e], fp32
  * accumulation.  x bf16 [T][H], w_r bf16 [E][H], b fp32 [E] or NULL, logits
- * fp32 [T][E].  Same kernels moe_layer_forward runs.  Needs ws (>=
- * moe_workspace_size with the same H, E and T).
+ * fp32 [T][E].  Same kernels moe_layer_forward runs.  ws / ws_bytes are
+ * not used (may be NULL / 0).
  * Reading: the pages place "routers" in the dense part (model card, "Files /
  * Main model") and give no formula; a linear router with a per-expert bias. */
 moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,

@@ -58,14 +58,14 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // ---- workspace layout for one (shape, T)
 struct Ws {
-    size_t x16, part, shp, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm,
+    size_t x16, shp, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm,
         y_sh, hist, total;
     int max_tiles;
 };
 
 // The layer runs the bandwidth path for T <= kDecMaxT tokens when its up|gate
 // kernel can stage two items of the hidden size; otherwise the grouped GEMMs.
-bool dec_path(int T, int H) { return T <= kDecMaxT && upgate_dec_supported(H); }
+bool dec_path(int T, int H, int E) { return T <= kDecMaxT && upgate_dec_supported(H, T, E); }
 
 // tiles of the expert kernels: one per active expert (bandwidth path) or per
 // kGemmBM rows of an expert (grouped GEMM)
@@ -85,10 +85,9 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     };
     const size_t n = (size_t)T * k;
     const int tdec = T < kDecMaxT ? T : kDecMaxT;
-    s.max_tiles = max_tiles_for(T, E, k, dec_path(T, H));
+    s.max_tiles = max_tiles_for(T, E, k, dec_path(T, H, E));
     s.x16 = take((size_t)T * H * 2);
-    s.part = take((size_t)(H / kRouterKChunk) * tdec * E * 4);
-    s.shp = take((size_t)(H / kRouterKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
+    s.shp = take((size_t)(H / kShKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
     s.logits = take((size_t)T * E * 4);
     s.ids = take(n * 4);
     s.w = take(n * 4);
@@ -195,14 +194,13 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
         return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18, H % 256 == 0 in [256, 8192], 1 <= E <= 1024");
     if (!al16(x) || !al16(w_r) || !al4(logits) || (b && !al4(b)))
         return fail(MOE_ERR_ALIGN, "x and w_r must be 16-byte aligned");
-    const size_t need = (T <= kDecMaxT) ? (size_t)(H / kRouterKChunk) * T * E * 4 : 0;
-    if (need && (!ws || ws_bytes < need)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+    (void)ws;
+    (void)ws_bytes;
     moe_status s = check_device();
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     if (T <= kDecMaxT) {
-        launch_dec_stage1(x, T, H, E, w_r, (float*)ws, nullptr, 0, nullptr, nullptr, st);
-        launch_router_reduce((const float*)ws, H / kRouterKChunk, T, E, b, logits, st);
+        launch_dec_stage1(x, T, H, E, w_r, b, logits, nullptr, 0, nullptr, nullptr, st);
     } else {
         launch_gemm_router(x, T, H, E, w_r, b, logits, st);
     }
@@ -350,7 +348,6 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     const uint16_t* sug = has_sh ? (const uint16_t*)wts->shared_upgate : nullptr;
     const uint16_t* sdn = has_sh ? (const uint16_t*)wts->shared_down : nullptr;
     uint16_t* x16 = at<uint16_t>(ws, L.x16);
-    float* part = at<float>(ws, L.part);
     float* shp = at<float>(ws, L.shp);
     float* lg = at<float>(ws, L.logits);
     int32_t* ids = at<int32_t>(ws, L.ids);
@@ -367,18 +364,17 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     int32_t* hist = at<int32_t>(ws, L.hist);
 
     mk->mark();
-    if (dec_path(T, H)) {
-        // stage 1 always runs: router partials (no given logits), shared up|gate
+    if (dec_path(T, H, E)) {
+        // stage 1 always runs: router logits (none given), shared up|gate
         // partials (shared expert present) and the fp16 copy of x
         launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
-                          part, sug, Is, shp, x16, st);
+                          wts->router_b, lg, sug, Is, shp, x16, st);
         mk->mark();
-        launch_route_small(part, H / kRouterKChunk, wts->router_b, logits_or_null, x, H, nullptr,
-                           T, E, k, ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt,
-                           st);
-        mk->mark();
-        launch_upgate_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, T, H, I,
-                          a16, has_sh ? shp : nullptr, Is, ash, n_cu, st);
+        // routing runs inside the up|gate kernel (its block 0 writes it out)
+        const RouteOut ro{ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt};
+        launch_upgate_dec(ex, wts->expert_stride, logits_or_null ? logits_or_null : lg, E, k,
+                          L.max_tiles, x16, T, H, I, a16, has_sh ? shp : nullptr, Is, ash, ro,
+                          n_cu, st);
         mk->mark();
         launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, k, sdn, ash,
                         Is, yp, ysh, n_cu, st);

@@ -150,38 +150,79 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // Exact top-k of one row of E logits by one wave64 (E <= 1024, k <= 32).
 // Lane j < k returns (id_j, L_j) in selection order; other lanes return
 // (-1, 0).  `get(e)` yields the fp32 logit of expert e (lane l holds experts
-// l, l+64, ...).  Each round: the largest value key over the wave, then the
-// lowest expert index among the lanes holding that value.
-template <typename Get>
-__device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, float& out_val) {
-    const int lane = __lane_id();
-    uint32_t keys[16];
-    uint32_t alive = 0;
+// l, l+64, ...).  Each lane first sorts its Q candidates by (logit desc,
+// expert asc) with a sorting network (all pairs distinct, so any network
+// gives the one order); then each round takes the largest head over the wave
+// (then the lowest expert among equal heads) and the winning lane drops its
+// head.
+template <int Q>
+__device__ __forceinline__ void lane_sort_desc(uint32_t* key, int* idx) {
+    auto ce = [&](int a, int b) {                  // a < b: put the larger (key, -idx) first
+        const bool sw = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
+        const uint32_t ka = key[a], kb = key[b];
+        const int ia = idx[a], ib = idx[b];
+        key[a] = sw ? kb : ka;
+        key[b] = sw ? ka : kb;
+        idx[a] = sw ? ib : ia;
+        idx[b] = sw ? ia : ib;
+    };
+    if constexpr (Q == 8) {                        // Batcher's odd-even merge sort, 19 pairs
+        ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+        ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+        ce(1, 2); ce(5, 6);
+        ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+        ce(2, 4); ce(3, 5);
+        ce(1, 2); ce(3, 4); ce(5, 6);
+    } else {                                       // odd-even transposition sort
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        keys[i] = (e < E) ? order_key(get(e)) : 0u;
-        alive |= (e < E) ? (1u << i) : 0u;
+        for (int rd = 0; rd < Q; ++rd)
+#pragma unroll
+            for (int a = rd & 1; a + 1 < Q; a += 2) ce(a, a + 1);
     }
+}
+
+template <int Q, typename Get>
+__device__ __forceinline__ void wave_topk_q(Get get, int E, int k, int& out_id, float& out_val) {
+    const int lane = __lane_id();
+    uint32_t key[Q];
+    int idx[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? order_key(get(e)) : 0u;     // 0 sorts last (below every real key)
+        idx[i] = (e < E) ? i : 1024;
+    }
+    lane_sort_desc<Q>(key, idx);
     out_id = -1;
     out_val = 0.f;
     for (int j = 0; j < k; ++j) {
-        uint32_t best = 0u, bi = 16u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bool take = ((alive >> i) & 1u) && (bi == 16u || keys[i] > best);
-            best = take ? keys[i] : best;
-            bi = take ? (uint32_t)i : bi;
-        }
-        const uint32_t m = wave_max_u32(bi < 16u ? best : 0u);
-        const uint32_t cand = (bi < 16u && best == m) ? (uint32_t)lane + 64u * bi : 0xffffffffu;
+        const bool has = idx[0] < 1024;
+        const uint32_t m = wave_max_u32(has ? key[0] : 0u);
+        const uint32_t cand = (has && key[0] == m) ? (uint32_t)(lane + 64 * idx[0]) : 0xffffffffu;
         const uint32_t win = wave_min_u32(cand);
-        if ((int)(win & 63u) == lane) alive &= ~(1u << (win >> 6));
+        if ((int)(win & 63u) == lane) {                  // drop the head
+#pragma unroll
+            for (int i = 0; i + 1 < Q; ++i) {
+                key[i] = key[i + 1];
+                idx[i] = idx[i + 1];
+            }
+            key[Q - 1] = 0u;
+            idx[Q - 1] = 1024;
+        }
         if (lane == j) {
             out_id = (int)win;
             out_val = order_key_value(m);
         }
     }
+}
+
+template <typename Get>
+__device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, float& out_val) {
+    if (E <= 64) wave_topk_q<1>(get, E, k, out_id, out_val);
+    else if (E <= 128) wave_topk_q<2>(get, E, k, out_id, out_val);
+    else if (E <= 256) wave_topk_q<4>(get, E, k, out_id, out_val);
+    else if (E <= 512) wave_topk_q<8>(get, E, k, out_id, out_val);
+    else wave_topk_q<16>(get, E, k, out_id, out_val);
 }
 
 // Softmax over the k selected logits held by lanes 0..k-1 (lane 0 = max).

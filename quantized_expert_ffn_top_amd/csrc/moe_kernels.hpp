@@ -8,7 +8,8 @@ namespace moe {
 
 // Work sizes shared by host and device code.
 constexpr int kDecMaxT = 16;          // tokens handled by the bandwidth path
-constexpr int kRouterKChunk = 256;    // K per router partial (bandwidth path)
+constexpr int kShKChunk = 256;        // K per shared up|gate partial (bandwidth path)
+constexpr int kMaxSlots = kDecMaxT * 32;  // T * k slots of the bandwidth path
 constexpr int kGemmBM = 128;          // rows per grouped-GEMM tile
 constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
@@ -18,13 +19,6 @@ void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, 
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st);
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                  int32_t* ids2, float* w2, hipStream_t st);
-void launch_router_reduce(const float* part, int nkc, int T, int E, const float* bias,
-                          float* logits, hipStream_t st);
-void launch_route_small(const float* part, int nkc, const float* bias, const float* given,
-                        const uint16_t* x, int H, uint16_t* x16, int T, int E, int k,
-                        int32_t* ids, float* w, int32_t* ids_out, float* w_out,
-                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* ntiles, hipStream_t st);
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t st);
 void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32_t* hist,
@@ -38,14 +32,28 @@ void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps,
                     uint16_t* normed, hipStream_t st);
 
 // ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT and
-// upgate_dec_supported(H) (the staged up|gate rows of two items fit in LDS)
-bool upgate_dec_supported(int H);
-void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
-                       const uint16_t* sh_ug, int Is, float* shp, uint16_t* x16, hipStream_t st);
-void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
-                       const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
-                       const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                       const float* shp, int Is, uint16_t* a_sh, int n_cu, hipStream_t st);
+// upgate_dec_supported(H, T, E) (the staged up|gate rows of two items and the
+// routing scratch fit in LDS)
+bool upgate_dec_supported(int H, int T, int E);
+void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
+                       const float* bias, float* logits, const uint16_t* sh_ug, int Is,
+                       float* shp, uint16_t* x16, hipStream_t st);
+// Routing results of the bandwidth path, written by the up|gate kernel.
+struct RouteOut {
+    int32_t* ids;
+    float* w;
+    int32_t* ids_out;        // optional copies for the caller
+    float* w_out;
+    int32_t* offsets;        // [E + 1]
+    int32_t* perm;           // [T * k]
+    int32_t* inv;            // [T * k]
+    int32_t* tiles;          // [3 * active experts]
+    int32_t* ntiles;
+};
+void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int E,
+                       int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
+                       uint16_t* a16_perm, const float* shp, int Is, uint16_t* a_sh,
+                       const RouteOut& ro, int n_cu, hipStream_t st);
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                      const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int T, int H,
                      int I, int k, const uint16_t* sh_down, const uint16_t* a_sh, int Is,

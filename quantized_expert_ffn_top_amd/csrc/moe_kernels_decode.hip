@@ -28,26 +28,69 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 }
 
 // ---------------------------------------------------------------- stage 1
-// Wave-sized items, no block-level synchronisation.  Items [0, n_r): router
-// partial logits of 16 experts over one 256-wide K chunk, part[kc][t][e].
-// Items [n_r, n_r + n_s): shared expert up|gate partials of 16 rows (rows
-// 0..Is-1 up, Is..2Is-1 gate) over one K chunk, shp[kc][t][2 Is]; summed and
-// passed through SwiGLU by the up|gate kernel.  A = tokens (bf16, rows >= T
-// zero), B = bf16 weight rows, 16x16x32 bf16 steps.  The last H/256 waves
-// write the fp16 copy of the tokens, one 256-wide K chunk each.
-__global__ void __launch_bounds__(512) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
+// Blocks of 16 waves.  Blocks [0, n_rb): router logits of 16 experts: the
+// waves split K in 16 equal parts (16x16x32 bf16 steps, A = tokens, rows >= T
+// zero), their partial sums are added in wave order through LDS and the bias
+// is added last: logits[t][e].  Blocks [n_rb, ...): wave-sized items, no
+// block synchronisation.  Items [0, n_s): shared expert up|gate partials of 16
+// rows (rows 0..Is-1 up, Is..2Is-1 gate) over one 256-wide K chunk,
+// shp[kc][t][2 Is]; summed and passed through SwiGLU by the up|gate kernel.
+// The last H/256 wave items write the fp16 copy of the tokens, one 256-wide
+// K chunk each.
+__global__ void __launch_bounds__(1024) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
                                                     int E, const uint16_t* __restrict__ w_r,
-                                                    float* __restrict__ part, int n_r,
+                                                    const float* __restrict__ bias,
+                                                    float* __restrict__ logits, int n_rb,
                                                     const uint16_t* __restrict__ sh_ug, int Is,
                                                     float* __restrict__ shp, int n_s,
                                                     uint16_t* __restrict__ x16) {
-    const int lane = __lane_id();
-    const int wi = blockIdx.x * 8 + (int)(threadIdx.x >> 6);
-    const int n_x = H / kRouterKChunk;               // waves [n_r + n_s, +n_x): fp16 copy of x
-    if (wi >= n_r + n_s && wi < n_r + n_s + n_x) {
-        const int k0 = (wi - n_r - n_s) * kRouterKChunk;
-        for (int i = lane; i < T * (kRouterKChunk / 4); i += 64) {
-            const int t = i / (kRouterKChunk / 4), c = (i % (kRouterKChunk / 4)) * 4;
+    __shared__ f32x4 red[16][64];
+    const int lane = __lane_id(), w = (int)(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bool vt = r < T;
+    if ((int)blockIdx.x < n_rb) {
+        const int row = blockIdx.x * 16 + r;
+        const bool vr = row < E;
+        const int S = H / 32, sa = w * S / 16, sb = (w + 1) * S / 16;   // this wave's K steps
+        const uint16_t* brow = w_r + (int64_t)(vr ? row : 0) * H + 8 * g;
+        const uint16_t* arow = x + (int64_t)(vt ? r : 0) * H + 8 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = sa; s0 < sb; s0 += 8) {                // up to 8 steps' loads in flight
+            u32x4 a[8], b[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bool ok = s0 + s < sb;
+                a[s] = (vt && ok) ? ld16(arow + 32 * (s0 + s)) : zero;
+                b[s] = (vr && ok) ? ld16_stream(brow + 32 * (s0 + s)) : zero;
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) acc = mfma16_bf16(a[s], b[s], acc);
+        }
+        red[w][lane] = acc;
+        __syncthreads();
+        if (w == 0) {
+            f32x4 sum = red[0][lane];
+#pragma unroll
+            for (int v = 1; v < 16; ++v)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum[i] += red[v][lane][i];
+            const float bb = (vr && bias) ? bias[row] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i;
+                if (m < T && vr) logits[(int64_t)m * E + row] = sum[i] + bb;
+            }
+        }
+        return;
+    }
+    const int wi = (blockIdx.x - n_rb) * 16 + w;
+    const int n_x = H / kShKChunk;               // waves [n_s, n_s + n_x): fp16 copy of x
+    if (wi >= n_s) {
+        if (wi >= n_s + n_x) return;
+        const int k0 = (wi - n_s) * kShKChunk;
+        for (int i = lane; i < T * (kShKChunk / 4); i += 64) {
+            const int t = i / (kShKChunk / 4), c = (i % (kShKChunk / 4)) * 4;
             const uint2 v = *reinterpret_cast<const uint2*>(x + (int64_t)t * H + k0 + c);
             *reinterpret_cast<uint2*>(x16 + (int64_t)t * H + k0 + c) = make_uint2(
                 pack2(f32_to_f16_bits(bf16_to_f32(v.x & 0xffffu)), f32_to_f16_bits(bf16_to_f32(v.x >> 16))),
@@ -55,49 +98,168 @@ __global__ void __launch_bounds__(512) k_dec_stage1(const uint16_t* __restrict__
         }
         return;
     }
-    const int r = lane & 15, g = lane >> 4;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bool vt = r < T;
-    const uint16_t* W;
-    int rows_total, row0, kc, ld_out;
-    float* out;
-    if (wi < n_r) {
-        const int n_et = (E + 15) / 16;
-        row0 = (wi % n_et) * 16;
-        kc = wi / n_et;
-        W = w_r;
-        rows_total = E;
-        out = part + (int64_t)kc * T * E;
-        ld_out = E;
-    } else if (wi < n_r + n_s) {
-        const int si = wi - n_r, n_st = 2 * Is / 16;
-        row0 = (si % n_st) * 16;
-        kc = si / n_st;
-        W = sh_ug;
-        rows_total = 2 * Is;
-        out = shp + (int64_t)kc * T * 2 * Is;
-        ld_out = 2 * Is;
-    } else {
-        return;
-    }
+    const int n_st = 2 * Is / 16;
+    const int row0 = (wi % n_st) * 16, kc = wi / n_st;
     const int row = row0 + r;
-    const bool vr = row < rows_total;
-    const uint16_t* brow = W + (int64_t)(vr ? row : 0) * H + kc * kRouterKChunk + 8 * g;
-    const uint16_t* arow = x + (int64_t)(vt ? r : 0) * H + kc * kRouterKChunk + 8 * g;
+    const uint16_t* brow = sh_ug + (int64_t)row * H + kc * kShKChunk + 8 * g;
+    const uint16_t* arow = x + (int64_t)(vt ? r : 0) * H + kc * kShKChunk + 8 * g;
     u32x4 a[8], b[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         a[s] = vt ? ld16(arow + 32 * s) : zero;
-        b[s] = vr ? ld16_stream(brow + 32 * s) : zero;
+        b[s] = ld16_stream(brow + 32 * s);
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc = mfma16_bf16(a[s], b[s], acc);
+    float* out = shp + (int64_t)kc * T * 2 * Is;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < T && vr) out[(int64_t)m * ld_out + row] = acc[i];
+        if (m < T) out[(int64_t)m * 2 * Is + row] = acc[i];
     }
+}
+
+// ---------------------------------------------------------------- routing
+// Block-wide exclusive scan of one int per thread (NT threads, <= 16 waves);
+// `total` receives the sum.  lds: >= 33 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
+    constexpr int NW = NT / 64;
+    const int lane = __lane_id(), wid = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) lds[wid] = incl;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int sv = lane < NW ? lds[lane] : 0;
+        int si = sv;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int o = __shfl_up(si, off, 64);
+            if (lane >= off) si += o;
+        }
+        if (lane < NW) lds[16 + lane] = si - sv;
+        if (lane == NW - 1) lds[32] = si;
+    }
+    __syncthreads();
+    total = lds[32];
+    const int r = lds[16 + wid] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+// Routing of T <= 16 tokens by one block of NT threads (README of the
+// model: 10 of 512 experts per token; softmax over the selected logits):
+// top-k per token (one wave per token: larger logit first, lower expert
+// index on ties), the softmax of the selected logits, then the stable
+// counting sort of the T*k slots by expert.  A token selects an expert at
+// most once, so the rank of slot (t, j) in expert e is the number of earlier
+// tokens that selected e: a popcount of the token mask of e.  Results in LDS:
+// s_tiles (active experts in ascending order: expert, first slot, slots),
+// s_perm (slot -> flat index t*k + j) and *s_nt; with `publish` also to global
+// memory (ids, w, the optional copies, offsets [E+1], perm, inv, tiles,
+// ntiles).  scr: >= route_scratch_bytes(T, E) of LDS (the logits are staged
+// there with batched loads before the top-k reads them).
+__host__ __device__ constexpr int route_scratch_bytes(int T, int E) { return 10752 + T * E * 4; }
+
+template <int NT>
+__device__ __forceinline__ void route_block(const float* __restrict__ logits, int T, int E, int k,
+                                            uint8_t* scr, int* s_tiles, int* s_perm, int* s_nt,
+                                            bool publish, int32_t* ids, float* wts,
+                                            int32_t* ids_out, float* w_out, int32_t* offsets,
+                                            int32_t* perm, int32_t* inv, int32_t* tiles,
+                                            int32_t* ntiles) {
+    uint32_t* s_mask = reinterpret_cast<uint32_t*>(scr);          // [1024]
+    int* s_first = reinterpret_cast<int*>(scr + 4096);             // [1024]
+    int* s_ids = reinterpret_cast<int*>(scr + 8192);               // [512]
+    int* s_scan = reinterpret_cast<int*>(scr + 10240);             // [40]
+    float* s_log = reinterpret_cast<float*>(scr + 10752);          // [T][E]
+    const int tid = threadIdx.x, lane = __lane_id(), wid = threadIdx.x >> 6;
+    for (int e = tid; e < 1024; e += NT) s_mask[e] = 0u;
+    const int nl = T * E;
+    for (int i0 = tid; i0 < nl; i0 += 8 * NT) {                    // 8 loads in flight per thread
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = logits[min(i0 + u * NT, nl - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (i0 + u * NT < nl) s_log[i0 + u * NT] = v[u];
+    }
+    __syncthreads();
+    for (int t = wid; t < T; t += NT / 64) {
+        const float* row = s_log + t * E;
+        int id;
+        float v;
+        wave_topk([&](int e) { return row[e]; }, E, k, id, v);
+        const float wt = wave_softmax_selected(v, k);
+        if (lane < k) {
+            s_ids[t * k + lane] = id;
+            atomicOr(&s_mask[id], 1u << t);
+            if (publish) {
+                ids[t * k + lane] = id;
+                wts[t * k + lane] = wt;
+                if (ids_out) ids_out[t * k + lane] = id;
+                if (w_out) w_out[t * k + lane] = wt;
+            }
+        }
+    }
+    __syncthreads();
+    // thread tid owns experts QE*tid .. QE*tid + QE - 1 (in order)
+    constexpr int QE = (1024 + NT - 1) / NT;
+    int c[QE], cs = 0, as = 0;
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+        const int e = QE * tid + q;
+        c[q] = e < E ? __popc(s_mask[e]) : 0;
+        cs += c[q];
+        as += c[q] > 0 ? 1 : 0;
+    }
+    int tot_c, tot_a;
+    int off = block_excl_scan<NT>(cs, s_scan, tot_c);
+    int ai = block_excl_scan<NT>(as, s_scan, tot_a);
+#pragma unroll
+    for (int q = 0; q < QE; ++q) {
+        const int e = QE * tid + q;
+        if (e < E) {
+            s_first[e] = off;
+            if (publish) offsets[e] = off;
+            if (c[q] > 0) {
+                s_tiles[3 * ai] = e;
+                s_tiles[3 * ai + 1] = off;
+                s_tiles[3 * ai + 2] = c[q];
+                if (publish) {
+                    tiles[3 * ai] = e;
+                    tiles[3 * ai + 1] = off;
+                    tiles[3 * ai + 2] = c[q];
+                }
+                ++ai;
+            }
+            off += c[q];
+        }
+    }
+    if (tid == 0) {
+        *s_nt = tot_a;
+        if (publish) {
+            offsets[E] = tot_c;
+            *ntiles = tot_a;
+        }
+    }
+    __syncthreads();
+    for (int f = tid; f < T * k; f += NT) {
+        const int t = f / k, e = s_ids[f];
+        const int p = s_first[e] + __popc(s_mask[e] & ((1u << t) - 1u));
+        s_perm[p] = f;
+        if (publish) {
+            perm[p] = f;
+            inv[f] = p;
+        }
+    }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- up|gate
@@ -135,6 +297,8 @@ __device__ __forceinline__ uint32_t q3_pair_addr(const uint32_t* w, uint32_t bas
 __host__ __device__ constexpr int ug_red_bytes(int waves) { return 2 * waves * 2 * 64 * 16; }
 
 __host__ __device__ constexpr int ug_stage_stride(int H) { return (H / 256) * 104 + 8; }
+// static LDS of the up|gate kernel: the table, the tiles and slot map of the routing
+constexpr int kUgStaticLds = kQ3LutDw * 4 + 4 * (4 * kMaxSlots + 1) + 16;
 // one stage: 32 rows and a 16-byte scratch slot for the loads past the rows
 __host__ __device__ constexpr int ug_stage_bytes(int H) { return 32 * ug_stage_stride(H) + 16; }
 // 12 waves (3 per SIMD) when the H/128 K groups split evenly over them, else 8
@@ -161,15 +325,15 @@ __host__ __device__ constexpr int ug_waves(int H) {
 // expert: a_sh[t][o] = bf16(silu(sum_c g) * sum_c u) over the stage-1 chunks.
 template <int GPW, bool FULL, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
-    const uint8_t* __restrict__ experts, int64_t estride, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ ntiles, const int32_t* __restrict__ perm, int k,
-    const uint16_t* __restrict__ x16, int T, int H, int I, uint16_t* __restrict__ a16_perm,
-    const float* __restrict__ shp, int nkc, int Is, uint16_t* __restrict__ a_sh) {
+    const uint8_t* __restrict__ experts, int64_t estride, const float* __restrict__ logits, int E,
+    int k, const uint16_t* __restrict__ x16, int T, int H, int I, uint16_t* __restrict__ a16_perm,
+    const float* __restrict__ shp, int nkc, int Is, uint16_t* __restrict__ a_sh, RouteOut ro) {
     constexpr int NT = 64 * WAVES;                          // threads
     constexpr int CH = FULL ? 16 : 8;                       // bytes per staging load
     // chunks per thread: 32 rows of <= 52 * WAVES * GPW bytes
     constexpr int NCH = (32 * 52 * WAVES * GPW / CH + NT - 1) / NT;
     __shared__ __attribute__((aligned(8192))) uint32_t lut[kQ3LutDw];  // pair bits OR onto the address
+    __shared__ int s_tiles[3 * kMaxSlots], s_perm[kMaxSlots], s_nt;
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     f32x4 (*red)[WAVES][2][64] = reinterpret_cast<f32x4 (*)[WAVES][2][64]>(dyn);
     uint8_t* stage = dyn + ug_red_bytes(WAVES);
@@ -177,8 +341,11 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int tid = threadIdx.x, lane = __lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
+    // routing (every block; block 0 publishes it), in the partial-sum space
+    route_block<NT>(logits, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids, ro.w,
+                    ro.ids_out, ro.w_out, ro.offsets, ro.perm, ro.inv, ro.tiles, ro.ntiles);
     const int nsl = I / 16;
-    const int n_items = __builtin_amdgcn_readfirstlane(*ntiles) * nsl;
+    const int n_items = __builtin_amdgcn_readfirstlane(s_nt) * nsl;
     const int G = gridDim.x;
     const int i0 = (int)((int64_t)blockIdx.x * n_items / G);
     const int i1 = (int)((int64_t)(blockIdx.x + 1) * n_items / G);
@@ -220,7 +387,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     Buf P0, P1;
     auto issue = [&](int i, Buf& B) {
         const int ic = min(i, max(0, min(i1, n_items) - 1)), at = ic / nsl, sl = ic - at * nsl;
-        const int e = tiles[3 * at];
+        const int e = __builtin_amdgcn_readfirstlane(s_tiles[3 * at]);
         const uint8_t* base = experts + (int64_t)e * estride + (int64_t)(16 * sl) * rb;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -254,7 +421,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
 
     auto decode = [&](int it, int sb) {                     // sb: stage of item it
         const int at = it / nsl, sl = it - at * nsl;
-        const int row0 = tiles[3 * at + 1], rows = tiles[3 * at + 2];
+        const int row0 = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 1]);
+        const int rows = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 2]);
         const uint32_t st = lds_addr(stage + sb * ug_stage_bytes(H));
         f32x4 acc_u = {0.f, 0.f, 0.f, 0.f}, acc_g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -313,12 +481,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
         const int j = tid >> 4, n = tid & 15;
         uint16_t av16 = 0;
         if (w < 4) {
-            // slots 4w .. 4w+3 of the tile (scalar loads; past `rows` they are
-            // other tiles' slots or the next workspace array, never used)
-            const int* ps = perm + row0 + 4 * w;
-            const int s0 = ps[0], s1 = ps[1], s2 = ps[2], s3 = ps[3];
-            const int slot = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
-            const int tj = (int)(((uint32_t)(j < rows ? slot : 0) * kmag) >> 16);
+            const int slot = s_perm[row0 + (j < rows ? j : 0)];
+            const int tj = (int)(((uint32_t)slot * kmag) >> 16);
             const float* ru =
                 reinterpret_cast<const float*>(&red[buf][0][0][(tj >> 2) * 16 + n]) + (tj & 3);
             float u = 0.f, gg = 0.f;
@@ -382,15 +546,17 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
             for (int c0 = 0; c0 < nkc; c0 += 8) {           // 16 loads in flight, summed in chunk order
                 float pu[8], pg[8];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float* p = shp + ((int64_t)(c0 + c) * T + t) * 2 * Is;
-                    pu[c] = c0 + c < nkc ? p[o] : 0.f;
-                    pg[c] = c0 + c < nkc ? p[Is + o] : 0.f;
+                for (int c = 0; c < 8; ++c) {                // clamped: no branch around the loads
+                    const float* p = shp + ((int64_t)min(c0 + c, nkc - 1) * T + t) * 2 * Is;
+                    pu[c] = p[o];
+                    pg[c] = p[Is + o];
                 }
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    u += pu[c];
-                    gg += pg[c];
+                    if (c0 + c < nkc) {
+                        u += pu[c];
+                        gg += pg[c];
+                    }
                 }
             }
             a_sh[i] = (uint16_t)f32_to_bf16(silu_mul(gg, u));
@@ -628,48 +794,52 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
 
 // ---------------------------------------------------------------- launchers
 
-void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r, float* part,
-                       const uint16_t* sh_ug, int Is, float* shp, uint16_t* x16, hipStream_t st) {
-    const int nkc = H / kRouterKChunk;
-    const int n_r = w_r ? ((E + 15) / 16) * nkc : 0;
+void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
+                       const float* bias, float* logits, const uint16_t* sh_ug, int Is,
+                       float* shp, uint16_t* x16, hipStream_t st) {
+    const int nkc = H / kShKChunk;
+    const int n_rb = w_r ? (E + 15) / 16 : 0;
     const int n_s = (sh_ug && Is > 0) ? (2 * Is / 16) * nkc : 0;
     const int n_x = x16 ? nkc : 0;
-    if (n_r + n_s + n_x == 0) return;
-    k_dec_stage1<<<(n_r + n_s + n_x + 7) / 8, 512, 0, st>>>(x, T, H, E, w_r, part, n_r, sh_ug, Is,
-                                                            shp, n_s, x16);
+    const int n_wb = (n_s + n_x + 15) / 16;
+    if (n_rb + n_wb == 0) return;
+    k_dec_stage1<<<n_rb + n_wb, 1024, 0, st>>>(x, T, H, E, w_r, bias, logits, n_rb, sh_ug, Is, shp,
+                                              n_s, x16);
 }
 
 template <int GPW, bool FULL, int WAVES>
 static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, int64_t estride,
-                         const int32_t* tiles, const int32_t* ntiles, const int32_t* perm, int k,
-                         const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                         const float* shp, int nkc, int Is, uint16_t* a_sh) {
-    const size_t dyn = ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H);
+                         const float* logits, int E, int k, const uint16_t* x16, int T, int H,
+                         int I, uint16_t* a16_perm, const float* shp, int nkc, int Is,
+                         uint16_t* a_sh, const RouteOut& ro) {
+    const size_t dyn = std::max((size_t)ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H),
+                                (size_t)route_scratch_bytes(T, E));
     static bool attr = false;                      // opt in to more than 64 KB of LDS once
     if (!attr) {
         hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kQ3LutDw * 4);
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024 - kUgStaticLds);
         attr = true;
     }
     k_upgate_dec<GPW, FULL, WAVES><<<grid, 64 * WAVES, dyn, st>>>(
-        experts, estride, tiles, ntiles, perm, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh);
+        experts, estride, logits, E, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro);
 }
 
-void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
-                       const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
-                       const uint16_t* x16, int T, int H, int I, uint16_t* a16_perm,
-                       const float* shp, int Is, uint16_t* a_sh, int n_cu, hipStream_t st) {
+void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int E,
+                       int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
+                       uint16_t* a16_perm, const float* shp, int Is, uint16_t* a_sh,
+                       const RouteOut& ro, int n_cu, hipStream_t st) {
     const int max_items = max_tiles * (I / 16);
     const unsigned grid = (unsigned)std::max(1, std::min(n_cu, max_items));
-    const int nkc = H / kRouterKChunk;
+    const int nkc = H / kShKChunk;
     // 12 waves (3 per SIMD) when the K groups split evenly over them, else 8
     const int NG = H / 128;
     const int waves = ug_waves(H);
     const int gpw = (NG + waves - 1) / waves;
     const bool full = NG == waves * gpw;
     shp = (Is > 0) ? shp : nullptr;
-#define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, tiles, ntiles, perm, k, \
-                                               x16, T, H, I, a16_perm, shp, nkc, Is, a_sh)
+#define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, logits, E, k, x16, T, H, \
+                                               I, a16_perm, shp, nkc, Is, a_sh, ro)
     if (waves == 12) {
         if (gpw == 1) MOE_UGT(1, true, 12);
         else MOE_UGT(2, true, 12);
@@ -688,9 +858,9 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const int32_t* t
 #undef MOE_UGT
 }
 
-bool upgate_dec_supported(int H) {
-    return H / 128 <= 8 * 4 &&
-           kQ3LutDw * 4 + ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H) <= 160 * 1024;
+bool upgate_dec_supported(int H, int T, int E) {
+    const int dyn = std::max(ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H), route_scratch_bytes(T, E));
+    return H / 128 <= 8 * 4 && kUgStaticLds + dyn <= 160 * 1024;
 }
 
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,

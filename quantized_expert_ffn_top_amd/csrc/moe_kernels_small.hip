@@ -84,16 +84,6 @@ __global__ void k_topk(const float* __restrict__ logits, int T, int E, int k,
     }
 }
 
-// Sum of the per-chunk router partials (+ bias) -> logits fp32 [T][E].
-__global__ void k_router_reduce(const float* __restrict__ part, int nkc, int T, int E,
-                                const float* __restrict__ bias, float* __restrict__ logits) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= T * E) return;
-    float s = 0.f;
-    for (int c = 0; c < nkc; ++c) s += part[(int64_t)c * T * E + i];
-    if (bias) s += bias[i % E];
-    logits[i] = s;
-}
 
 // Block-wide exclusive scan of one int per thread (blockDim must be 1024).
 // `total` receives the sum over the block.  lds: >= 33 ints.
@@ -132,10 +122,10 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* lds, int& total)
 // is the number of set bits of s_mask[e] below bit t.  Writes offsets [E+1],
 // perm, inv and (if `tiles`) the active experts as tiles (expert, first row,
 // rows) in ascending expert order.
-__device__ void small_counting_sort(const int* s_ids, const uint32_t* s_mask, int* s_first,
-                                    int* s_scan, int T, int E, int k, int32_t* offsets,
-                                    int32_t* perm, int32_t* inv, int32_t* tiles,
-                                    int32_t* ntiles) {
+__device__ __forceinline__ void small_counting_sort(const int* s_ids, const uint32_t* s_mask,
+                                                    int* s_first, int* s_scan, int T, int E, int k,
+                                                    int32_t* offsets, int32_t* perm, int32_t* inv,
+                                                    int32_t* tiles, int32_t* ntiles) {
     const int tid = threadIdx.x;
     const int c = (tid < E) ? __popc(s_mask[tid]) : 0;
     int tot_c, tot_a;
@@ -163,89 +153,7 @@ __device__ void small_counting_sort(const int* s_ids, const uint32_t* s_mask, in
     }
 }
 
-// Decode routing, T <= 16, one workgroup of 1024 threads: the fp16 copy of
-// x; the logits (sum of the router partials in chunk order + bias, or the
-// given ones) into LDS; top-k + softmax per token (wave t); then the stable
-// counting sort of the T*k slots, the active experts as tiles and their
-// token-major view.
-__global__ void __launch_bounds__(1024) k_route_small(
-    const float* __restrict__ part, int nkc, const float* __restrict__ bias,
-    const float* __restrict__ given_logits, const uint16_t* __restrict__ x, int H,
-    uint16_t* __restrict__ x16, int T, int E, int k,
-    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-    __shared__ float s_log[16 * 1024];
-    __shared__ int s_ids[16 * 32];
-    __shared__ uint32_t s_mask[1024];
-    __shared__ int s_first[1024];
-    __shared__ int s_scan[40];
-    const int tid = threadIdx.x, lane = __lane_id(), wid = tid >> 6;
-
-    s_mask[tid] = 0u;
-    // fp16 copy of x (when stage 1 did not make it), 8 elements per step
-    const int n8 = x16 ? T * H / 8 : 0;
-    for (int i = tid; i < n8; i += 1024) {
-        const u32x4 v = ld16(x + 8 * (int64_t)i);
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            o[q] = pack2(f32_to_f16_bits(bf16_to_f32(v[q] & 0xffffu)),
-                         f32_to_f16_bits(bf16_to_f32(v[q] >> 16)));
-        *reinterpret_cast<u32x4*>(x16 + 8 * (int64_t)i) = o;
-    }
-    const int nl = T * E;
-    if (given_logits) {
-        for (int i = tid; i < nl; i += 1024) s_log[i] = given_logits[i];
-    } else {
-        // every partial of this thread's (up to 16) logits is loaded before any
-        // is summed; chunks are summed in ascending order
-        for (int i0 = 0; i0 < nl; i0 += 4 * 1024) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < nkc; c0 += 8) {
-                float v[4][8];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const int i = i0 + u * 1024 + tid;
-                        v[u][c] = (i < nl && c0 + c < nkc) ? part[(int64_t)(c0 + c) * nl + i] : 0.f;
-                    }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[u] += v[u][c];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * 1024 + tid;
-                if (i < nl) s_log[i] = bias ? acc[u] + bias[i % E] : acc[u];
-            }
-        }
-    }
-    __syncthreads();
-
-    if (wid < T) {
-        const int t = wid;
-        const float* row = s_log + t * E;
-        int id;
-        float v;
-        wave_topk([&](int e) { return row[e]; }, E, k, id, v);
-        float wt = wave_softmax_selected(v, k);
-        if (lane < k) {
-            ids[t * k + lane] = id;
-            w[t * k + lane] = wt;
-            if (ids_out) ids_out[t * k + lane] = id;
-            if (w_out) w_out[t * k + lane] = wt;
-            s_ids[t * k + lane] = id;
-            atomicOr(&s_mask[id], 1u << t);
-        }
-    }
-    __syncthreads();
-    small_counting_sort(s_ids, s_mask, s_first, s_scan, T, E, k, offsets, perm, inv, tiles, ntiles);
-}
-
-// Stand-alone counting sort for T <= 16 (same code as the decode routing).
+// Stand-alone counting sort for T <= 16.
 __global__ void __launch_bounds__(1024) k_permute_small(
     const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
@@ -454,20 +362,6 @@ void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st) 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                  int32_t* ids2, float* w2, hipStream_t st) {
     k_topk<<<cdiv(T, 4), 256, 0, st>>>(logits, T, E, k, ids, w, ids2, w2);
-}
-
-void launch_router_reduce(const float* part, int nkc, int T, int E, const float* bias,
-                          float* logits, hipStream_t st) {
-    k_router_reduce<<<cdiv((int64_t)T * E, 256), 256, 0, st>>>(part, nkc, T, E, bias, logits);
-}
-
-void launch_route_small(const float* part, int nkc, const float* bias, const float* given,
-                        const uint16_t* x, int H, uint16_t* x16, int T, int E, int k,
-                        int32_t* ids, float* w, int32_t* ids_out, float* w_out,
-                        int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* tiles,
-                        int32_t* ntiles, hipStream_t st) {
-    k_route_small<<<1, 1024, 0, st>>>(part, nkc, bias, given, x, H, x16, T, E, k, ids, w,
-                                      ids_out, w_out, offsets, perm, inv, tiles, ntiles);
 }
 
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,

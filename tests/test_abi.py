@@ -102,7 +102,7 @@ def test_stage_error_paths():
     assert lib.moe_dequantize(3, P + 8, 32, P2, None) == 4
     assert lib.moe_rmsnorm_residual(P, None, P, 1e-6, 4, 256, None, None) == 1
     assert lib.moe_router_logits(P, 4, 250, 16, P, None, P2, P, 1 << 20, None) == 2
-    assert lib.moe_router_logits(P, 4, 256, 16, P, None, P2, None, 0, None) == 5
+    assert lib.moe_router_logits(None, 4, 256, 16, P, None, P2, None, 0, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
