@@ -302,16 +302,25 @@ def summarize_csv(path):
         for (k, g, c), v in sorted(agg.items()):
             print("| %s | %d | %s | %d | %.6g |" % (k, g, c, len(v), sum(v) / len(v)))
     else:
+        # every kernel of a layer forward is tagged with the batch of the layer:
+        # the token count T of the combine kernel that ends it (grid = T * H / 4)
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        tag = [None] * len(rows)
+        nxt = None
+        for i in range(len(rows) - 1, -1, -1):
+            if "k_combine" in rows[i]["Kernel_Name"]:
+                nxt = grid(rows[i]) * 4 // H
+            tag[i] = nxt
         agg = collections.defaultdict(list)
-        for r in rows:
+        for r, t in zip(rows, tag):
             if keep(r["Kernel_Name"]):
-                agg[(short(r["Kernel_Name"]), grid(r))].append(
+                agg[(short(r["Kernel_Name"]), grid(r), t)].append(
                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        print("| kernel | grid (work-items) | dispatches | mean us | min us | max us |")
-        print("|---|---|---|---|---|---|")
-        for (k, g), v in sorted(agg.items()):
-            print("| %s | %d | %d | %.2f | %.2f | %.2f |" % (k, g, len(v), sum(v) / len(v),
-                                                            min(v), max(v)))
+        print("| kernel | grid (work-items) | layer T | dispatches | mean us | min us | max us |")
+        print("|---|---|---|---|---|---|---|")
+        for (k, g, t), v in sorted(agg.items(), key=lambda kv: (kv[0][0], kv[0][1], kv[0][2] or 0)):
+            print("| %s | %d | %s | %d | %.2f | %.2f | %.2f |" % (k, g, t if t else "-", len(v),
+                                                                 sum(v) / len(v), min(v), max(v)))
     print()
 
 
