@@ -1,10 +1,12 @@
 // Bandwidth path of the layer (T <= 16 tokens): every weight byte of the
 // router, of each routed expert hit by the batch and of the shared expert is
-// streamed from HBM once, in four launches:
-//   1. router partial logits + shared-expert up|gate (both need only x),
-//   2. routing + counting sort (moe_kernels_small.hip),
-//   3. routed up|gate + SwiGLU (weight rows staged through LDS),
-//   4. down projections (routed + shared), then the weighted combine.
+// streamed from HBM once, in three launches before the combine:
+//   1. router logits + shared-expert up|gate partials (both need only x),
+//   2. routing (top-k, softmax, counting sort, redundantly in every block)
+//      followed by the routed up|gate + SwiGLU (weight rows staged through
+//      LDS) and the shared SwiGLU,
+//   3. down projections (routed + shared); the weighted combine follows
+//      (moe_kernels_small.hip).
 // The matrix cores do the arithmetic (16x16x32 steps); decoding costs one
 // table lookup per pair of weights, from tables replicated once per LDS bank
 // so that random indices never conflict.

@@ -39,6 +39,7 @@ def assert_close(y, ref, what=""):
     assert np.all(np.isfinite(y)), what + ": non-finite output"
     r = OM.rel_l2(y, ref)
     m = OM.max_abs_over_rms(y, ref)
+    print("[parity] %s: rel_l2 %.3g max_abs/rms %.3g" % (what, r, m), flush=True)
     assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, "%s: rel_l2 %.3g (tol %g), max_abs/rms %.3g (tol %g)" % (
         what, r, REL_L2_TOL, m, MAX_ABS_TOL)
     return r, m
