@@ -10,8 +10,8 @@ namespace moe {
 constexpr int kDecMaxT = 16;          // tokens handled by the bandwidth path
 constexpr int kShKChunk = 256;        // K per shared up|gate partial (bandwidth path)
 constexpr int kMaxSlots = kDecMaxT * 32;  // T * k slots of the bandwidth path
-constexpr int kGemmBM = 128;          // rows per grouped-GEMM tile
-constexpr int kGemmBN = 128;
+constexpr int kGemmBM = 64;           // rows per grouped-GEMM tile
+constexpr int kGemmBN = 256;          // weight rows per grouped-GEMM tile
 constexpr int kGemmBK = 64;
 
 // ---- small kernels (moe_kernels_small.hip)

@@ -1,14 +1,32 @@
 // Grouped-GEMM path of the layer (prefill-sized batches).  One kernel
 // template, five uses:
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
-//           (fp16), B = Q3S-256 weights dequantised into LDS, epilogue SwiGLU
+//           (fp16), B = Q3S-256 weights, epilogue SwiGLU
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
-//           weights dequantised into LDS, epilogue fp32 store (permuted rows)
+//           weights, epilogue fp32 store (permuted rows)
 //   UG_BF16 shared up|gate (bf16 x bf16), epilogue SwiGLU
 //   DN_BF16 shared down (bf16 x bf16), epilogue fp32 store
 //   ROUTER  router logits (bf16 x bf16), epilogue fp32 store + bias
-// Tile 128 x 128 x 64, 256 threads = 2 x 2 waves of 64 x 64, 32x32x16 MFMA,
-// double-buffered LDS with a 16-byte XOR swizzle, one barrier per K step.
+//
+// Tile 64 token rows x 256 weight rows, K steps of 64; four waves, wave w
+// owns 64 weight rows (SwiGLU modes: 32 up rows and the 32 gate rows of the
+// same outputs) against all 64 token rows, 32x32x16 MFMA; two blocks per CU.
+//
+// Loads go through registers (the compiler tracks them exactly):
+//   A: the tile's 64 rows x 64 k, loaded two K steps ahead and written into
+//      one of two LDS stages one step ahead (XOR-swizzled 16-byte chunks);
+//      one barrier per K step.
+//   B, quantized: the packed bytes of the wave's 64 weight rows for one
+//      period (a Q3 block = 4 K steps, or four NL4 blocks = 2 K steps) are
+//      loaded coalesced, a period ahead, into a per-wave LDS area; each lane
+//      reads back the bytes of its own MFMA fragment (one 32-weight
+//      sub-block or block of one row per 32-column half) and decodes them
+//      with a replicated LDS table chunk by chunk between the MFMAs.
+//   B, bf16: each lane loads its fragments (32 values of one row per half)
+//      two steps ahead.
+// The MFMA's reduction order within a K step is permuted (lane half h takes
+// k = 32h .. 32h + 31) so that a lane's fragment is one contiguous sub-block;
+// A is read from LDS in the same order.
 //
 // Numerics: Q3S weights enter the matrix cores as s*c (an fp16 integer,
 // |s*c| <= 1016, exact) and d/128 is applied in fp32 to the partial sum of
@@ -22,11 +40,17 @@
 namespace moe {
 
 typedef _Float16 h2g __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int N> struct Cnt { static constexpr int value = N; };
 
 enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_BF16 = 2, DN_BF16 = 3, ROUTER = 4 };
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int kRowChunks = BK / 8;       // 16-byte chunks per LDS row
+constexpr int kStages = 2;               // A stages in LDS
+constexpr int kAL = BM * 8 / 256;        // A 16-byte loads per lane per K step
+constexpr int kSMX = BM / 32;            // 32-row groups per tile
+constexpr int kLutDw = 2048;             // decode table dwords (8 KB)
 
 struct GemmArgs {
     const uint8_t* experts;
@@ -50,27 +74,52 @@ struct GemmArgs {
     int ldo;                 // output row length
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowChunks + (chunk ^ (row & 7)); }
+// A tile in LDS: row r, 16-byte chunk c at slot r*8 + (c ^ ((r/2) % 8)), so
+// that 16 consecutive rows read at one chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int aslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// LDS address of the Q3 pair-table entry for the 6-bit field at bit P of a
+// 96-bit index word: the field lands at address bits 7..12, ORed into cb.
+template <int P> __device__ __forceinline__ uint32_t q3_lut_addr(const uint32_t (&q)[3], uint32_t cb) {
+    constexpr int w = P >> 5, b = P & 31;
+    uint32_t x;
+    if constexpr (b + 6 > 32) x = __builtin_amdgcn_alignbit(q[w + 1], q[w], b - 7);
+    else if constexpr (b >= 7) x = q[w] >> (b - 7);
+    else x = q[w] << (7 - b);
+    return (x & 0x1F80u) | cb;
+}
+// Table addresses of the four pairs of chunk KK (weights 8 KK .. 8 KK + 7).
+template <int KK>
+__device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t cb, uint32_t (&aa)[4]) {
+    aa[0] = q3_lut_addr<24 * KK + 0>(q, cb);
+    aa[1] = q3_lut_addr<24 * KK + 6>(q, cb);
+    aa[2] = q3_lut_addr<24 * KK + 12>(q, cb);
+    aa[3] = q3_lut_addr<24 * KK + 18>(q, cb);
+}
 
 template <int MODE>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
-    __shared__ u32x4 As[2][BM * kRowChunks];
-    __shared__ u32x4 Bs[2][BN * kRowChunks];
-    __shared__ uint32_t lut[256];
-    __shared__ float ds_d[2][BN];
-
     constexpr bool kQ3 = MODE == UG_Q3;
     constexpr bool kNL = MODE == DN_NL4;
     constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_BF16;
     constexpr bool kRouted = MODE == UG_Q3 || MODE == DN_NL4;
-    constexpr bool kF16 = MODE == UG_Q3 || MODE == DN_NL4;
 
-    const int tid = threadIdx.x, lane = __lane_id(), w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    __shared__ u32x4 As[kStages][BM * 8];
+    // Decode tables, replicated so that random indices spread over the banks:
+    // Q3 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
+    // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8).
+    __shared__ __attribute__((aligned(8192))) uint32_t lut[kRouted ? kLutDw : 1];
+    constexpr int kPer = kQ3 ? 4 : 2;               // quantized B: K steps per period
+    constexpr int kRowB = kQ3 ? 104 : 72;           // bytes of a weight row per period
+    constexpr int kUPR = kRowB / 8;                 // 8-byte units per row = per lane
+    __shared__ __attribute__((aligned(16))) uint8_t Bq[4][kRouted ? 64 * kRowB : 8];
+
+    const int tid = threadIdx.x, lane = __lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int l32 = lane & 31, hh = lane >> 5;
 
     // ---- tile coordinates (XCD-aware: the N tiles of one M tile share an XCD)
-    const int NT = (g.N + BN - 1) / BN;
+    const int NT = kSwi ? (g.half_n + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     const int bid = blockIdx.x, xcd = bid & 7, li = bid >> 3;
     const int mt = (li / NT) * 8 + xcd, nt = li % NT;
     int row0, rows, e = 0;
@@ -85,229 +134,354 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         rows = min(BM, g.T - row0);
     }
 
-    // ---- per-thread A rows (4 chunks: rows (tid>>3) + 32 i, chunk tid & 7)
-    const int ach = tid & 7;
-    const uint16_t* arow[4];
+    // ---- A: lane's load i (0..kAL-1) is row (kAL w + i) * 8 + lane / 8,
+    // physical chunk lane % 8 of the stage.  Rows past the tile's end read its
+    // last row again (their outputs are never stored).
+    const uint16_t* asrc[kAL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        if (r < rows) {
-            int64_t src;
-            if (MODE == UG_Q3) src = (int64_t)(g.perm[row0 + r] / g.k);
-            else src = row0 + r;
-            arow[i] = g.A + src * g.lda + ach * 8;
-        } else {
-            arow[i] = nullptr;
-        }
+    for (int i = 0; i < kAL; ++i) {
+        const int r = (kAL * w + i) * 8 + (lane >> 3);
+        const int rc = min(r, rows - 1);
+        int64_t src;
+        if (MODE == UG_Q3) src = (int64_t)(g.perm[row0 + rc] / g.k);
+        else src = row0 + rc;
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        asrc[i] = g.A + src * g.lda + c * 8;
     }
 
-    // ---- B rows
-    // SwiGLU modes: tile row rr -> output o = nt*64 + (rr>>6)*32 + (rr&31);
-    // weight row o (up, (rr>>5)&1 == 0) or half_n + o (gate).
-    auto wrow_of = [&](int rr) -> int {
+    // ---- B: weight row of this lane for column half sn (0, 1)
+    int brow[2];
+    bool ocol[2];                                   // column holds an output
+#pragma unroll
+    for (int sn = 0; sn < 2; ++sn) {
         if (kSwi) {
-            const int o = nt * 64 + (rr >> 6) * 32 + (rr & 31);
-            return ((rr >> 5) & 1) ? g.half_n + o : o;
-        }
-        return nt * BN + rr;
-    };
-    // bf16 modes: 4 chunks per thread like A
-    const uint16_t* brow[4];
-    // quantized modes: one sub-block (Q3) / block (NL4) per thread: row tid>>1, part tid&1
-    const uint8_t* qrow = nullptr;
-    const int qrr = tid >> 1, qsub = tid & 1;
-    if (kF16) {
-        const uint8_t* W = g.experts + (int64_t)e * g.estride;
-        if (kQ3) {
-            const int64_t rb = (int64_t)(g.H / kQ3Weights) * kQ3Bytes;
-            qrow = W + (int64_t)wrow_of(qrr) * rb;
+            const int o = nt * (BN / 2) + 32 * w + l32;
+            ocol[sn] = o < g.half_n;
+            const int oc = min(o, g.half_n - 1);
+            brow[sn] = sn ? g.half_n + oc : oc;
         } else {
-            const int64_t rb = (int64_t)(g.I / 32) * kNL4Bytes;
-            const int64_t ug = (int64_t)2 * g.I * (g.H / kQ3Weights) * kQ3Bytes;
-            qrow = W + ug + (int64_t)wrow_of(qrr) * rb;
-        }
-        // LUT: Q3 pair -> (C3[lo], C3[hi]); NL4 byte -> (T4[lo]/128, T4[hi]/128)
-        if (kQ3) {
-            if (tid < 64)
-                lut[tid] = pack2(f32_to_f16_bits((float)kC3[tid & 7]), f32_to_f16_bits((float)kC3[tid >> 3]));
-        } else {
-            lut[tid] = pack2(f32_to_f16_bits((float)kT4[tid & 15] * 0.0078125f),
-                             f32_to_f16_bits((float)kT4[tid >> 4] * 0.0078125f));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = (tid >> 3) + 32 * i;
-            const int wr = wrow_of(rr);
-            brow[i] = (kSwi || wr < g.N) ? g.Bw + (int64_t)wr * g.K + ach * 8 : nullptr;
+            const int n = nt * BN + 64 * w + 32 * sn + l32;
+            ocol[sn] = n < g.N;
+            brow[sn] = min(n, g.N - 1);
         }
     }
-
-    // ---- staging registers
-    u32x4 ra[4], rb4[4];
-    uint32_t qi[5];
-    uint64_t qt = 0;
-
-    auto load_a = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = arow[i] ? ld16(arow[i] + kt * BK) : zero;
+    // ---- A loads into registers (the compiler tracks them exactly)
+    struct RawA {
+        u32x4 v[kAL];
     };
-    auto load_b = [&](int kt) {
-        if (kQ3) {
-            const int j = 2 * kt + qsub;                 // sub-block index along the row
-            const int b = j >> 3, js = j & 7;
-            const uint8_t* p = qrow + b * kQ3Bytes;
-            qi[0] = ld4(p + 12 * js);
-            qi[1] = ld4(p + 12 * js + 4);
-            qi[2] = ld4(p + 12 * js + 8);
-            qt = *reinterpret_cast<const uint64_t*>(p + 96);
-        } else if (kNL) {
-            const int j = 2 * kt + qsub;                 // NL4 block index along the row
-            const uint8_t* p = qrow + 18 * j - ((j & 1) ? 2 : 0);
+    auto load_a = [&](int kt, RawA& R) {
 #pragma unroll
-            for (int u = 0; u < 5; ++u) qi[u] = ld4(p + 4 * u);
+        for (int i = 0; i < kAL; ++i) R.v[i] = *reinterpret_cast<const u32x4*>(asrc[i] + kt * BK);
+    };
+    // A(kt) from registers into stage st: load i of wave w fills slots
+    // (kAL w + i) * 64 + lane.
+    auto put_a = [&](int st, const RawA& R) {
+#pragma unroll
+        for (int i = 0; i < kAL; ++i) As[st][(kAL * w + i) * 64 + lane] = R.v[i];
+    };
+
+    // ---- quantized B: the packed bytes of one period (Q3: one 256-weight
+    // block = 4 K steps, 104 B per row; NL4: four 32-weight blocks = 2 K
+    // steps, 72 B per row) of the wave's 64 weight rows (row r = 32 sn + l,
+    // l = lane % 32 of the fragments) are loaded with 8-byte loads in
+    // row-major unit order (unit u = lane + 64 i = r * UPR + part), one period
+    // ahead, into registers, then written to the wave's LDS area in the same
+    // order; each lane reads its fragment's bytes back per K step.  Reads past
+    // a row's last block (NL4, odd step count) stay inside the expert record
+    // or return zeros (buffer loads) and are never used.
+    __amdgpu_buffer_rsrc_t wsrc;
+    int ug_rb = 0, dn_rb = 0, ug = 0;
+    if constexpr (kRouted) {
+        const uint8_t* W = g.experts + (int64_t)e * g.estride;
+        wsrc = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)g.estride, 0x00020000);
+        ug_rb = (g.H / kQ3Weights) * kQ3Bytes;
+        dn_rb = (g.I / kNL4Weights) * kNL4Bytes;
+        ug = 2 * g.I * ug_rb;
+    }
+    // byte offset in the record of unit i of this lane, period 0
+    auto unit_off = [&](int i) {
+        const int u = lane + 64 * i, r = u / kUPR, part = u - r * kUPR;
+        int wr;
+        if (kSwi) {
+            const int oc = min(nt * (BN / 2) + 32 * w + (r & 31), g.half_n - 1);
+            wr = (r >> 5) ? g.half_n + oc : oc;
         } else {
+            wr = min(nt * BN + 64 * w + r, g.N - 1);
+        }
+        return (kQ3 ? wr * ug_rb : ug + wr * dn_rb) + 8 * part;
+    };
+    struct RawP {
+        u32x2 u[kUPR];
+    };
+    auto load_period = [&](int p, RawP& R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rb4[i] = brow[i] ? ld16_stream(brow[i] + kt * BK) : zero;
+        for (int i = 0; i < kUPR; ++i)
+            R.u[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, unit_off(i) + p * kRowB, 0, 0));
+    };
+    auto put_period = [&](const RawP& R) {
+#pragma unroll
+        for (int i = 0; i < kUPR; ++i) *reinterpret_cast<u32x2*>(&Bq[w][8 * (lane + 64 * i)]) = R.u[i];
+    };
+    // The lane's raw bytes of step kt from the period area: Q3 q[sn][0..2] =
+    // the 12 index bytes of sub-block 2 (kt % 4) + h, q[sn][3..4] = the tail;
+    // NL4 q[sn][0..4] = the 20 dword-aligned bytes holding block 2 (kt % 2) + h.
+    auto read_raw = [&](int kt, uint32_t (&q)[2][5]) {
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+            const uint8_t* rb = &Bq[w][(32 * sn + l32) * kRowB];
+            if constexpr (kQ3) {
+                const uint32_t* ip = reinterpret_cast<const uint32_t*>(rb + 12 * (2 * (kt & 3) + hh));
+                q[sn][0] = ip[0];
+                q[sn][1] = ip[1];
+                q[sn][2] = ip[2];
+                const u32x2 t = *reinterpret_cast<const u32x2*>(rb + 96);
+                q[sn][3] = t[0];
+                q[sn][4] = t[1];
+            } else {
+                const uint32_t* ip = reinterpret_cast<const uint32_t*>(rb + kNL4Bytes * (2 * (kt & 1) + hh) - 2 * hh);
+#pragma unroll
+                for (int u = 0; u < 5; ++u) q[sn][u] = ip[u];
+            }
         }
     };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) As[buf][swz((tid >> 3) + 32 * i, ach)] = ra[i];
+
+    // ---- bf16 B: each lane loads its own fragments (32 values of one row
+    // per half: full 128-byte row segments per wave load) two steps ahead.
+    struct RawBF {
+        u32x4 v[2][4];
     };
-    auto store_b = [&](int buf, int kt) {
-        if (kQ3) {
-            const int js = (2 * kt + qsub) & 7;
-            const _Float16 s = (_Float16)(float)q3_tail_s(qt, js);
-            const h2g s2 = {s, s};
+    const uint8_t* bfrow[2];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                u32x4 v;
+    for (int sn = 0; sn < 2; ++sn) bfrow[sn] = reinterpret_cast<const uint8_t*>(g.Bw + (int64_t)brow[sn] * g.K);
+    auto load_bf = [&](int kt, RawBF& R) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int P = 24 * c + 6 * p;
-                    uint32_t pr;
-                    if ((P & 31) <= 26) pr = (qi[P >> 5] >> (P & 31)) & 63u;
-                    else pr = __builtin_amdgcn_alignbit(qi[(P >> 5) + 1], qi[P >> 5], P & 31) & 63u;
-                    v[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lut[pr]) * s2);
-                }
-                Bs[buf][swz(qrr, qsub * 4 + c)] = v;
-            }
-            if (qsub == 0) ds_d[buf][qrr] = q3_tail_d(qt) * 0.0078125f;
-        } else if (kNL) {
-            const int j = 2 * kt + qsub;
-            uint32_t dbits, nb[4];
-            if (j & 1) {
-                dbits = qi[0] >> 16;
+        for (int sn = 0; sn < 2; ++sn) {
+            const u32x4* vp = reinterpret_cast<const u32x4*>(bfrow[sn] + (kt * BK + 32 * hh) * 2);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) nb[u] = qi[u + 1];
-            } else {
-                dbits = qi[0] & 0xffffu;
+            for (int kk = 0; kk < 4; ++kk) R.v[sn][kk] = vp[kk];
+        }
+    };
+
+    // LDS byte address of a table entry = cb | entry << 7 (Q3) or << 5 (NL4).
+    const uint32_t cb = lds_addr(lut) | (kQ3 ? (uint32_t)l32 * 4u : (uint32_t)(lane & 7) * 4u);
+
+    // Fragments of one K step: f[sn][kk] = weights k = 32h + 8kk .. +7 of
+    // column half sn; Q3: dl[sn] = d / 128 of the lane's column in this block.
+    struct Frag {
+        u32x4 f[2][4];
+        float dl[2];
+    };
+    // Chunk kk of both halves from the step's raw bytes.
+    auto decode_kk = [&](int kt, const uint32_t (&R)[2][5], Frag& F, auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) nb[u] = __builtin_amdgcn_alignbit(qi[u + 1], qi[u], 16);
-            }
-            const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
-            const h2g d2 = {d, d};
+        for (int sn = 0; sn < 2; ++sn) {
+            if constexpr (kQ3) {
+                const uint64_t tail = ((uint64_t)R[sn][4] << 32) | R[sn][3];
+                const _Float16 s = (_Float16)(float)q3_tail_s(tail, 2 * (kt & 3) + hh);
+                const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(R[sn][3] & 0xffffu));
+                const h2g s2 = {s, s};
+                if (kk == 0) F.dl[sn] = (float)d * 0.0078125f;
+                const uint32_t q[3] = {R[sn][0], R[sn][1], R[sn][2]};
+                uint32_t aa[4];
+                q3_chunk_addrs<kk>(q, cb, aa);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                u32x4 v;
+                for (int p = 0; p < 4; ++p)               // c * s, an exact fp16 integer
+                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * s2);
+            } else if constexpr (kNL) {
+                // h = 0: d in bytes 0-1, indices in bytes 2..17;
+                // h = 1: d in bytes 2-3, indices in bytes 4..19.
+                const uint32_t dbits = __builtin_amdgcn_perm(0u, R[sn][0], hh ? 0x0c0c0302u : 0x0c0c0100u);
+                const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+                const h2g d2 = {d, d};
+                const uint32_t nb = __builtin_amdgcn_perm(R[sn][kk + 1], R[sn][kk], hh ? 0x07060504u : 0x05040302u);
+                const uint32_t aa[4] = {((nb << 5) & 0x1FE0u) | cb, ((nb >> 3) & 0x1FE0u) | cb,
+                                        ((nb >> 11) & 0x1FE0u) | cb, ((nb >> 19) & 0x1FE0u) | cb};
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    v[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lut[(nb[c] >> (8 * p)) & 255u]) * d2);
-                Bs[buf][swz(qrr, qsub * 4 + c)] = v;
+                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * d2);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Bs[buf][swz((tid >> 3) + 32 * i, ach)] = rb4[i];
         }
     };
 
-    f32x16 acc[2][2], tmp[2][2];
+    // acc: the output sums; Q3: tmp holds the current 256-weight block's sums
+    // of x * s * c, added to acc times d / 128 at the block's end.
+    f32x16 acc[kSMX][2], tmp[kQ3 ? kSMX : 1][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kSMX; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[a][b][r] = 0.f;
-                tmp[a][b][r] = 0.f;
-            }
-
-    const int nk = g.K / BK;
-    if (kF16) __syncthreads();                 // LUT ready
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    store_b(0, 0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            load_a(kt + 1);
-            load_b(kt + 1);
-        }
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    if constexpr (kQ3) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            u32x4 fa[2], fb[2];
-            const int ch = 2 * kk + (lane >> 5);
+        for (int a = 0; a < kSMX; ++a)
 #pragma unroll
-            for (int sm = 0; sm < 2; ++sm) fa[sm] = As[cur][swz(wm * 64 + sm * 32 + (lane & 31), ch)];
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int sn = 0; sn < 2; ++sn) fb[sn] = Bs[cur][swz(wn * 64 + sn * 32 + (lane & 31), ch)];
-#pragma unroll
-            for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-                for (int sn = 0; sn < 2; ++sn) {
-                    if (kQ3) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn], tmp[sm][sn]);
-                    else if (kF16) acc[sm][sn] = mfma32_f16(fa[sm], fb[sn], acc[sm][sn]);
-                    else acc[sm][sn] = mfma32_bf16(fa[sm], fb[sn], acc[sm][sn]);
-                }
-        }
-        if (kQ3 && (kt & 3) == 3) {             // end of a 256-weight block: apply d/128
-#pragma unroll
-            for (int sn = 0; sn < 2; ++sn) {
-                const float dcol = ds_d[cur][wn * 64 + sn * 32 + (lane & 31)];
-#pragma unroll
-                for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        acc[sm][sn][r] += tmp[sm][sn][r] * dcol;
-                        tmp[sm][sn][r] = 0.f;
-                    }
-            }
-        }
-        if (kt + 1 < nk) {
-            store_a(cur ^ 1);
-            store_b(cur ^ 1, kt + 1);
-        }
-        __syncthreads();
+                for (int r = 0; r < 16; ++r) tmp[a][b][r] = 0.f;
     }
 
-    // ---- epilogue.  Lane l, register r of sub-tile (sm, sn): row
-    // wm*64 + sm*32 + 8(r/4) + 4(l/32) + r%4, column (l & 31) of the sub-tile.
-    const int lc = lane & 31, lh = lane >> 5;
+    // MFMAs of chunk kk of a K step (A from stage st) over the first SM
+    // 32-row groups of the tile.
+    auto mma_kk = [&](int st, int kk, const u32x4 (&fb)[2][4], auto smc) {
+        constexpr int SM = decltype(smc)::value;
+        u32x4 fa[SM];
 #pragma unroll
-    for (int sm = 0; sm < 2; ++sm) {
+        for (int sm = 0; sm < SM; ++sm) fa[sm] = As[st][aslot(32 * sm + l32, 4 * hh + kk)];
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+            for (int sn = 0; sn < 2; ++sn) {
+                if constexpr (kQ3) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], tmp[sm][sn]);
+                else if constexpr (kRouted) acc[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], acc[sm][sn]);
+                else acc[sm][sn] = mfma32_bf16(fa[sm], fb[sn][kk], acc[sm][sn]);
+            }
+    };
+    // Q3, end of a 256-weight block: acc += tmp * d / 128, tmp = 0.
+    auto apply_d = [&](const Frag& F, auto smc) {
+        constexpr int SM = decltype(smc)::value;
+        if constexpr (kQ3) {
+#pragma unroll
+            for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        acc[sm][sn][r] += tmp[sm][sn][r] * F.dl[sn];
+                        tmp[sm][sn][r] = 0.f;
+                    }
+        }
+    };
+
+    // ---- pipeline (two LDS stages for A, A registers alternating by step
+    // parity).  Step kt: A(kt + 1) registers -> stage (kt + 1) % 2 (read last
+    // in step kt - 1, before the barrier that ended it); load A(kt + 3) into
+    // the freed registers; then, quantized: if step kt opens a period, its
+    // bytes (loaded a period ago) go to the wave's area and the next period is
+    // loaded; the lane's raw bytes of step kt are read, and per chunk kk the
+    // fragments are decoded and the MFMAs issued.  bf16: the MFMAs read the B
+    // registers of step kt directly, then B(kt + 2) is loaded into them.
+    // Barrier.  Past the last step, loads repeat the last step or read unused
+    // bytes.
+    const int nk = g.K / BK;
+    if constexpr (kRouted) {
+        for (int i = tid; i < kLutDw; i += 256) {
+            uint32_t v;
+            if (kQ3) {
+                const int en = i >> 5;
+                v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
+            } else {
+                const int en = i >> 3;
+                v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.0078125f),
+                          f32_to_f16_bits((float)kT4[en >> 4] * 0.0078125f));
+            }
+            lut[i] = v;
+        }
+    }
+    RawA A0, A1;
+    load_a(0, A0);
+    load_a(min(1, nk - 1), A1);
+    put_a(0, A0);
+    load_a(min(2, nk - 1), A0);
+
+    auto run = [&](auto smc) {
+        if constexpr (kRouted) {
+            RawP P;
+            load_period(0, P);
+            __syncthreads();                         // stage 0 and the table written
+            // Ra: A(kt + 1) (refilled with kt + 3); opens: step kt starts a period
+            auto step = [&](int kt, RawA& Ra, bool opens, Frag& F) {
+                const int st = kt & 1;
+                put_a(st ^ 1, Ra);
+                load_a(min(kt + 3, nk - 1), Ra);
+                if (opens) {
+                    put_period(P);
+                    load_period(kt / kPer + 1, P);
+                }
+                uint32_t q[2][5];
+                read_raw(kt, q);
+                decode_kk(kt, q, F, Cnt<0>{});
+                mma_kk(st, 0, F.f, smc);
+                decode_kk(kt, q, F, Cnt<1>{});
+                mma_kk(st, 1, F.f, smc);
+                decode_kk(kt, q, F, Cnt<2>{});
+                mma_kk(st, 2, F.f, smc);
+                decode_kk(kt, q, F, Cnt<3>{});
+                mma_kk(st, 3, F.f, smc);
+                __syncthreads();
+            };
+            Frag F;
+            if constexpr (kQ3) {
+                // K = H is a multiple of 256: a period per four steps, d applied
+                // after the fourth
+                for (int kt = 0; kt < nk; kt += 4) {
+                    step(kt, A1, true, F);
+                    step(kt + 1, A0, false, F);
+                    step(kt + 2, A1, false, F);
+                    step(kt + 3, A0, false, F);
+                    apply_d(F, smc);
+                }
+            } else {
+                int kt = 0;
+                for (; kt + 2 <= nk; kt += 2) {
+                    step(kt, A1, true, F);
+                    step(kt + 1, A0, false, F);
+                }
+                if (kt < nk) step(kt, A1, true, F);
+            }
+        } else {
+            RawBF B0, B1;
+            load_bf(0, B0);
+            load_bf(min(1, nk - 1), B1);
+            __syncthreads();                         // stage 0 written
+            // Ra: A(kt + 1); Rc: B(kt)
+            auto step = [&](int kt, RawA& Ra, RawBF& Rc) {
+                const int st = kt & 1;
+                put_a(st ^ 1, Ra);
+                load_a(min(kt + 3, nk - 1), Ra);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) mma_kk(st, kk, Rc.v, smc);
+                load_bf(min(kt + 2, nk - 1), Rc);
+                __syncthreads();
+            };
+            int kt = 0;
+            for (; kt + 2 <= nk; kt += 2) {
+                step(kt, A1, B0);
+                step(kt + 1, A0, B1);
+            }
+            if (kt < nk) step(kt, A1, B0);
+        }
+    };
+    // The loop is instantiated per count of live 32-row groups (ragged
+    // expert tails skip the MFMAs of groups past their rows).
+    const int nsm = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
+    if (nsm == 2) run(Cnt<2>{});
+    else run(Cnt<1>{});
+
+    // ---- epilogue.  Lane l, register r of group (sm, sn): row
+    // 32 sm + 8 (r / 4) + 4 (l / 32) + r % 4, the lane's column of half sn.
+#pragma unroll
+    for (int sm = 0; sm < kSMX; ++sm) {
+        if (sm >= nsm) break;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int m = wm * 64 + sm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int m = 32 * sm + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (m >= rows) continue;
-            if (kSwi) {
-                const int o = nt * 64 + wn * 32 + lc;
+            if constexpr (kSwi) {
+                if (!ocol[0]) continue;
+                const int o = brow[0];
                 const float u = acc[sm][0][r], gv = acc[sm][1][r];
                 const uint32_t bf = f32_to_bf16(gv / (1.0f + expf(-gv)) * u);
-                const uint16_t v = kF16 ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
+                const uint16_t v = kRouted ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
                 g.out16[(int64_t)(row0 + m) * g.ldo + o] = v;
             } else {
 #pragma unroll
                 for (int sn = 0; sn < 2; ++sn) {
-                    const int n = nt * BN + wn * 64 + sn * 32 + lc;
-                    if (n < g.N) {
-                        float v = acc[sm][sn][r];
-                        if (MODE == ROUTER && g.bias) v += g.bias[n];
-                        g.out32[(int64_t)(row0 + m) * g.ldo + n] = v;
-                    }
+                    if (!ocol[sn]) continue;
+                    float v = acc[sm][sn][r];
+                    if (MODE == ROUTER && g.bias) v += g.bias[brow[sn]];
+                    g.out32[(int64_t)(row0 + m) * g.ldo + brow[sn]] = v;
                 }
             }
         }
@@ -316,11 +490,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------- launchers
 
-static unsigned gemm_grid(int n_cols, int m_tiles) {
-    const int NT = (n_cols + BN - 1) / BN;
+static unsigned gemm_grid(int n_tiles, int m_tiles) {
     const int MTp = ((m_tiles + 7) / 8) * 8;
-    return (unsigned)(NT * MTp);
+    return (unsigned)(n_tiles * MTp);
 }
+static int swi_tiles(int half_n) { return (half_n + BN / 2 - 1) / (BN / 2); }
+static int col_tiles(int n) { return (n + BN - 1) / BN; }
 
 void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
                         const float* bias, float* logits, hipStream_t st) {
@@ -328,7 +503,7 @@ void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* 
     a.A = x; a.lda = H; a.T = T; a.Bw = w_r; a.N = E; a.K = H; a.bias = bias;
     a.out32 = logits; a.ldo = E;
     const int mtiles = (T + BM - 1) / BM;
-    k_gemm<ROUTER><<<gemm_grid(E, mtiles), 256, 0, st>>>(a);
+    k_gemm<ROUTER><<<gemm_grid(col_tiles(E), mtiles), 256, 0, st>>>(a);
 }
 
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
@@ -338,7 +513,7 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.perm = perm; a.k = k; a.A = x16; a.lda = H;
     a.N = 2 * I; a.K = H; a.half_n = I; a.H = H; a.I = I; a.out16 = a16_perm; a.ldo = I;
-    k_gemm<UG_Q3><<<gemm_grid(2 * I, max_tiles), 256, 0, st>>>(a);
+    k_gemm<UG_Q3><<<gemm_grid(swi_tiles(I), max_tiles), 256, 0, st>>>(a);
 }
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
@@ -348,7 +523,7 @@ void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* ti
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
     a.out32 = y_perm; a.ldo = H;
-    k_gemm<DN_NL4><<<gemm_grid(H, max_tiles), 256, 0, st>>>(a);
+    k_gemm<DN_NL4><<<gemm_grid(col_tiles(H), max_tiles), 256, 0, st>>>(a);
 }
 
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
@@ -358,10 +533,10 @@ void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
     GemmArgs a{};
     a.A = x; a.lda = H; a.T = T; a.Bw = sh_ug; a.N = 2 * Is; a.K = H; a.half_n = Is;
     a.out16 = a_sh; a.ldo = Is;
-    k_gemm<UG_BF16><<<gemm_grid(2 * Is, mtiles), 256, 0, st>>>(a);
+    k_gemm<UG_BF16><<<gemm_grid(swi_tiles(Is), mtiles), 256, 0, st>>>(a);
     GemmArgs b{};
     b.A = a_sh; b.lda = Is; b.T = T; b.Bw = sh_down; b.N = H; b.K = Is; b.out32 = y_sh; b.ldo = H;
-    k_gemm<DN_BF16><<<gemm_grid(H, mtiles), 256, 0, st>>>(b);
+    k_gemm<DN_BF16><<<gemm_grid(col_tiles(H), mtiles), 256, 0, st>>>(b);
 }
 
 }  // namespace moe
