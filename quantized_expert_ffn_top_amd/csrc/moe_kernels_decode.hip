@@ -30,23 +30,26 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 }
 
 // ---------------------------------------------------------------- stage 1
-// Blocks of 16 waves.  Blocks [0, n_rb): router logits of 16 experts: the
-// waves split K in 16 equal parts (16x16x32 bf16 steps, A = tokens, rows >= T
-// zero), their partial sums are added in wave order through LDS and the bias
-// is added last: logits[t][e].  Blocks [n_rb, ...): wave-sized items, no
-// block synchronisation.  Items [0, n_s): shared expert up|gate partials of 16
-// rows (rows 0..Is-1 up, Is..2Is-1 gate) over one 256-wide K chunk,
-// shp[kc][t][2 Is]; summed and passed through SwiGLU by the up|gate kernel.
-// The last H/256 wave items write the fp16 copy of the tokens, one 256-wide
-// K chunk each.
-__global__ void __launch_bounds__(1024) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
+// Blocks of 4 waves, spread over the whole chip.  Blocks [0, n_rb): router
+// logits of 16 experts: the waves split K in 4 equal parts (16x16x32 bf16
+// steps, A = tokens, rows >= T zero; a wave's loads, up to 24 steps, are all
+// in flight at once), their partial sums are added in wave order through
+// LDS and the bias is added last: logits[t][e].  Blocks [n_rb, ...): wave
+// items, no block synchronisation.  Items [0, n_s): shared expert up|gate
+// partials of 16 rows (rows 0..Is-1 up, Is..2Is-1 gate) over one 256-wide K
+// chunk, shp[kc][t][2 Is]; summed and passed through SwiGLU by the up|gate
+// kernel.  The last H/256 wave items write the fp16 copy of the tokens, one
+// 256-wide K chunk each.
+constexpr int kS1Waves = 4;
+constexpr int kS1Batch = 24;                    // K steps in flight per wave
+__global__ void __launch_bounds__(64 * kS1Waves) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
                                                     int E, const uint16_t* __restrict__ w_r,
                                                     const float* __restrict__ bias,
                                                     float* __restrict__ logits, int n_rb,
                                                     const uint16_t* __restrict__ sh_ug, int Is,
                                                     float* __restrict__ shp, int n_s,
                                                     uint16_t* __restrict__ x16) {
-    __shared__ f32x4 red[16][64];
+    __shared__ f32x4 red[kS1Waves][64];
     const int lane = __lane_id(), w = (int)(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -54,27 +57,27 @@ __global__ void __launch_bounds__(1024) k_dec_stage1(const uint16_t* __restrict_
     if ((int)blockIdx.x < n_rb) {
         const int row = blockIdx.x * 16 + r;
         const bool vr = row < E;
-        const int S = H / 32, sa = w * S / 16, sb = (w + 1) * S / 16;   // this wave's K steps
+        const int S = H / 32, sa = w * S / kS1Waves, sb = (w + 1) * S / kS1Waves;   // this wave's K steps
         const uint16_t* brow = w_r + (int64_t)(vr ? row : 0) * H + 8 * g;
         const uint16_t* arow = x + (int64_t)(vt ? r : 0) * H + 8 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = sa; s0 < sb; s0 += 8) {                // up to 8 steps' loads in flight
-            u32x4 a[8], b[8];
+        for (int s0 = sa; s0 < sb; s0 += kS1Batch) {
+            u32x4 a[kS1Batch], b[kS1Batch];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
+            for (int s = 0; s < kS1Batch; ++s) {
                 const bool ok = s0 + s < sb;
                 a[s] = (vt && ok) ? ld16(arow + 32 * (s0 + s)) : zero;
                 b[s] = (vr && ok) ? ld16_stream(brow + 32 * (s0 + s)) : zero;
             }
 #pragma unroll
-            for (int s = 0; s < 8; ++s) acc = mfma16_bf16(a[s], b[s], acc);
+            for (int s = 0; s < kS1Batch; ++s) acc = mfma16_bf16(a[s], b[s], acc);
         }
         red[w][lane] = acc;
         __syncthreads();
         if (w == 0) {
             f32x4 sum = red[0][lane];
 #pragma unroll
-            for (int v = 1; v < 16; ++v)
+            for (int v = 1; v < kS1Waves; ++v)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sum[i] += red[v][lane][i];
             const float bb = (vr && bias) ? bias[row] : 0.f;
@@ -86,7 +89,7 @@ __global__ void __launch_bounds__(1024) k_dec_stage1(const uint16_t* __restrict_
         }
         return;
     }
-    const int wi = (blockIdx.x - n_rb) * 16 + w;
+    const int wi = (blockIdx.x - n_rb) * kS1Waves + w;
     const int n_x = H / kShKChunk;               // waves [n_s, n_s + n_x): fp16 copy of x
     if (wi >= n_s) {
         if (wi >= n_s + n_x) return;
@@ -803,10 +806,10 @@ void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w
     const int n_rb = w_r ? (E + 15) / 16 : 0;
     const int n_s = (sh_ug && Is > 0) ? (2 * Is / 16) * nkc : 0;
     const int n_x = x16 ? nkc : 0;
-    const int n_wb = (n_s + n_x + 15) / 16;
+    const int n_wb = (n_s + n_x + kS1Waves - 1) / kS1Waves;
     if (n_rb + n_wb == 0) return;
-    k_dec_stage1<<<n_rb + n_wb, 1024, 0, st>>>(x, T, H, E, w_r, bias, logits, n_rb, sh_ug, Is, shp,
-                                              n_s, x16);
+    k_dec_stage1<<<n_rb + n_wb, 64 * kS1Waves, 0, st>>>(x, T, H, E, w_r, bias, logits, n_rb, sh_ug, Is,
+                                                        shp, n_s, x16);
 }
 
 template <int GPW, bool FULL, int WAVES>
