@@ -283,7 +283,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
     if (do_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, shared_y, st);
     launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16, st);
-    launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, y_perm, st);
+    launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, y_perm, nullptr, st);
     return launched("moe_expert_ffn");
 }
 
@@ -398,8 +398,15 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         }
         launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
         mk->mark();
-        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, yp, st);
+        // the unweighted rows go through memory as fp16 (one rounding,
+        // relative error <= 2^-11) on this path: half the bytes written and read
+        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, nullptr,
+                         reinterpret_cast<uint16_t*>(yp), st);
         mk->mark();
+        launch_combine16(reinterpret_cast<const uint16_t*>(yp), inv, wv, T, k, H,
+                         has_sh ? ysh : nullptr, y, st);
+        mk->mark();
+        return launched("moe_layer_forward");
     }
     launch_combine(yp, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
     mk->mark();

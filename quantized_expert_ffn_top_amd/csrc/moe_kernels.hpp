@@ -28,6 +28,8 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
                         hipStream_t st);
 void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
                     const float* shared, float* y, hipStream_t st);
+void launch_combine16(const uint16_t* y_perm16, const int32_t* inv, const float* w, int T, int k,
+                      int H, const float* shared, float* y, hipStream_t st);
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st);
 
@@ -65,9 +67,11 @@ void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* 
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                         const uint16_t* x16, int H, int I, uint16_t* a16_perm, hipStream_t st);
+// y_perm16 non-null: the unweighted rows are stored as fp16 there (the
+// layer's own combine reads them); else fp32 to y_perm.
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, float* y_perm, hipStream_t st);
+                      int I, float* y_perm, uint16_t* y_perm16, hipStream_t st);
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
                         const uint16_t* sh_down, int Is, uint16_t* a_sh, float* y_sh,
                         hipStream_t st);

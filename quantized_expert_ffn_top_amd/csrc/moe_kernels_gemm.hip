@@ -3,7 +3,7 @@
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
 //           (fp16), B = Q3S-256 weights, epilogue SwiGLU
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
-//           weights, epilogue fp32 store (permuted rows)
+//           weights, epilogue fp32 (or fp16) store (permuted rows)
 //   UG_BF16 shared up|gate (bf16 x bf16), epilogue SwiGLU
 //   DN_BF16 shared down (bf16 x bf16), epilogue fp32 store
 //   ROUTER  router logits (bf16 x bf16), epilogue fp32 store + bias
@@ -71,6 +71,7 @@ struct GemmArgs {
     const float* bias;       // router bias or null
     uint16_t* out16;         // a16_perm / a_sh
     float* out32;            // y_perm / y_sh / logits
+    uint16_t* y16;           // DN_NL4: y_perm as fp16 instead (null: fp32 to out32)
     int ldo;                 // output row length
 };
 
@@ -481,7 +482,9 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                     if (!ocol[sn]) continue;
                     float v = acc[sm][sn][r];
                     if (MODE == ROUTER && g.bias) v += g.bias[brow[sn]];
-                    g.out32[(int64_t)(row0 + m) * g.ldo + brow[sn]] = v;
+                    const int64_t o = (int64_t)(row0 + m) * g.ldo + brow[sn];
+                    if (MODE == DN_NL4 && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
+                    else g.out32[o] = v;
                 }
             }
         }
@@ -518,11 +521,11 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, float* y_perm, hipStream_t st) {
+                      int I, float* y_perm, uint16_t* y_perm16, hipStream_t st) {
     GemmArgs a{};
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
-    a.out32 = y_perm; a.ldo = H;
+    a.out32 = y_perm; a.y16 = y_perm16; a.ldo = H;
     k_gemm<DN_NL4><<<gemm_grid(col_tiles(H), max_tiles), 256, 0, st>>>(a);
 }
 

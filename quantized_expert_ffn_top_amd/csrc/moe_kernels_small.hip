@@ -286,16 +286,46 @@ __global__ void __launch_bounds__(1024) k_build_tiles(const int32_t* __restrict_
 // ---------------------------------------------------------------- combine
 
 // y[t][h] = sum_j w[t][j] * y_perm[inv[t*k+j]][h] (+ shared[t][h]); 4 h per thread.
-__global__ void k_combine(const float* __restrict__ y_perm, const int32_t* __restrict__ inv,
+// y[t][h..h+3] = sum_j w[t][j] * y_perm[inv[t k + j]][h..h+3] (j in order)
+// + shared[t][h..h+3]; y_perm fp32 or fp16.
+template <typename YT>
+__device__ __forceinline__ float4 load4(const YT* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_float4(f16_bits_to_f32(v.x & 0xffffu), f16_bits_to_f32(v.x >> 16),
+                       f16_bits_to_f32(v.y & 0xffffu), f16_bits_to_f32(v.y >> 16));
+}
+template <typename YT>
+__global__ void k_combine(const YT* __restrict__ y_perm, const int32_t* __restrict__ inv,
                           const float* __restrict__ w, int T, int k, int H,
                           const float* __restrict__ shared, float* __restrict__ y) {
     const int t = blockIdx.y;
     const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (h >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {                      // four rows in flight
+        float4 v[4];
+        float wt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            wt[u] = w[t * k + j + u];
+            v[u] = load4(y_perm + (int64_t)inv[t * k + j + u] * H + h);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc.x += wt[u] * v[u].x;
+            acc.y += wt[u] * v[u].y;
+            acc.z += wt[u] * v[u].z;
+            acc.w += wt[u] * v[u].w;
+        }
+    }
+    for (; j < k; ++j) {
         const float wt = w[t * k + j];
-        const float4 v = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + j] * H + h);
+        const float4 v = load4(y_perm + (int64_t)inv[t * k + j] * H + h);
         acc.x += wt * v.x;
         acc.y += wt * v.y;
         acc.z += wt * v.z;
@@ -386,7 +416,13 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
 void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
                     const float* shared, float* y, hipStream_t st) {
     dim3 grid(cdiv(H / 4, 256), T);
-    k_combine<<<grid, 256, 0, st>>>(y_perm, inv, w, T, k, H, shared, y);
+    k_combine<float><<<grid, 256, 0, st>>>(y_perm, inv, w, T, k, H, shared, y);
+}
+
+void launch_combine16(const uint16_t* y_perm16, const int32_t* inv, const float* w, int T, int k,
+                      int H, const float* shared, float* y, hipStream_t st) {
+    dim3 grid(cdiv(H / 4, 256), T);
+    k_combine<uint16_t><<<grid, 256, 0, st>>>(y_perm16, inv, w, T, k, H, shared, y);
 }
 
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
