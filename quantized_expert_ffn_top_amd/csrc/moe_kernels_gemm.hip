@@ -48,8 +48,10 @@ enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_BF16 = 2, DN_BF16 = 3, ROUTER = 4 };
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int kStages = 2;               // A stages in LDS
-constexpr int kAL = BM * 8 / 256;        // A 16-byte loads per lane per K step
-constexpr int kSMX = BM / 32;            // 32-row groups per tile
+// Token rows per tile: routed modes 64 (two blocks per CU, ragged expert
+// tails); the dense bf16 modes (shared expert, router) 128 (one block per
+// CU: every weight fragment serves twice the rows).
+template <int MODE> constexpr int tile_rows() { return (MODE == 2 || MODE == 3) ? 2 * BM : BM; }
 constexpr int kLutDw = 2048;             // decode table dwords (8 KB)
 
 struct GemmArgs {
@@ -99,13 +101,16 @@ __device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t 
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
+__global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(GemmArgs g) {
     constexpr bool kQ3 = MODE == UG_Q3;
     constexpr bool kNL = MODE == DN_NL4;
     constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_BF16;
     constexpr bool kRouted = MODE == UG_Q3 || MODE == DN_NL4;
+    constexpr int TBM = tile_rows<MODE>();
+    constexpr int kAL = TBM * 8 / 256;              // A 16-byte loads per lane per K step
+    constexpr int kSMX = TBM / 32;                  // 32-row groups per tile
 
-    __shared__ u32x4 As[kStages][BM * 8];
+    __shared__ u32x4 As[kStages][TBM * 8];
     // Decode tables, replicated so that random indices spread over the banks:
     // Q3 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
     // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8).
@@ -130,9 +135,9 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         row0 = g.tiles[3 * mt + 1];
         rows = g.tiles[3 * mt + 2];
     } else {
-        row0 = mt * BM;
+        row0 = mt * TBM;
         if (row0 >= g.T) return;
-        rows = min(BM, g.T - row0);
+        rows = min(TBM, g.T - row0);
     }
 
     // ---- A: lane's load i (0..kAL-1) is row (kAL w + i) * 8 + lane / 8,
@@ -457,8 +462,15 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // The loop is instantiated per count of live 32-row groups (ragged
     // expert tails skip the MFMAs of groups past their rows).
     const int nsm = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
-    if (nsm == 2) run(Cnt<2>{});
-    else run(Cnt<1>{});
+    if constexpr (kSMX == 4) {
+        if (nsm == 4) run(Cnt<4>{});
+        else if (nsm == 3) run(Cnt<3>{});
+        else if (nsm == 2) run(Cnt<2>{});
+        else run(Cnt<1>{});
+    } else {
+        if (nsm == 2) run(Cnt<2>{});
+        else run(Cnt<1>{});
+    }
 
     // ---- epilogue.  Lane l, register r of group (sm, sn): row
     // 32 sm + 8 (r / 4) + 4 (l / 32) + r % 4, the lane's column of half sn.
@@ -532,7 +544,7 @@ void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* ti
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
                         const uint16_t* sh_down, int Is, uint16_t* a_sh, float* y_sh,
                         hipStream_t st) {
-    const int mtiles = (T + BM - 1) / BM;
+    const int mtiles = (T + 2 * BM - 1) / (2 * BM);
     GemmArgs a{};
     a.A = x; a.lda = H; a.T = T; a.Bw = sh_ug; a.N = 2 * Is; a.K = H; a.half_n = Is;
     a.out16 = a_sh; a.ldo = Is;
