@@ -75,6 +75,7 @@ struct GemmArgs {
     float* out32;            // y_perm / y_sh / logits
     uint16_t* y16;           // DN_NL4: y_perm as fp16 instead (null: fp32 to out32)
     int ldo;                 // output row length
+    int npb;                 // routed: N tiles per block (consecutive, same M tile)
 };
 
 // A tile in LDS: row r, 16-byte chunk c at slot r*8 + (c ^ ((r/2) % 8)), so
@@ -124,10 +125,14 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // ---- tile coordinates (XCD-aware: the N tiles of one M tile share an XCD)
+    // ---- tile coordinates (XCD-aware: the N tiles of one M tile share an
+    // XCD).  A routed block takes npb consecutive N tiles [nt0, nt1) of its M
+    // tile, one after the other, with the loads running on across them.
     const int NT = kSwi ? (g.half_n + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+    const int npb = kRouted ? g.npb : 1;
+    const int NGr = (NT + npb - 1) / npb;
     const int bid = blockIdx.x, xcd = bid & 7, li = bid >> 3;
-    const int mt = (li / NT) * 8 + xcd, nt = li % NT;
+    const int mt = (li / NGr) * 8 + xcd, nt0 = (li % NGr) * npb, nt1 = min(nt0 + npb, NT);
     int row0, rows, e = 0;
     if (kRouted) {
         if (mt >= *g.ntiles) return;
@@ -155,22 +160,18 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         asrc[i] = g.A + src * g.lda + c * 8;
     }
 
-    // ---- B: weight row of this lane for column half sn (0, 1)
-    int brow[2];
-    bool ocol[2];                                   // column holds an output
-#pragma unroll
-    for (int sn = 0; sn < 2; ++sn) {
+    // ---- B: weight row of this lane for column half sn (0, 1) of N tile nt
+    auto brow_of = [&](int nt, int sn) {
         if (kSwi) {
-            const int o = nt * (BN / 2) + 32 * w + l32;
-            ocol[sn] = o < g.half_n;
-            const int oc = min(o, g.half_n - 1);
-            brow[sn] = sn ? g.half_n + oc : oc;
-        } else {
-            const int n = nt * BN + 64 * w + 32 * sn + l32;
-            ocol[sn] = n < g.N;
-            brow[sn] = min(n, g.N - 1);
+            const int oc = min(nt * (BN / 2) + 32 * w + l32, g.half_n - 1);
+            return sn ? g.half_n + oc : oc;
         }
-    }
+        return min(nt * BN + 64 * w + 32 * sn + l32, g.N - 1);
+    };
+    auto ocol_of = [&](int nt, int sn) {                  // the column holds an output
+        if (kSwi) return nt * (BN / 2) + 32 * w + l32 < g.half_n;
+        return nt * BN + 64 * w + 32 * sn + l32 < g.N;
+    };
     // ---- A loads into registers (the compiler tracks them exactly)
     struct RawA {
         u32x4 v[kAL];
@@ -204,8 +205,8 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         dn_rb = (g.I / kNL4Weights) * kNL4Bytes;
         ug = 2 * g.I * ug_rb;
     }
-    // byte offset in the record of unit i of this lane, period 0
-    auto unit_off = [&](int i) {
+    // byte offset in the record of unit i of this lane, N tile nt, period 0
+    auto unit_off = [&](int nt, int i) {
         const int u = lane + 64 * i, r = u / kUPR, part = u - r * kUPR;
         int wr;
         if (kSwi) {
@@ -219,10 +220,10 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     struct RawP {
         u32x2 u[kUPR];
     };
-    auto load_period = [&](int p, RawP& R) {
+    auto load_period = [&](int nt, int p, RawP& R) {
 #pragma unroll
         for (int i = 0; i < kUPR; ++i)
-            R.u[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, unit_off(i) + p * kRowB, 0, 0));
+            R.u[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, unit_off(nt, i) + p * kRowB, 0, 0));
     };
     auto put_period = [&](const RawP& R) {
 #pragma unroll
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     };
     const uint8_t* bfrow[2];
 #pragma unroll
-    for (int sn = 0; sn < 2; ++sn) bfrow[sn] = reinterpret_cast<const uint8_t*>(g.Bw + (int64_t)brow[sn] * g.K);
+    for (int sn = 0; sn < 2; ++sn) bfrow[sn] = reinterpret_cast<const uint8_t*>(g.Bw + (int64_t)brow_of(nt0, sn) * g.K);
     auto load_bf = [&](int kt, RawBF& R) {
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
@@ -360,6 +361,40 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         }
     };
 
+    // ---- epilogue of N tile nt.  Lane l, register r of group (sm, sn): row
+    // 32 sm + 8 (r / 4) + 4 (l / 32) + r % 4, the lane's column of half sn.
+    auto epilogue = [&](int nt, auto smc) {
+        constexpr int SM = decltype(smc)::value;
+        const int br0 = brow_of(nt, 0), br1 = brow_of(nt, 1);
+        const bool oc0 = ocol_of(nt, 0), oc1 = ocol_of(nt, 1);
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 32 * sm + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (m >= rows) continue;
+                if constexpr (kSwi) {
+                    if (!oc0) continue;
+                    const float u = acc[sm][0][r], gv = acc[sm][1][r];
+                    const uint32_t bf = f32_to_bf16(gv / (1.0f + expf(-gv)) * u);
+                    const uint16_t v = kRouted ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
+                    g.out16[(int64_t)(row0 + m) * g.ldo + br0] = v;
+                } else {
+#pragma unroll
+                    for (int sn = 0; sn < 2; ++sn) {
+                        if (!(sn ? oc1 : oc0)) continue;
+                        const int br = sn ? br1 : br0;
+                        float v = acc[sm][sn][r];
+                        if (MODE == ROUTER && g.bias) v += g.bias[br];
+                        const int64_t o = (int64_t)(row0 + m) * g.ldo + br;
+                        if (MODE == DN_NL4 && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
+                        else g.out32[o] = v;
+                    }
+                }
+            }
+        }
+    };
+
     // ---- pipeline (two LDS stages for A, A registers alternating by step
     // parity).  Step kt: A(kt + 1) registers -> stage (kt + 1) % 2 (read last
     // in step kt - 1, before the barrier that ended it); load A(kt + 3) into
@@ -387,23 +422,34 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     }
     RawA A0, A1;
     load_a(0, A0);
-    load_a(min(1, nk - 1), A1);
+    load_a(1 % nk, A1);
     put_a(0, A0);
-    load_a(min(2, nk - 1), A0);
+    load_a(2 % nk, A0);
 
     auto run = [&](auto smc) {
         if constexpr (kRouted) {
+            // N tiles nt0 .. nt1 - 1 back to back: nk is even (or npb = 1), so the
+            // A stages, A register slots and B periods carry on across tiles; A
+            // rows are the same for every N tile, so A is loaded at k mod K.
             RawP P;
-            load_period(0, P);
+            load_period(nt0, 0, P);
             __syncthreads();                         // stage 0 and the table written
+            const int npt = nk / kPer;               // periods per N tile
             // Ra: A(kt + 1) (refilled with kt + 3); opens: step kt starts a period
-            auto step = [&](int kt, RawA& Ra, bool opens, Frag& F) {
+            auto step = [&](int nt, int kt, RawA& Ra, bool opens, Frag& F) {
                 const int st = kt & 1;
                 put_a(st ^ 1, Ra);
-                load_a(min(kt + 3, nk - 1), Ra);
-                if (opens) {
-                    put_period(P);
-                    load_period(kt / kPer + 1, P);
+                if (opens) put_period(P);
+                if constexpr (kQ3) {                 // a single N tile
+                    load_a(min(kt + 3, nk - 1), Ra);
+                    if (opens) load_period(nt, kt / kPer + 1, P);
+                } else {
+                    load_a((kt + 3) % nk, Ra);
+                    if (opens) {
+                        const int pn = kt / kPer + 1;    // next period: this tile's or the next tile's first
+                        if (pn < npt) load_period(nt, pn, P);
+                        else load_period(min(nt + 1, NT - 1), 0, P);
+                    }
                 }
                 uint32_t q[2][5];
                 read_raw(kt, q);
@@ -419,22 +465,34 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
             };
             Frag F;
             if constexpr (kQ3) {
-                // K = H is a multiple of 256: a period per four steps, d applied
-                // after the fourth
+                // one N tile per block (48 steps at H = 3072); K = H is a multiple
+                // of 256: a period per four steps, d applied after the fourth
                 for (int kt = 0; kt < nk; kt += 4) {
-                    step(kt, A1, true, F);
-                    step(kt + 1, A0, false, F);
-                    step(kt + 2, A1, false, F);
-                    step(kt + 3, A0, false, F);
+                    step(nt0, kt, A1, true, F);
+                    step(nt0, kt + 1, A0, false, F);
+                    step(nt0, kt + 2, A1, false, F);
+                    step(nt0, kt + 3, A0, false, F);
                     apply_d(F, smc);
                 }
+                epilogue(nt0, smc);
             } else {
-                int kt = 0;
-                for (; kt + 2 <= nk; kt += 2) {
-                    step(kt, A1, true, F);
-                    step(kt + 1, A0, false, F);
+                for (int nt = nt0; nt < nt1; ++nt) {
+                    if (nt > nt0) {
+#pragma unroll
+                        for (int a = 0; a < kSMX; ++a)
+#pragma unroll
+                            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+                    }
+                    int kt = 0;
+                    for (; kt + 2 <= nk; kt += 2) {
+                        step(nt, kt, A1, true, F);
+                        step(nt, kt + 1, A0, false, F);
+                    }
+                    if (kt < nk) step(nt, kt, A1, true, F);
+                    epilogue(nt, smc);
                 }
-                if (kt < nk) step(kt, A1, true, F);
             }
         } else {
             RawBF B0, B1;
@@ -457,6 +515,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                 step(kt + 1, A0, B1);
             }
             if (kt < nk) step(kt, A1, B0);
+            epilogue(nt0, smc);
         }
     };
     // The loop is instantiated per count of live 32-row groups (ragged
@@ -472,35 +531,6 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         else run(Cnt<1>{});
     }
 
-    // ---- epilogue.  Lane l, register r of group (sm, sn): row
-    // 32 sm + 8 (r / 4) + 4 (l / 32) + r % 4, the lane's column of half sn.
-#pragma unroll
-    for (int sm = 0; sm < kSMX; ++sm) {
-        if (sm >= nsm) break;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * sm + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (m >= rows) continue;
-            if constexpr (kSwi) {
-                if (!ocol[0]) continue;
-                const int o = brow[0];
-                const float u = acc[sm][0][r], gv = acc[sm][1][r];
-                const uint32_t bf = f32_to_bf16(gv / (1.0f + expf(-gv)) * u);
-                const uint16_t v = kRouted ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
-                g.out16[(int64_t)(row0 + m) * g.ldo + o] = v;
-            } else {
-#pragma unroll
-                for (int sn = 0; sn < 2; ++sn) {
-                    if (!ocol[sn]) continue;
-                    float v = acc[sm][sn][r];
-                    if (MODE == ROUTER && g.bias) v += g.bias[brow[sn]];
-                    const int64_t o = (int64_t)(row0 + m) * g.ldo + brow[sn];
-                    if (MODE == DN_NL4 && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
-                    else g.out32[o] = v;
-                }
-            }
-        }
-    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -528,7 +558,8 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.perm = perm; a.k = k; a.A = x16; a.lda = H;
     a.N = 2 * I; a.K = H; a.half_n = I; a.H = H; a.I = I; a.out16 = a16_perm; a.ldo = I;
-    k_gemm<UG_Q3><<<gemm_grid(swi_tiles(I), max_tiles), 256, 0, st>>>(a);
+    a.npb = 1;
+    k_gemm<UG_Q3><<<gemm_grid((swi_tiles(I) + a.npb - 1) / a.npb, max_tiles), 256, 0, st>>>(a);
 }
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
@@ -538,7 +569,8 @@ void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* ti
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
     a.out32 = y_perm; a.y16 = y_perm16; a.ldo = H;
-    k_gemm<DN_NL4><<<gemm_grid(col_tiles(H), max_tiles), 256, 0, st>>>(a);
+    a.npb = (I / BK) % 2 == 0 ? 4 : 1;               // tiles chain only with an even step count
+    k_gemm<DN_NL4><<<gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles), 256, 0, st>>>(a);
 }
 
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
