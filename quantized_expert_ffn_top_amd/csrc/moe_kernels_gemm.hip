@@ -434,7 +434,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
             RawP P;
             load_period(nt0, 0, P);
             __syncthreads();                         // stage 0 and the table written
-            const int npt = nk / kPer;               // periods per N tile
+            const int npt = (nk + kPer - 1) / kPer;  // periods per N tile (the last may be half)
             // Ra: A(kt + 1) (refilled with kt + 3); opens: step kt starts a period
             auto step = [&](int nt, int kt, RawA& Ra, bool opens, Frag& F) {
                 const int st = kt & 1;

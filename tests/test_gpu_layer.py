@@ -50,8 +50,7 @@ def test_tiny_layer(T):
     assert_close(y, ref["y"], "tiny T=%d" % T)
 
 
-def _real_case(T, seed, zipf_s=1.0, sample=None):
-    sh = synth.REAL
+def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
     lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev())
     x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
@@ -77,6 +76,28 @@ def _real_case(T, seed, zipf_s=1.0, sample=None):
 @pytest.mark.parametrize("T", [1, 3, 8, 16])
 def test_real_decode_layer(T):
     _real_case(T, seed=2)
+
+
+# Edge shape for both paths: I = 3 * 64 (an odd count of 64-wide K steps in
+# the down projection, a partial last up|gate output tile), 24 experts (not a
+# multiple of the 16-expert router tile), top-3, a 64-wide shared expert.
+ODD = synth.Shape(hidden=512, inter=192, n_experts=24, top_k=3, shared_inter=64)
+
+
+@pytest.mark.parametrize("T", [5, 16, 40])
+def test_odd_shape_layer(T):
+    _real_case(T, seed=6, sh=ODD)
+
+
+# Degenerate routing: every expert selected (k = E), and a single expert (k = 1).
+ALL_EXPERTS = synth.Shape(hidden=256, inter=64, n_experts=8, top_k=8, shared_inter=0)
+ONE_EXPERT = synth.Shape(hidden=256, inter=128, n_experts=32, top_k=1, shared_inter=0)
+
+
+@pytest.mark.parametrize("sh", [ALL_EXPERTS, ONE_EXPERT], ids=["k_eq_E", "k_1"])
+@pytest.mark.parametrize("T", [3, 33])
+def test_degenerate_routing_layer(T, sh):
+    _real_case(T, seed=7, sh=sh)
 
 
 @pytest.mark.parametrize("T", [17, 64])
