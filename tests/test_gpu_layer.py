@@ -66,7 +66,8 @@ def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
     rows = np.arange(T) if sample is None else np.asarray(sample)
     cache = ExpertCache(sh, lambda e: synth.expert_record(sh, seed, 0, e).numpy())
     ref = OM.layer_forward(xs[rows], sh.top_k, cache, sh.n_experts, logits=L[rows],
-                           shared=real_shared_np(lay), force_ids=ids[rows])
+                           shared=real_shared_np(lay) if sh.shared_inter else None,
+                           force_ids=ids[rows])
     assert np.abs(w[rows] - ref["w"]).max() <= 1e-5
     assert_close(y[rows], ref["y"], "real T=%d" % T)
     assert np.all(np.isfinite(y))
