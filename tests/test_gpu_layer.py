@@ -101,6 +101,19 @@ def test_degenerate_routing_layer(T, sh):
     _real_case(T, seed=7, sh=sh)
 
 
+# Limits of the descriptor: the widest hidden size (8192; its up|gate rows do
+# not fit the bandwidth path's LDS staging, so small batches take the GEMM
+# path too) and the most experts / largest top-k (1024, 32).
+WIDE = synth.Shape(hidden=8192, inter=64, n_experts=16, top_k=2, shared_inter=64)
+MANY = synth.Shape(hidden=256, inter=64, n_experts=1024, top_k=32, shared_inter=0)
+
+
+@pytest.mark.parametrize("sh", [WIDE, MANY], ids=["H8192", "E1024_k32"])
+@pytest.mark.parametrize("T", [2, 20])
+def test_limit_shape_layer(T, sh):
+    _real_case(T, seed=8, sh=sh)
+
+
 @pytest.mark.parametrize("T", [17, 64])
 def test_real_small_gemm_layer(T):
     _real_case(T, seed=7)
