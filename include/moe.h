@@ -163,9 +163,9 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
 /* The whole layer (A1-A8): y fp32 [T][H] from x bf16 [T][H].  If
  * logits_or_null is given (fp32 [T][E]) the router is skipped.  Optional
  * outputs: topk_ids_out int32 [T][k], topk_w_out fp32 [T][k].  Tokens T <= 16
- * take the bandwidth path (weights streamed once; the down projection and the
- * weighted combine fused, summed per output row in a fixed order), larger T
- * the grouped-GEMM path; both compute the same function. */
+ * take the bandwidth path (every weight byte streamed once), larger T the
+ * grouped-GEMM path; both compute the same function, and each output row is
+ * summed in a fixed order (runs repeat bit for bit). */
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* wts,
                              const uint16_t* x, int32_t T, const float* logits_or_null,
                              float* y, int32_t* topk_ids_out, float* topk_w_out,
@@ -175,12 +175,12 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
  * addition events[0] (hipEvent_t, created by the caller) is recorded on
  * `stream` before the first kernel and events[i] after the i-th kernel, while
  * i < n_events.  *n_marks receives the number of marks the call wanted
- * (kernels + 1).  Kernel order -- T <= 16: [router partials and/or shared
- * up|gate (when a router runs or a shared expert exists)], routing +
- * permutation, routed up|gate, down + combine; T > 16: [router GEMM (if no
- * logits)], top-k, fp16 staging, permutation (3 kernels, one mark), [shared
- * expert GEMMs (2 kernels, one mark)], routed up|gate GEMM, routed down GEMM,
- * combine. */
+ * (kernels + 1).  Kernel order -- T <= 16: stage 1 (router logits, shared
+ * up|gate partials, fp16 copy of x), routed up|gate (routing, top-k and
+ * permutation, at its start), down projections (routed + shared), combine;
+ * T > 16: [router GEMM (if no logits)], top-k, fp16 staging, permutation (3
+ * kernels, one mark), [shared expert GEMMs (2 kernels, one mark)], routed
+ * up|gate GEMM, routed down GEMM, combine. */
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,
                                    const uint16_t* x, int32_t T, const float* logits_or_null,
                                    float* y, int32_t* topk_ids_out, float* topk_w_out, void* ws,
