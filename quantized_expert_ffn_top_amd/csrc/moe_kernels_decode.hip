@@ -586,6 +586,7 @@ constexpr int kDnWaves = 8;
 constexpr int kDnChunkDw = 72;                    // 16 NL4 blocks of a row (288 bytes)
 constexpr int kDnStageDw = kDnChunkDw + 2;        // stage row stride (= 10 mod 32: the 16 rows x 2 lane groups of a half-wave hit distinct banks)
 constexpr int kDnLoads = 16 * kDnChunkDw / 64;    // dword loads per lane per staged chunk (18)
+constexpr int kDnShSteps = 16;                    // shared down: 16x16x32 steps per load batch (Is <= 512 at once)
 
 // Persistent: blocks of kDnWaves waves; after the table is built every wave works
 // alone.  The waves are dealt to the active experts (2 shares each) and to
@@ -637,20 +638,63 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         const bool vt = r < T;
         const uint16_t* arow = a_sh + (int64_t)(vt ? r : 0) * Is + 8 * g;
         const __amdgpu_buffer_rsrc_t yo = __builtin_amdgcn_make_buffer_rsrc(y_sh, 0, T * H * 4, 0x00020000);
-        for (int sl = s0; sl < s1; ++sl) {
-            const uint16_t* brow = sh_down + (int64_t)(16 * sl + r) * Is + 8 * g;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int kk = 0; kk < Is / 32; ++kk) {
-                const u32x4 av = vt ? ld16(arow + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
-                acc = mfma16_bf16(av, ld16_stream(brow + 32 * kk), acc);
-            }
+        auto store = [&](int sl, const f32x4& acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * g + i;
                 const uint32_t off = m < T ? (uint32_t)((m * H + 16 * sl + r) * 4) : 0x80000000u;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), yo, off, 0, 0);
             }
+        };
+        const int nks = Is / 32;
+        if (nks <= kDnShSteps) {
+            // A in registers; a slice's whole K (<= 1 KB per lane group row)
+            // loaded at once, the next slice in flight during the steps.  Steps
+            // past Is load nothing (out-of-range buffer offsets read zero).
+            const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(sh_down), 0, H * Is * 2, 0x00020000);
+            u32x4 a[kDnShSteps], B0[kDnShSteps], B1[kDnShSteps];
+#pragma unroll
+            for (int i = 0; i < kDnShSteps; ++i)
+                a[i] = (vt && i < nks) ? ld16(arow + 32 * i) : u32x4{0u, 0u, 0u, 0u};
+            auto load_b = [&](int sl, u32x4* B) {
+                const uint32_t rowo = (uint32_t)(((16 * min(sl, s1 - 1) + r) * Is + 8 * g) * 2);
+#pragma unroll
+                for (int i = 0; i < kDnShSteps; ++i)
+                    B[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        bsrc, i < nks ? rowo + 64u * i : 0x80000000u, 0, 0));
+            };
+            auto steps = [&](int sl, const u32x4* B) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < kDnShSteps; ++i) acc = mfma16_bf16(a[i], B[i], acc);
+                store(sl, acc);
+            };
+            load_b(s0, B0);
+            for (int sl = s0; sl < s1; sl += 2) {
+                load_b(sl + 1, B1);
+                steps(sl, B0);
+                if (sl + 1 >= s1) break;
+                load_b(sl + 2, B0);
+                steps(sl + 1, B1);
+            }
+            return;
+        }
+        for (int sl = s0; sl < s1; ++sl) {
+            const uint16_t* brow = sh_down + (int64_t)(16 * sl + r) * Is + 8 * g;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < nks; k0 += kDnShSteps) {  // kDnShSteps loads in flight
+                u32x4 av[kDnShSteps], bv[kDnShSteps];
+#pragma unroll
+                for (int i = 0; i < kDnShSteps; ++i) {
+                    const bool ok = k0 + i < nks;
+                    av[i] = (vt && ok) ? ld16(arow + 32 * (k0 + i)) : u32x4{0u, 0u, 0u, 0u};
+                    bv[i] = ok ? ld16_stream(brow + 32 * (k0 + i)) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int i = 0; i < kDnShSteps; ++i) acc = mfma16_bf16(av[i], bv[i], acc);
+            }
+            store(sl, acc);
         }
         return;
     }
