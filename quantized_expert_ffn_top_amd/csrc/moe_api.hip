@@ -88,7 +88,7 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     s.max_tiles = max_tiles_for(T, E, k, dec_path(T, H, E));
     s.x16 = take((size_t)T * H * 2);
     s.shp = take((size_t)(H / kShKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
-    s.logits = take((size_t)T * E * 4);
+    s.logits = take((size_t)(dec_path(T, H, E) ? kDecLogitParts : 1) * T * E * 4);
     s.ids = take(n * 4);
     s.w = take(n * 4);
     s.offsets = take((size_t)(E + 1) * 4);
@@ -200,7 +200,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     if (T <= kDecMaxT) {
-        launch_dec_stage1(x, T, H, E, w_r, b, logits, nullptr, 0, nullptr, nullptr, st);
+        launch_dec_stage1(x, T, H, E, w_r, b, logits, nullptr, 0, nullptr, nullptr, 1, st);
     } else {
         launch_gemm_router(x, T, H, E, w_r, b, logits, st);
     }
@@ -368,11 +368,15 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         // stage 1 always runs: router logits (none given), shared up|gate
         // partials (shared expert present) and the fp16 copy of x
         launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
-                          wts->router_b, lg, sug, Is, shp, x16, st);
+                          wts->router_b, lg, sug, Is, shp, x16, kDecLogitParts, st);
         mk->mark();
         // routing runs inside the up|gate kernel (its block 0 writes it out)
         const RouteOut ro{ids, wv, topk_ids_out, topk_w_out, offs, perm, inv, tiles, nt};
-        launch_upgate_dec(ex, wts->expert_stride, logits_or_null ? logits_or_null : lg, E, k,
+        // given logits are used as they are; the router's are kDecLogitParts
+        // partial planes, summed with the bias by the routing
+        launch_upgate_dec(ex, wts->expert_stride, logits_or_null ? logits_or_null : lg,
+                          logits_or_null ? 1 : kDecLogitParts,
+                          logits_or_null ? nullptr : wts->router_b, E, k,
                           L.max_tiles, x16, T, H, I, a16, has_sh ? shp : nullptr, Is, ash, ro,
                           n_cu, st);
         mk->mark();

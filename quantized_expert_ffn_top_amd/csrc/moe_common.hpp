@@ -122,28 +122,62 @@ __device__ __forceinline__ float order_key_value(uint32_t k) {
 
 // Wave-wide max / min of a u32 through DPP row permutations (max over each
 // 16-lane row) and four lane reads; the result is wave-uniform.
+// (Every lane of a full row is a valid source for these patterns, so the
+// moves carry no old value and fold into the max / min as DPP operands.)
+#define MOE_DPP(v, ctrl) ((uint32_t)__builtin_amdgcn_mov_dpp((int)(v), (ctrl), 0xF, 0xF, true))
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));  // xor 1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));  // xor 2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false)); // half mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false)); // mirror
+    v = max(v, MOE_DPP(v, 0xB1));                  // xor 1
+    v = max(v, MOE_DPP(v, 0x4E));                  // xor 2
+    v = max(v, MOE_DPP(v, 0x141));                 // half mirror
+    v = max(v, MOE_DPP(v, 0x140));                 // mirror
     const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
     const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
     return max(max(a, b), max(c, d));
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
-    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+    v = min(v, MOE_DPP(v, 0xB1));
+    v = min(v, MOE_DPP(v, 0x4E));
+    v = min(v, MOE_DPP(v, 0x141));
+    v = min(v, MOE_DPP(v, 0x140));
     const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
     const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
     return min(min(a, b), min(c, d));
 }
+#undef MOE_DPP
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Wave-wide sum of a float through DPP (sums of 16-lane rows, then the four
+// row sums added as (r0 + r1) + (r2 + r3)); the result is wave-uniform and
+// the same for equal inputs.
+__device__ __forceinline__ float wave_sum_f32_dpp(float v) {
+#define MOE_DPPF(x, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), (ctrl), 0xF, 0xF, true))
+    v += MOE_DPPF(v, 0xB1);                        // xor 1
+    v += MOE_DPPF(v, 0x4E);                        // xor 2
+    v += MOE_DPPF(v, 0x141);                       // half mirror
+    v += MOE_DPPF(v, 0x140);                       // mirror
+#undef MOE_DPPF
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (a + b) + (c + d);
+}
+
+// Inclusive scan of an int over the wave through DPP: shifts by 1, 2, 4, 8
+// within each 16-lane row, then row 0's last lane into row 1 and rows 0-1's
+// last lane into rows 2-3 (rows that do not take a step add zero).
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
     return v;
 }
 
@@ -153,8 +187,9 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // l, l+64, ...).  Each lane first sorts its Q candidates by (logit desc,
 // expert asc) with a sorting network (all pairs distinct, so any network
 // gives the one order); then each round takes the largest head over the wave
-// (then the lowest expert among equal heads) and the winning lane drops its
-// head.
+// (then the lowest expert among equal heads: looked for only when a ballot
+// finds the largest head on more than one lane) and the winning lane drops
+// its head.
 template <int Q>
 __device__ __forceinline__ void lane_sort_desc(uint32_t* key, int* idx) {
     auto ce = [&](int a, int b) {                  // a < b: put the larger (key, -idx) first
@@ -198,8 +233,15 @@ __device__ __forceinline__ void wave_topk_q(Get get, int E, int k, int& out_id, 
     for (int j = 0; j < k; ++j) {
         const bool has = idx[0] < 1024;
         const uint32_t m = wave_max_u32(has ? key[0] : 0u);
-        const uint32_t cand = (has && key[0] == m) ? (uint32_t)(lane + 64 * idx[0]) : 0xffffffffu;
-        const uint32_t win = wave_min_u32(cand);
+        const bool at = has && key[0] == m;
+        const uint64_t tied = __ballot(at);
+        uint32_t win;
+        if (__popcll(tied) == 1) {                       // one lane holds the largest head
+            const int wl = __ffsll((unsigned long long)tied) - 1;
+            win = (uint32_t)(wl + 64 * __builtin_amdgcn_readlane(idx[0], wl));
+        } else {
+            win = wave_min_u32(at ? (uint32_t)(lane + 64 * idx[0]) : 0xffffffffu);
+        }
         if ((int)(win & 63u) == lane) {                  // drop the head
 #pragma unroll
             for (int i = 0; i + 1 < Q; ++i) {
@@ -228,9 +270,9 @@ __device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, fl
 // Softmax over the k selected logits held by lanes 0..k-1 (lane 0 = max).
 __device__ __forceinline__ float wave_softmax_selected(float v, int k) {
     const int lane = __lane_id();
-    const float m = __shfl(v, 0, 64);
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     const float ex = (lane < k) ? expf(v - m) : 0.f;
-    return ex / wave_sum_f32(ex);
+    return ex / wave_sum_f32_dpp(ex);
 }
 
 // ---------------------------------------------------------------- decoders

@@ -9,6 +9,8 @@ namespace moe {
 // Work sizes shared by host and device code.
 constexpr int kDecMaxT = 16;          // tokens handled by the bandwidth path
 constexpr int kShKChunk = 256;        // K per shared up|gate partial (bandwidth path)
+constexpr int kDecLogitParts = 4;     // K parts of the layer's router on the bandwidth path
+constexpr int kMaxLogitParts = 4;
 constexpr int kMaxSlots = kDecMaxT * 32;  // T * k slots of the bandwidth path
 constexpr int kGemmBM = 64;           // rows per grouped-GEMM tile
 constexpr int kGemmBN = 256;          // weight rows per grouped-GEMM tile
@@ -37,9 +39,11 @@ void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps,
 // upgate_dec_supported(H, T, E) (the staged up|gate rows of two items and the
 // routing scratch fit in LDS)
 bool upgate_dec_supported(int H, int T, int E);
+// kp: K parts of the router (1: logits[T][E] with the bias; > 1: partial
+// planes logits[kp][T][E] without it, for the up|gate kernel's routing)
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
                        const float* bias, float* logits, const uint16_t* sh_ug, int Is,
-                       float* shp, uint16_t* x16, hipStream_t st);
+                       float* shp, uint16_t* x16, int kp, hipStream_t st);
 // Routing results of the bandwidth path, written by the up|gate kernel.
 struct RouteOut {
     int32_t* ids;
@@ -52,8 +56,9 @@ struct RouteOut {
     int32_t* tiles;          // [3 * active experts]
     int32_t* ntiles;
 };
-void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int E,
-                       int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
+// logits: np planes [np][T][E] summed in plane order, then lbias if non-null
+void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int np,
+                       const float* lbias, int E, int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
                        uint16_t* a16_perm, const float* shp, int Is, uint16_t* a_sh,
                        const RouteOut& ro, int n_cu, hipStream_t st);
 void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* tiles,
