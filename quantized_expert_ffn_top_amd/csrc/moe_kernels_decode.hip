@@ -31,10 +31,12 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 
 // ---------------------------------------------------------------- stage 1
 // Blocks of 4 waves, spread over the whole chip.  Blocks [0, n_rb): router
-// logits of 16 experts: the waves split K in 4 equal parts (16x16x32 bf16
-// steps, A = tokens, rows >= T zero; a wave's loads, up to 24 steps, are all
-// in flight at once), their partial sums are added in wave order through
-// LDS and the bias is added last: logits[t][e].  Blocks [n_rb, ...): wave
+// logits of 16 experts over one of kp equal K parts (block = tile * kp +
+// part): the waves split the part in 4 (16x16x32 bf16 steps, A = tokens,
+// rows >= T zero; a wave's loads, up to 24 steps, are all in flight at once)
+// and their partial sums are added in wave order through LDS.  kp = 1: the
+// bias is added last, logits[t][e]; kp > 1: partial planes logits[part][t][e]
+// without the bias, summed in part order (then the bias) by the routing.  Blocks [n_rb, ...): wave
 // items, no block synchronisation.  Items [0, n_s): shared expert up|gate
 // partials of 16 rows (rows 0..Is-1 up, Is..2Is-1 gate) over one 256-wide K
 // chunk, shp[kc][t][2 Is]; summed and passed through SwiGLU by the up|gate
@@ -45,7 +47,7 @@ constexpr int kS1Batch = 24;                    // K steps in flight per wave
 __global__ void __launch_bounds__(64 * kS1Waves) k_dec_stage1(const uint16_t* __restrict__ x, int T, int H,
                                                     int E, const uint16_t* __restrict__ w_r,
                                                     const float* __restrict__ bias,
-                                                    float* __restrict__ logits, int n_rb,
+                                                    float* __restrict__ logits, int n_rb, int kp,
                                                     const uint16_t* __restrict__ sh_ug, int Is,
                                                     float* __restrict__ shp, int n_s,
                                                     uint16_t* __restrict__ x16) {
@@ -55,9 +57,11 @@ __global__ void __launch_bounds__(64 * kS1Waves) k_dec_stage1(const uint16_t* __
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const bool vt = r < T;
     if ((int)blockIdx.x < n_rb) {
-        const int row = blockIdx.x * 16 + r;
+        const int tile = blockIdx.x / kp, part = blockIdx.x - tile * kp;
+        const int row = tile * 16 + r;
         const bool vr = row < E;
-        const int S = H / 32, sa = w * S / kS1Waves, sb = (w + 1) * S / kS1Waves;   // this wave's K steps
+        const int S = H / 32, pa = part * S / kp, pb = (part + 1) * S / kp;
+        const int sa = pa + w * (pb - pa) / kS1Waves, sb = pa + (w + 1) * (pb - pa) / kS1Waves;   // this wave's K steps
         const uint16_t* brow = w_r + (int64_t)(vr ? row : 0) * H + 8 * g;
         const uint16_t* arow = x + (int64_t)(vt ? r : 0) * H + 8 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -80,11 +84,12 @@ __global__ void __launch_bounds__(64 * kS1Waves) k_dec_stage1(const uint16_t* __
             for (int v = 1; v < kS1Waves; ++v)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sum[i] += red[v][lane][i];
-            const float bb = (vr && bias) ? bias[row] : 0.f;
+            const float bb = (vr && bias && kp == 1) ? bias[row] : 0.f;
+            float* out = logits + (int64_t)part * T * E;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * g + i;
-                if (m < T && vr) logits[(int64_t)m * E + row] = sum[i] + bb;
+                if (m < T && vr) out[(int64_t)m * E + row] = sum[i] + bb;
             }
         }
         return;
@@ -132,22 +137,12 @@ template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
     constexpr int NW = NT / 64;
     const int lane = __lane_id(), wid = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    const int incl = wave_incl_scan_dpp(v);
     if (lane == 63) lds[wid] = incl;
     __syncthreads();
     if (threadIdx.x < 64) {
         const int sv = lane < NW ? lds[lane] : 0;
-        int si = sv;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int o = __shfl_up(si, off, 64);
-            if (lane >= off) si += o;
-        }
+        const int si = wave_incl_scan_dpp(sv);
         if (lane < NW) lds[16 + lane] = si - sv;
         if (lane == NW - 1) lds[32] = si;
     }
@@ -168,12 +163,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
 // s_tiles (active experts in ascending order: expert, first slot, slots),
 // s_perm (slot -> flat index t*k + j) and *s_nt; with `publish` also to global
 // memory (ids, w, the optional copies, offsets [E+1], perm, inv, tiles,
-// ntiles).  scr: >= route_scratch_bytes(T, E) of LDS (the logits are staged
-// there with batched loads before the top-k reads them).
+// ntiles).  The logits are np planes [np][T][E] summed in plane order, plus
+// `bias` when given (np = 1, no bias: the logits as they are).  scr: >=
+// route_scratch_bytes(T, E) of LDS (the sums are staged there before the
+// top-k reads them).
 __host__ __device__ constexpr int route_scratch_bytes(int T, int E) { return 10752 + T * E * 4; }
 
 template <int NT>
-__device__ __forceinline__ void route_block(const float* __restrict__ logits, int T, int E, int k,
+__device__ __forceinline__ void route_block(const float* __restrict__ logits, int np,
+                                            const float* __restrict__ bias, int T, int E, int k,
                                             uint8_t* scr, int* s_tiles, int* s_perm, int* s_nt,
                                             bool publish, int32_t* ids, float* wts,
                                             int32_t* ids_out, float* w_out, int32_t* offsets,
@@ -187,13 +185,25 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     const int tid = threadIdx.x, lane = __lane_id(), wid = threadIdx.x >> 6;
     for (int e = tid; e < 1024; e += NT) s_mask[e] = 0u;
     const int nl = T * E;
-    for (int i0 = tid; i0 < nl; i0 += 8 * NT) {                    // 8 loads in flight per thread
-        float v[8];
+    for (int i0 = tid; i0 < nl; i0 += 8 * NT) {                    // 8 x (np + 1) loads in flight
+        float v[8][kMaxLogitParts + 1];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = logits[min(i0 + u * NT, nl - 1)];
+        for (int u = 0; u < 8; ++u) {
+            const int i = min(i0 + u * NT, nl - 1);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (i0 + u * NT < nl) s_log[i0 + u * NT] = v[u];
+            for (int p = 0; p < kMaxLogitParts; ++p) v[u][p] = p < np ? logits[(int64_t)p * nl + i] : 0.f;
+            v[u][kMaxLogitParts] = bias ? bias[i % E] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (i0 + u * NT < nl) {
+                float sum = v[u][0];
+#pragma unroll
+                for (int p = 1; p < kMaxLogitParts; ++p)
+                    if (p < np) sum += v[u][p];
+                s_log[i0 + u * NT] = bias ? sum + v[u][kMaxLogitParts] : sum;
+            }
+        }
     }
     __syncthreads();
     for (int t = wid; t < T; t += NT / 64) {
@@ -224,9 +234,11 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
         cs += c[q];
         as += c[q] > 0 ? 1 : 0;
     }
-    int tot_c, tot_a;
-    int off = block_excl_scan<NT>(cs, s_scan, tot_c);
-    int ai = block_excl_scan<NT>(as, s_scan, tot_a);
+    // one scan of both counts: slots (< 2^9) in the low half, experts (< 2^11) above
+    int tot;
+    const int pre = block_excl_scan<NT>(cs | (as << 16), s_scan, tot);
+    int off = pre & 0xffff, ai = pre >> 16;
+    const int tot_c = tot & 0xffff, tot_a = tot >> 16;
 #pragma unroll
     for (int q = 0; q < QE; ++q) {
         const int e = QE * tid + q;
@@ -330,8 +342,9 @@ __host__ __device__ constexpr int ug_waves(int H) {
 // expert: a_sh[t][o] = bf16(silu(sum_c g) * sum_c u) over the stage-1 chunks.
 template <int GPW, bool FULL, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
-    const uint8_t* __restrict__ experts, int64_t estride, const float* __restrict__ logits, int E,
-    int k, const uint16_t* __restrict__ x16, int T, int H, int I, uint16_t* __restrict__ a16_perm,
+    const uint8_t* __restrict__ experts, int64_t estride, const float* __restrict__ logits, int np,
+    const float* __restrict__ lbias, int E, int k, const uint16_t* __restrict__ x16, int T, int H,
+    int I, uint16_t* __restrict__ a16_perm,
     const float* __restrict__ shp, int nkc, int Is, uint16_t* __restrict__ a_sh, RouteOut ro) {
     constexpr int NT = 64 * WAVES;                          // threads
     constexpr int CH = FULL ? 16 : 8;                       // bytes per staging load
@@ -347,7 +360,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     // routing (every block; block 0 publishes it), in the partial-sum space
-    route_block<NT>(logits, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids, ro.w,
+    route_block<NT>(logits, np, lbias, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids, ro.w,
                     ro.ids_out, ro.w_out, ro.offsets, ro.perm, ro.inv, ro.tiles, ro.ntiles);
     const int nsl = I / 16;
     const int n_items = __builtin_amdgcn_readfirstlane(s_nt) * nsl;
@@ -845,20 +858,21 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
 
 void launch_dec_stage1(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
                        const float* bias, float* logits, const uint16_t* sh_ug, int Is,
-                       float* shp, uint16_t* x16, hipStream_t st) {
+                       float* shp, uint16_t* x16, int kp, hipStream_t st) {
     const int nkc = H / kShKChunk;
-    const int n_rb = w_r ? (E + 15) / 16 : 0;
+    const int n_rb = w_r ? (E + 15) / 16 * kp : 0;
     const int n_s = (sh_ug && Is > 0) ? (2 * Is / 16) * nkc : 0;
     const int n_x = x16 ? nkc : 0;
     const int n_wb = (n_s + n_x + kS1Waves - 1) / kS1Waves;
     if (n_rb + n_wb == 0) return;
-    k_dec_stage1<<<n_rb + n_wb, 64 * kS1Waves, 0, st>>>(x, T, H, E, w_r, bias, logits, n_rb, sh_ug, Is,
+    k_dec_stage1<<<n_rb + n_wb, 64 * kS1Waves, 0, st>>>(x, T, H, E, w_r, bias, logits, n_rb, kp, sh_ug, Is,
                                                         shp, n_s, x16);
 }
 
 template <int GPW, bool FULL, int WAVES>
 static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, int64_t estride,
-                         const float* logits, int E, int k, const uint16_t* x16, int T, int H,
+                         const float* logits, int np, const float* lbias, int E, int k,
+                         const uint16_t* x16, int T, int H,
                          int I, uint16_t* a16_perm, const float* shp, int nkc, int Is,
                          uint16_t* a_sh, const RouteOut& ro) {
     const size_t dyn = std::max((size_t)ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H),
@@ -871,11 +885,11 @@ static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, 
         attr = true;
     }
     k_upgate_dec<GPW, FULL, WAVES><<<grid, 64 * WAVES, dyn, st>>>(
-        experts, estride, logits, E, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro);
+        experts, estride, logits, np, lbias, E, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro);
 }
 
-void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int E,
-                       int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
+void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* logits, int np,
+                       const float* lbias, int E, int k, int max_tiles, const uint16_t* x16, int T, int H, int I,
                        uint16_t* a16_perm, const float* shp, int Is, uint16_t* a_sh,
                        const RouteOut& ro, int n_cu, hipStream_t st) {
     const int max_items = max_tiles * (I / 16);
@@ -887,8 +901,8 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* log
     const int gpw = (NG + waves - 1) / waves;
     const bool full = NG == waves * gpw;
     shp = (Is > 0) ? shp : nullptr;
-#define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, logits, E, k, x16, T, H, \
-                                               I, a16_perm, shp, nkc, Is, a_sh, ro)
+#define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, logits, np, lbias, E, k, \
+                                               x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro)
     if (waves == 12) {
         if (gpw == 1) MOE_UGT(1, true, 12);
         else MOE_UGT(2, true, 12);
