@@ -28,6 +28,26 @@ NL4-32 block (32 weights, 18 bytes = 4.5 bits per weight)
                   little-endian stream (even i in the low nibble).
   value of weight i = d * T4[q_i] / 128  (exact in fp32).
 
+Two further codecs of the mixed-format layers of the same model (the model
+card, "Files / Main model": up/gate IQ2_S in 20 layers, down Q2_0 in 9; the
+page gives the type names only).  Readings taken here:
+
+Q2S-256 block (256 weights, 80 bytes = 2.5 bits per weight)
+  bytes [0, 64)   256 two-bit codebook indices, weight i at stream bits
+                  2i .. 2i+1 (little-endian stream as above).  Sub-block j
+                  is bytes [8j, 8j+8).
+  bytes [64, 66)  d, binary16.
+  bytes [66, 70)  eight signed 4-bit sub-scales, encoded as in Q3S-256.
+  bytes [70, 80)  reserved: writers store 0, readers ignore.
+  value of weight i = d * s_{i // 32} * C2[q_i] / 128  (exact in fp32).
+  The sign of the sub-scale mirrors the asymmetric codebook: this is the
+  "sign" of a 2-bit-plus-sign reading that fits the bit rate.
+
+Q2-32 block (32 weights, 10 bytes = 2.5 bits per weight)
+  bytes [0, 2)    d, binary16.
+  bytes [2, 10)   32 two-bit q, weight i at bits 2i .. 2i+1.
+  value of weight i = d * (q_i - 2)  (exact in fp32).
+
 Codebooks: sorted, distinct int8 levels placed at normal quantiles
 ("NF"-style), asymmetric with an exact zero: for a b-bit book with n = 2^b
 entries, p = 1 - 1/(2n); the n/2 positive levels are Phi^-1 at
@@ -38,7 +58,9 @@ the nearest integer.  The literals below are that rule's output, frozen.
 Matrix orientation: a weight matrix is stored as [out rows][in], blocks running
 along the reduction (input) dimension, so one block scale serves one dot
 product.  An expert record is up|gate = [2I][H] (rows 0..I-1 up, I..2I-1 gate)
-in Q3S-256, then down = [H][I] in NL4-32.
+in Q3S-256, then down = [H][I] in NL4-32.  The mixed-format layers store
+up|gate in Q3S-256, Q2S-256 or NL4-32 and down in NL4-32 or Q2-32, in the
+same order.
 """
 
 import numpy as np
@@ -48,11 +70,20 @@ Q3S_BLOCK_BYTES = 104
 Q3S_SUB_WEIGHTS = 32
 NL4_BLOCK_WEIGHTS = 32
 NL4_BLOCK_BYTES = 18
+Q2S_BLOCK_WEIGHTS = 256
+Q2S_BLOCK_BYTES = 80
+Q2S_SUB_WEIGHTS = 32
+Q2_BLOCK_WEIGHTS = 32
+Q2_BLOCK_BYTES = 10
 
 # 8-entry codebook of the 3.25-bpw up/gate codec (value = entry / 128).
 Q3S_CODEBOOK = (-127, -67, -31, 0, 23, 48, 78, 127)
 # 16-entry non-linear table of the 4-bit down codec (value = entry / 128).
 NL4_TABLE = (-127, -88, -66, -50, -36, -23, -11, 0, 10, 20, 31, 43, 56, 71, 91, 127)
+# 4-entry codebook of the 2.5-bpw up/gate codec (value = entry / 128).
+Q2S_CODEBOOK = (-127, 0, 54, 127)
+# Format numbers (the library's moe_format values).
+FMT_Q3S256, FMT_NL4_32, FMT_Q2S256, FMT_Q2_32 = 2, 3, 4, 5
 
 
 # --------------------------------------------------------------------------
@@ -165,6 +196,85 @@ def pack_nl4_block(d_bits, q):
     return bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF]) + stream.to_bytes(16, "little")
 
 
+def _subscales(v):
+    """Eight two's-complement nibbles of a u32, nibble j at bits 4j."""
+    out = []
+    for j in range(8):
+        nib = (v >> (4 * j)) & 0xF
+        out.append(nib - 16 if nib >= 8 else nib)
+    return out
+
+
+def unpack_q2s_block(block):
+    """Fields of one 80-byte Q2S-256 block: (d_bits, s[8], q[256])."""
+    block = bytes(block)
+    if len(block) != Q2S_BLOCK_BYTES:
+        raise ValueError("Q2S-256 block must be 80 bytes")
+    bits = _bit_stream(block[0:64])
+    q = [bits[2 * i] | (bits[2 * i + 1] << 1) for i in range(Q2S_BLOCK_WEIGHTS)]
+    d_bits = block[64] | (block[65] << 8)
+    v = block[66] | (block[67] << 8) | (block[68] << 16) | (block[69] << 24)
+    return d_bits, _subscales(v), q
+
+
+def dequant_q2s_block(block):
+    """256 weight values of one Q2S-256 block (Python floats, exact)."""
+    d_bits, s, q = unpack_q2s_block(block)
+    d = fp16_bits_to_float(d_bits)
+    return [d * s[i // Q2S_SUB_WEIGHTS] * Q2S_CODEBOOK[q[i]] / 128.0
+            for i in range(Q2S_BLOCK_WEIGHTS)]
+
+
+def pack_q2s_block(d_bits, s, q):
+    """Bytes of one Q2S-256 block from its fields (reserved bytes zero)."""
+    if len(s) != 8 or len(q) != Q2S_BLOCK_WEIGHTS:
+        raise ValueError("need 8 sub-scales and 256 indices")
+    stream = 0
+    for i, qi in enumerate(q):
+        if not 0 <= qi < 4:
+            raise ValueError("index out of range")
+        stream |= int(qi) << (2 * i)
+    out = bytearray(stream.to_bytes(64, "little"))
+    out += bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF])
+    v = 0
+    for j, sj in enumerate(s):
+        if not -8 <= sj <= 7:
+            raise ValueError("sub-scale out of range")
+        v |= (int(sj) & 0xF) << (4 * j)
+    out += v.to_bytes(4, "little")
+    out += bytes(10)
+    return bytes(out)
+
+
+def unpack_q2_block(block):
+    """Fields of one 10-byte Q2-32 block: (d_bits, q[32])."""
+    block = bytes(block)
+    if len(block) != Q2_BLOCK_BYTES:
+        raise ValueError("Q2-32 block must be 10 bytes")
+    d_bits = block[0] | (block[1] << 8)
+    bits = _bit_stream(block[2:10])
+    return d_bits, [bits[2 * i] | (bits[2 * i + 1] << 1) for i in range(Q2_BLOCK_WEIGHTS)]
+
+
+def dequant_q2_block(block):
+    """32 weight values of one Q2-32 block (Python floats, exact)."""
+    d_bits, q = unpack_q2_block(block)
+    d = fp16_bits_to_float(d_bits)
+    return [d * (qi - 2) for qi in q]
+
+
+def pack_q2_block(d_bits, q):
+    """Bytes of one Q2-32 block from its fields."""
+    if len(q) != Q2_BLOCK_WEIGHTS:
+        raise ValueError("need 32 indices")
+    stream = 0
+    for i, qi in enumerate(q):
+        if not 0 <= qi < 4:
+            raise ValueError("index out of range")
+        stream |= int(qi) << (2 * i)
+    return bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF]) + stream.to_bytes(8, "little")
+
+
 # --------------------------------------------------------------------------
 # vectorised (NumPy) codecs; pinned bit-exactly against the scalar ones
 # --------------------------------------------------------------------------
@@ -215,6 +325,43 @@ def dequant_nl4(arr):
     return d[..., None] * t / 128.0
 
 
+def unpack_q2s(arr):
+    """Vectorised Q2S-256 unpack: (d float64 [...], s int64 [..., 8],
+    q int64 [..., 256])."""
+    a = _as_blocks(arr, Q2S_BLOCK_BYTES)
+    bits = np.unpackbits(a[..., 0:64], axis=-1, bitorder="little")
+    bits = bits.reshape(a.shape[:-1] + (Q2S_BLOCK_WEIGHTS, 2)).astype(np.int64)
+    q = bits[..., 0] | (bits[..., 1] << 1)
+    d = np.ascontiguousarray(a[..., 64:66]).view("<f2")[..., 0].astype(np.float64)
+    v = np.ascontiguousarray(a[..., 66:70]).view("<u4")[..., 0].astype(np.int64)
+    s = np.stack([(v >> (4 * j)) & 0xF for j in range(8)], axis=-1)
+    s = np.where(s >= 8, s - 16, s)
+    return d, s, q
+
+
+def dequant_q2s(arr):
+    """Vectorised Q2S-256 dequant: float64 [..., 256] per block."""
+    d, s, q = unpack_q2s(arr)
+    c = np.asarray(Q2S_CODEBOOK, dtype=np.float64)[q]
+    sw = np.repeat(s, Q2S_SUB_WEIGHTS, axis=-1).astype(np.float64)
+    return d[..., None] * sw * c / 128.0
+
+
+def unpack_q2(arr):
+    """Vectorised Q2-32 unpack: (d float64 [...], q int64 [..., 32])."""
+    a = _as_blocks(arr, Q2_BLOCK_BYTES)
+    d = np.ascontiguousarray(a[..., 0:2]).view("<f2")[..., 0].astype(np.float64)
+    b = a[..., 2:10].astype(np.int64)
+    q = np.stack([(b >> (2 * t)) & 3 for t in range(4)], axis=-1).reshape(a.shape[:-1] + (Q2_BLOCK_WEIGHTS,))
+    return d, q
+
+
+def dequant_q2(arr):
+    """Vectorised Q2-32 dequant: float64 [..., 32] per block."""
+    d, q = unpack_q2(arr)
+    return d[..., None] * (q - 2).astype(np.float64)
+
+
 def dequant_q3s_matrix(raw, rows, cols):
     """Dequantise a Q3S-256 matrix stored [rows][cols] (cols % 256 == 0)."""
     nb = cols // Q3S_BLOCK_WEIGHTS
@@ -227,6 +374,34 @@ def dequant_nl4_matrix(raw, rows, cols):
     nb = cols // NL4_BLOCK_WEIGHTS
     a = np.asarray(raw, dtype=np.uint8).reshape(rows, nb, NL4_BLOCK_BYTES)
     return dequant_nl4(a).reshape(rows, cols)
+
+
+def pack_q2s(d_bits, s, q):
+    """Vectorised pack: d_bits uint16 [...], s int [..., 8], q int [..., 256]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    s = np.asarray(s, dtype=np.int64)
+    q = np.asarray(q, dtype=np.int64)
+    lead = d_bits.shape
+    out = np.zeros(lead + (Q2S_BLOCK_BYTES,), dtype=np.uint8)
+    bits = np.stack([(q >> b) & 1 for b in range(2)], axis=-1).reshape(lead + (512,))
+    out[..., 0:64] = np.packbits(bits.astype(np.uint8), axis=-1, bitorder="little")
+    out[..., 64:66] = d_bits[..., None].view(np.uint8).reshape(lead + (2,))
+    v = np.zeros(lead, dtype=np.uint32)
+    for j in range(8):
+        v |= ((s[..., j] & 0xF).astype(np.uint32) << np.uint32(4 * j))
+    out[..., 66:70] = v.astype("<u4")[..., None].view(np.uint8).reshape(lead + (4,))
+    return out
+
+
+def pack_q2(d_bits, q):
+    """Vectorised pack: d_bits uint16 [...], q int [..., 32]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    q = np.asarray(q, dtype=np.int64).reshape(d_bits.shape + (8, 4))
+    lead = d_bits.shape
+    out = np.zeros(lead + (Q2_BLOCK_BYTES,), dtype=np.uint8)
+    out[..., 0:2] = d_bits[..., None].view(np.uint8).reshape(lead + (2,))
+    out[..., 2:10] = (q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)).astype(np.uint8)
+    return out
 
 
 def pack_q3s(d_bits, s, q):
@@ -305,6 +480,41 @@ def quantize_nl4(w):
     return pack_nl4(d_bits, q)
 
 
+def quantize_q2s(w):
+    """Round-to-nearest Q2S-256 encoding of weights w [..., 256]: the Q3S-256
+    rule with the codebook C2 (sigma_j = absmax_j / (max|C2|/128), d =
+    fp16_RNE(max_j sigma_j / 7), s_j = clamp(round_half_even(sigma_j / d),
+    -8, 7), q_i nearest, ties to the lower index; d = 0 gives s = q = 0).
+    Returns uint8 [..., 80]."""
+    w = np.asarray(w, dtype=np.float64)
+    lead = w.shape[:-1]
+    sub = w.reshape(lead + (8, Q2S_SUB_WEIGHTS))
+    cmax = max(abs(c) for c in Q2S_CODEBOOK) / 128.0
+    sigma = np.abs(sub).max(axis=-1) / cmax
+    d_bits = _fp16_rne_bits(sigma.max(axis=-1) / 7.0)
+    d = d_bits.view(np.float16).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = np.where(d[..., None] > 0, np.rint(sigma / d[..., None]), 0.0)
+    s = np.clip(s, -8, 7).astype(np.int64)
+    cands = (d[..., None, None] * s[..., None].astype(np.float64)
+             * np.asarray(Q2S_CODEBOOK, dtype=np.float64) / 128.0)
+    dist = np.abs(sub[..., None] - cands[..., None, :])
+    q = np.argmin(dist, axis=-1).reshape(lead + (Q2S_BLOCK_WEIGHTS,))
+    return pack_q2s(d_bits, s, q)
+
+
+def quantize_q2(w):
+    """Round-to-nearest Q2-32 encoding of weights w [..., 32]: d =
+    fp16_RNE(absmax / 2) (the levels are d * {-2, -1, 0, 1}); q_i = the level
+    nearest w_i, ties to the lower index.  Returns uint8 [..., 10]."""
+    w = np.asarray(w, dtype=np.float64)
+    d_bits = _fp16_rne_bits(np.abs(w).max(axis=-1) / 2.0)
+    d = d_bits.view(np.float16).astype(np.float64)
+    cands = d[..., None] * np.arange(-2, 2, dtype=np.float64)
+    q = np.argmin(np.abs(w[..., None] - cands[..., None, :]), axis=-1)
+    return pack_q2(d_bits, q)
+
+
 def quantize_q3s_matrix(w):
     """Quantise a matrix [rows][cols] (cols % 256 == 0) to Q3S-256 bytes
     [rows][cols/256*104]."""
@@ -324,51 +534,85 @@ def quantize_nl4_matrix(w):
 
 
 # --------------------------------------------------------------------------
-# expert records: up|gate (Q3S-256, [2I][H]) then down (NL4-32, [H][I])
+# any of the four codecs by format number
 # --------------------------------------------------------------------------
 
-def upgate_bytes(hidden, inter):
-    return 2 * inter * (hidden // Q3S_BLOCK_WEIGHTS) * Q3S_BLOCK_BYTES
+# format -> (weights per block, bytes per block, vectorised dequant,
+#            scalar block dequant, round-to-nearest quantiser)
+CODECS = {
+    FMT_Q3S256: (Q3S_BLOCK_WEIGHTS, Q3S_BLOCK_BYTES, dequant_q3s, dequant_q3s_block, quantize_q3s),
+    FMT_NL4_32: (NL4_BLOCK_WEIGHTS, NL4_BLOCK_BYTES, dequant_nl4, dequant_nl4_block, quantize_nl4),
+    FMT_Q2S256: (Q2S_BLOCK_WEIGHTS, Q2S_BLOCK_BYTES, dequant_q2s, dequant_q2s_block, quantize_q2s),
+    FMT_Q2_32: (Q2_BLOCK_WEIGHTS, Q2_BLOCK_BYTES, dequant_q2, dequant_q2_block, quantize_q2),
+}
+UPGATE_FORMATS = (FMT_Q3S256, FMT_Q2S256, FMT_NL4_32)
+DOWN_FORMATS = (FMT_NL4_32, FMT_Q2_32)
 
 
-def down_bytes(hidden, inter):
-    return hidden * (inter // NL4_BLOCK_WEIGHTS) * NL4_BLOCK_BYTES
+def matrix_bytes(fmt, rows, cols):
+    nw, nb = CODECS[fmt][:2]
+    return rows * (cols // nw) * nb
 
 
-def expert_record_bytes(hidden, inter):
-    return upgate_bytes(hidden, inter) + down_bytes(hidden, inter)
+def dequant_matrix(fmt, raw, rows, cols):
+    """Dequantise a matrix stored [rows][cols] in format fmt."""
+    nw, nb, deq = CODECS[fmt][:3]
+    a = np.asarray(raw, dtype=np.uint8).reshape(rows, cols // nw, nb)
+    return deq(a).reshape(rows, cols)
 
 
-def expert_matrices(record, hidden, inter):
+def quantize_matrix(fmt, w):
+    """Round-to-nearest encoding of a matrix [rows][cols] in format fmt."""
+    nw, nb, _, _, quant = CODECS[fmt]
+    w = np.asarray(w, dtype=np.float64)
+    rows, cols = w.shape
+    return quant(w.reshape(rows, cols // nw, nw)).reshape(rows, -1)
+
+
+# --------------------------------------------------------------------------
+# expert records: up|gate ([2I][H]) then down ([H][I]); Q3S-256 and NL4-32
+# unless other formats are given
+# --------------------------------------------------------------------------
+
+def upgate_bytes(hidden, inter, fmt=FMT_Q3S256):
+    return matrix_bytes(fmt, 2 * inter, hidden)
+
+
+def down_bytes(hidden, inter, fmt=FMT_NL4_32):
+    return matrix_bytes(fmt, hidden, inter)
+
+
+def expert_record_bytes(hidden, inter, ug_fmt=FMT_Q3S256, dn_fmt=FMT_NL4_32):
+    return upgate_bytes(hidden, inter, ug_fmt) + down_bytes(hidden, inter, dn_fmt)
+
+
+def expert_matrices(record, hidden, inter, ug_fmt=FMT_Q3S256, dn_fmt=FMT_NL4_32):
     """Dequantised (W_up [I][H], W_gate [I][H], W_down [H][I]) of one packed
     expert record (uint8, length >= expert_record_bytes)."""
     rec = np.asarray(record, dtype=np.uint8).reshape(-1)
-    nug = upgate_bytes(hidden, inter)
-    ug = dequant_q3s_matrix(rec[:nug], 2 * inter, hidden)
-    dn = dequant_nl4_matrix(rec[nug:nug + down_bytes(hidden, inter)], hidden, inter)
+    nug = upgate_bytes(hidden, inter, ug_fmt)
+    ug = dequant_matrix(ug_fmt, rec[:nug], 2 * inter, hidden)
+    dn = dequant_matrix(dn_fmt, rec[nug:nug + down_bytes(hidden, inter, dn_fmt)], hidden, inter)
     return ug[:inter], ug[inter:], dn
 
 
-def expert_matrices_scalar(record, hidden, inter):
+def _matrix_scalar(fmt, rec, base, rows, cols):
+    nw, nb, _, deq_block, _ = CODECS[fmt]
+    nbr = cols // nw
+    out = []
+    for r in range(rows):
+        row = []
+        for b in range(nbr):
+            off = base + (r * nbr + b) * nb
+            row.extend(deq_block(rec[off:off + nb]))
+        out.append(row)
+    return np.array(out, dtype=np.float64)
+
+
+def expert_matrices_scalar(record, hidden, inter, ug_fmt=FMT_Q3S256, dn_fmt=FMT_NL4_32):
     """Same as expert_matrices, block by block with the scalar decoders (slow;
     for tiny shapes and sampled checks)."""
     rec = bytes(np.asarray(record, dtype=np.uint8).reshape(-1))
-    nbu = hidden // Q3S_BLOCK_WEIGHTS
-    ug = []
-    for r in range(2 * inter):
-        row = []
-        for b in range(nbu):
-            off = (r * nbu + b) * Q3S_BLOCK_BYTES
-            row.extend(dequant_q3s_block(rec[off:off + Q3S_BLOCK_BYTES]))
-        ug.append(row)
-    base = upgate_bytes(hidden, inter)
-    nbd = inter // NL4_BLOCK_WEIGHTS
-    dn = []
-    for r in range(hidden):
-        row = []
-        for b in range(nbd):
-            off = base + (r * nbd + b) * NL4_BLOCK_BYTES
-            row.extend(dequant_nl4_block(rec[off:off + NL4_BLOCK_BYTES]))
-        dn.append(row)
-    ug = np.array(ug, dtype=np.float64)
-    return ug[:inter], ug[inter:], np.array(dn, dtype=np.float64)
+    ug = _matrix_scalar(ug_fmt, rec, 0, 2 * inter, hidden)
+    dn = _matrix_scalar(dn_fmt, rec, upgate_bytes(hidden, inter, ug_fmt), hidden, inter)
+    return ug[:inter], ug[inter:], dn

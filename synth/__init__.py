@@ -32,6 +32,13 @@ particular range are overwritten bit-wise --
   negative sub-scales included); bytes 102..103 = 0.
   NL4-32 block: d (bytes 0..1) = 0x2800 | 10 random bits, a binary16 in
   [2^-5, 2^-4); index bytes uniform random.
+  Q2S-256 block (mixed-format layers): index bytes [0,64) uniform random; d
+  (bytes 64..65) = 0x1C00 | 10 random bits, in [2^-8, 2^-7); sub-scale bytes
+  66..69 as for Q3S-256; bytes 70..79 = 0.
+  Q2-32 block: d (bytes 0..1) = 0x2400 | 10 random bits, in [2^-6, 2^-5);
+  index bytes uniform random.
+  (Each d range is the one a round-to-nearest encoding of N(0, 0.02) weights
+  gives for that codec.)
 The counter hash is MurmurHash3's 32-bit finaliser (fmix32, Austin Appleby,
 public domain), applied twice with per-(seed, layer, expert) keys.
 """
@@ -47,6 +54,13 @@ import torch
 
 Q3S_BLOCK_BYTES = 104     # field widths of the codecs (byte layout only)
 NL4_BLOCK_BYTES = 18
+Q2S_BLOCK_BYTES = 80
+Q2_BLOCK_BYTES = 10
+# format number -> (weights per block, bytes per block); the numbers are the
+# library's moe_format values
+FMT_Q3S256, FMT_NL4_32, FMT_Q2S256, FMT_Q2_32 = 2, 3, 4, 5
+BLOCKS = {FMT_Q3S256: (256, Q3S_BLOCK_BYTES), FMT_NL4_32: (32, NL4_BLOCK_BYTES),
+          FMT_Q2S256: (256, Q2S_BLOCK_BYTES), FMT_Q2_32: (32, Q2_BLOCK_BYTES)}
 
 # Router-bias strength.  b_e = -ZIPF_ALPHA * s * ln(rank_e).  Chosen once by
 # bisection on the 8192-token prefill workload (seed 3, s = 1.0) so that the
@@ -62,14 +76,18 @@ class Shape:
     n_experts: int
     top_k: int
     shared_inter: int          # 0 = no shared expert
+    upgate_fmt: int = FMT_Q3S256
+    down_fmt: int = FMT_NL4_32
 
     @property
     def upgate_bytes(self):
-        return 2 * self.inter * (self.hidden // 256) * Q3S_BLOCK_BYTES
+        nw, nb = BLOCKS[self.upgate_fmt]
+        return 2 * self.inter * (self.hidden // nw) * nb
 
     @property
     def down_bytes(self):
-        return self.hidden * (self.inter // 32) * NL4_BLOCK_BYTES
+        nw, nb = BLOCKS[self.down_fmt]
+        return self.hidden * (self.inter // nw) * nb
 
     @property
     def expert_bytes(self):
@@ -168,13 +186,39 @@ def _fix_nl4_fields(blk):
     blk[:, 1] = (blk[:, 1] & 0x03) | 0x28
 
 
+def _fix_q2s_fields(blk, mode):
+    """blk: uint8 [n, 80] view; set d, sub-scale and reserved fields."""
+    blk[:, 65] = (blk[:, 65] & 0x03) | 0x1C
+    if mode == "rtn":
+        blk[:, 66:70] = (blk[:, 66:70] & 0x33) | 0x44
+    elif mode != "full":
+        raise ValueError("mode must be 'rtn' or 'full'")
+    blk[:, 70:80] = 0
+
+
+def _fix_q2_fields(blk):
+    blk[:, 1] = (blk[:, 1] & 0x03) | 0x24
+
+
+def _fix_fields(fmt, raw, mode):
+    blk = raw.view(-1, BLOCKS[fmt][1])
+    if fmt == FMT_Q3S256:
+        _fix_q3s_fields(blk, mode)
+    elif fmt == FMT_Q2S256:
+        _fix_q2s_fields(blk, mode)
+    elif fmt == FMT_NL4_32:
+        _fix_nl4_fields(blk)
+    else:
+        _fix_q2_fields(blk)
+
+
 def expert_record(shape, seed, layer, e, device="cpu", mode="rtn"):
     """Packed bytes (uint8 [expert_bytes]) of expert e of a layer."""
     k1 = key(seed, layer, 2 * e + 1)
     k2 = key(seed, layer, 2 * e + 2)
     rec = hash_bytes(k1, k2, shape.expert_bytes, device).clone()
-    _fix_q3s_fields(rec[:shape.upgate_bytes].view(-1, Q3S_BLOCK_BYTES), mode)
-    _fix_nl4_fields(rec[shape.upgate_bytes:].view(-1, NL4_BLOCK_BYTES))
+    _fix_fields(shape.upgate_fmt, rec[:shape.upgate_bytes], mode)
+    _fix_fields(shape.down_fmt, rec[shape.upgate_bytes:], mode)
     return rec
 
 

@@ -56,7 +56,8 @@ class ExpertCache:
     def __call__(self, e):
         if e not in self.cache:
             rec = self.record_fn(e)
-            self.cache[e] = OF.expert_matrices(rec, self.shape.hidden, self.shape.inter)
+            self.cache[e] = OF.expert_matrices(rec, self.shape.hidden, self.shape.inter,
+                                               self.shape.upgate_fmt, self.shape.down_fmt)
         return self.cache[e]
 
 

@@ -277,3 +277,177 @@ def test_matrix_helpers_and_expert_record():
     assert np.array_equal(up, up2) and np.array_equal(gate, gate2) and np.array_equal(down, down2)
     # quantisation error is small relative to the weights (RTN sanity)
     assert np.abs(np.concatenate([up, gate]) - wug).max() < 0.25 * np.abs(wug).max()
+
+
+# ---------------------------------------------------------------- the 2-bit codecs
+# (mixed-format layers of the same model card: up/gate IQ2_S, down Q2_0; the
+# layouts are readings, pinned by construction like the two codecs above)
+
+@pytest.mark.parametrize("case", GOLD["q2s_index_stream"])
+def test_q2s_index_stream_known_answer(case):
+    q = list(case["indices_first8"]) + [0] * 248
+    blk = F.pack_q2s_block(0, [0] * 8, q)
+    assert _hex(blk[:2]) == case["bytes_hex"]
+    assert F.unpack_q2s_block(blk)[2][:8] == case["indices_first8"]
+
+
+@pytest.mark.parametrize("case", GOLD["q2s_fields"])
+def test_q2s_field_offsets(case):
+    blk = F.pack_q2s_block(int(case["d_bits"], 16), case["s"], [0] * 256)
+    assert len(blk) == F.Q2S_BLOCK_BYTES == 80
+    assert _hex(blk[64:80]) == case["bytes_64_80_hex"]
+    d_bits, s, _ = F.unpack_q2s_block(blk)
+    assert d_bits == int(case["d_bits"], 16) and s == case["s"]
+
+
+@pytest.mark.parametrize("case", GOLD["q2s_values"])
+def test_q2s_known_values(case):
+    blk = F.pack_q2s_block(int(case["d_bits"], 16), [case["s"]] * 8, [case["q"]] * 256)
+    assert all(v == case["value"] for v in F.dequant_q2s_block(blk))
+    assert np.all(F.dequant_q2s(np.frombuffer(blk, np.uint8)[None]) == case["value"])
+
+
+@pytest.mark.parametrize("case", GOLD["q2_index_stream"])
+def test_q2_index_stream_known_answer(case):
+    blk = F.pack_q2_block(0, list(case["indices_first4"]) + [0] * 28)
+    assert len(blk) == F.Q2_BLOCK_BYTES == 10
+    assert _hex(blk[2:3]) == case["byte2_hex"]
+
+
+@pytest.mark.parametrize("case", GOLD["q2_values"])
+def test_q2_known_values(case):
+    blk = F.pack_q2_block(int(case["d_bits"], 16), [case["q"]] * 32)
+    assert all(v == case["value"] for v in F.dequant_q2_block(blk))
+    assert np.all(F.dequant_q2(np.frombuffer(blk, np.uint8)[None]) == case["value"])
+
+
+def test_q2s_codebook_follows_stated_rule():
+    assert F.Q2S_CODEBOOK == _nf_rule(2)
+    book = F.Q2S_CODEBOOK
+    assert list(book) == sorted(set(book)) and 0 in book
+    assert sum(1 for c in book if c < 0) == len(book) // 2 - 1
+
+
+def test_q2s_every_index_and_subscale_position():
+    s = [-8, -1, 0, 1, 7, 2, -3, 5]
+    q = [(i * 7 + i // 32) % 4 for i in range(256)]
+    blk = F.pack_q2s_block(0x3C00, s, q)
+    vals = F.dequant_q2s_block(blk)
+    for i in range(256):
+        assert vals[i] == s[i // 32] * F.Q2S_CODEBOOK[q[i]] / 128.0
+
+
+def test_q2_every_position():
+    q = [(5 * i + 1) % 4 for i in range(32)]
+    vals = F.dequant_q2_block(F.pack_q2_block(0x3800, q))
+    assert vals == [0.5 * (qi - 2) for qi in q]
+
+
+def _random_q2s_blocks(rng, n):
+    blk = rng.integers(0, 256, size=(n, F.Q2S_BLOCK_BYTES), dtype=np.uint8)
+    blk[:, 65] = (blk[:, 65] & 0x83) | 0x20          # finite d of either sign
+    return blk
+
+
+def test_vectorised_matches_scalar_q2s():
+    rng = np.random.default_rng(11)
+    blocks = _random_q2s_blocks(rng, 40)
+    vec = F.dequant_q2s(blocks)
+    for b in range(len(blocks)):
+        assert list(vec[b]) == F.dequant_q2s_block(bytes(blocks[b]))
+        d_bits, s, q = F.unpack_q2s_block(bytes(blocks[b]))
+        d2, s2, q2 = F.unpack_q2s(blocks[b][None])
+        assert list(s2[0]) == s and list(q2[0]) == q
+
+
+def test_vectorised_matches_scalar_q2():
+    rng = np.random.default_rng(12)
+    blocks = rng.integers(0, 256, size=(60, F.Q2_BLOCK_BYTES), dtype=np.uint8)
+    blocks[:, 1] = (blocks[:, 1] & 0x83) | 0x28
+    vec = F.dequant_q2(blocks)
+    for b in range(len(blocks)):
+        assert list(vec[b]) == F.dequant_q2_block(bytes(blocks[b]))
+
+
+def test_2bit_dequant_is_exact_in_fp32():
+    rng = np.random.default_rng(13)
+    for v in F.dequant_q2s(_random_q2s_blocks(rng, 30)).ravel():
+        assert float(np.float32(v)) == v
+    blocks = rng.integers(0, 256, size=(30, F.Q2_BLOCK_BYTES), dtype=np.uint8)
+    for v in F.dequant_q2(blocks).ravel():
+        if np.isfinite(v):
+            assert float(np.float32(v)) == v
+
+
+def test_2bit_packers_roundtrip_fields():
+    rng = np.random.default_rng(14)
+    d = rng.integers(0, 0x7C00, size=5).astype(np.uint16)
+    s = rng.integers(-8, 8, size=(5, 8))
+    q = rng.integers(0, 4, size=(5, 256))
+    vec = F.pack_q2s(d, s, q)
+    for b in range(5):
+        assert bytes(vec[b]) == F.pack_q2s_block(int(d[b]), list(s[b]), list(q[b]))
+    q2 = rng.integers(0, 4, size=(5, 32))
+    vec2 = F.pack_q2(d, q2)
+    for b in range(5):
+        assert bytes(vec2[b]) == F.pack_q2_block(int(d[b]), list(q2[b]))
+        assert F.unpack_q2_block(bytes(vec2[b])) == (int(d[b]), list(q2[b]))
+
+
+def test_q2s_quantiser_on_grid_roundtrip():
+    """Weights on the grid of one block (d, s fixed; each sub-block holds the
+    largest codebook entry so the rule recovers s) come back bit for bit."""
+    d_bits = 0x2400
+    d = float(np.uint16(d_bits).view(np.float16))
+    s = [7, 3, 1, 7, 5, 2, 6, 4]
+    rng = np.random.default_rng(15)
+    q = rng.integers(0, 4, size=256)
+    q[::32] = 3
+    w = np.array([d * s[i // 32] * F.Q2S_CODEBOOK[q[i]] / 128.0 for i in range(256)])
+    blk = F.quantize_q2s(w)
+    d2, s2, q2 = F.unpack_q2s_block(bytes(blk))
+    assert (d2, s2, q2) == (d_bits, s, list(q))
+
+
+def test_q2s_quantiser_is_nearest_brute_force():
+    rng = np.random.default_rng(16)
+    w = rng.normal(0, 0.02, size=(6, 256))
+    blks = F.quantize_q2s(w)
+    for b in range(6):
+        d_bits, s, q = F.unpack_q2s_block(bytes(blks[b]))
+        d = F.fp16_bits_to_float(d_bits)
+        for i in range(256):
+            lv = [d * s[i // 32] * c / 128.0 for c in F.Q2S_CODEBOOK]
+            best = min(range(4), key=lambda t: (abs(w[b, i] - lv[t]), t))
+            assert q[i] == best
+
+
+def test_q2_quantiser_is_nearest_brute_force():
+    rng = np.random.default_rng(17)
+    w = rng.normal(0, 0.02, size=(8, 32))
+    blks = F.quantize_q2(w)
+    for b in range(8):
+        d_bits, q = F.unpack_q2_block(bytes(blks[b]))
+        d = F.fp16_bits_to_float(d_bits)
+        assert d_bits == int(np.float16(np.abs(w[b]).max() / 2).view(np.uint16))
+        for i in range(32):
+            best = min(range(4), key=lambda t: (abs(w[b, i] - d * (t - 2)), t))
+            assert q[i] == best
+
+
+@pytest.mark.parametrize("ug,dn", [(F.FMT_Q2S256, F.FMT_Q2_32), (F.FMT_NL4_32, F.FMT_NL4_32),
+                                   (F.FMT_Q3S256, F.FMT_Q2_32)])
+def test_mixed_expert_record(ug, dn):
+    """Record layout for other format pairs: up|gate then down; the matrix
+    helpers agree with the scalar block decoders."""
+    H, I = 256, 64
+    rng = np.random.default_rng(18)
+    wug = rng.normal(0, 0.02, size=(2 * I, H))
+    wdn = rng.normal(0, 0.02, size=(H, I))
+    rec = np.concatenate([F.quantize_matrix(ug, wug).ravel(), F.quantize_matrix(dn, wdn).ravel()])
+    assert rec.size == F.expert_record_bytes(H, I, ug, dn)
+    a = F.expert_matrices(rec, H, I, ug, dn)
+    b = F.expert_matrices_scalar(rec, H, I, ug, dn)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    assert np.array_equal(np.concatenate([a[0], a[1]]), F.dequant_matrix(ug, F.quantize_matrix(ug, wug), 2 * I, H))
