@@ -76,18 +76,34 @@ typedef enum {
  *                  nibble.  w_i = d * T4[q_i] / 128 with T4 = {-127,-88,-66,
  *                  -50,-36,-23,-11,0,10,20,31,43,56,71,91,127}.  (Model card,
  *                  "Files / Main model": IQ4_NL down tensors.)
+ *  MOE_FMT_Q2S256  2.5-bpw super-blocks of 256 weights, 80 bytes each: [0,64)
+ *                  256 2-bit indices (weight i at bits 2i..2i+1 of the
+ *                  little-endian stream); [64,66) fp16 d; [66,70) eight signed
+ *                  4-bit sub-scales as in Q3S256; [70,80) reserved (ignored).
+ *                  w_i = d * s_{i/32} * C2[q_i] / 128, C2 = {-127,0,54,127}.
+ *                  (A reading of the model card's IQ2_S up/gate layers, which
+ *                  the page names only.)
+ *  MOE_FMT_Q2_32   2-bit 32-weight blocks, 10 bytes each: [0,2) fp16 d;
+ *                  [2,10) 32 2-bit q (weight i at bits 2i..2i+1).  w_i =
+ *                  d * (q_i - 2).  (A reading of the model card's Q2_0 down
+ *                  layers, which the page names only.)
  * Matrices are stored [out rows][in] with blocks along the input dimension. */
 typedef enum {
     MOE_FMT_BF16 = 1,
     MOE_FMT_Q3S256 = 2,
-    MOE_FMT_NL4_32 = 3
+    MOE_FMT_NL4_32 = 3,
+    MOE_FMT_Q2S256 = 4,
+    MOE_FMT_Q2_32 = 5
 } moe_format;
 
 /* Layer shape.  Supported: hidden % 256 == 0 (and <= 8192); inter % 64 == 0
  * (and <= 4096); 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
  * shared_inter == 0 (no shared expert) or shared_inter % 64 == 0 (<= 4096);
- * upgate_fmt == MOE_FMT_Q3S256 and down_fmt == MOE_FMT_NL4_32 for the routed
- * experts (the shared expert and the router are always bf16). */
+ * routed up|gate in MOE_FMT_Q3S256, MOE_FMT_Q2S256 or MOE_FMT_NL4_32 and
+ * routed down in MOE_FMT_NL4_32 or MOE_FMT_Q2_32 (the mixed-format layers of
+ * the model card use all five combinations' parts); the shared expert and the
+ * router are always bf16.  Batches of T <= 16 tokens with Q3S256 / NL4_32
+ * experts take the bandwidth kernels; every other case the grouped GEMMs. */
 typedef struct {
     int32_t hidden;        /* H                                              */
     int32_t inter;         /* I, routed expert intermediate size             */
@@ -187,10 +203,11 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
                                    size_t ws_bytes, void* stream, void* const* events,
                                    int32_t n_events, int32_t* n_marks);
 
-/* Helper, not the method: dequantize n_weights weights of one format (a whole
- * number of blocks, contiguous) to fp32 `out`, with the same device decoders
- * the FFN kernels inline.  Exact: equal bit for bit to d*s*c/128 (Q3S256) or
- * d*t/128 (NL4_32).  blocks must be 16-byte aligned. */
+/* Helper, not the method: dequantize n_weights weights of one quantized format
+ * (Q3S256, NL4_32, Q2S256 or Q2_32; a whole number of blocks, contiguous) to
+ * fp32 `out` with per-block device decoders.  Exact: equal bit for bit to
+ * d*s*c/128 (Q3S256, Q2S256), d*t/128 (NL4_32) or d*(q-2) (Q2_32).  blocks
+ * must be 16-byte aligned. */
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
                           void* stream);
 

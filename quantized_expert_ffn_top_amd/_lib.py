@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_FMT_BF16 = 1
 MOE_FMT_Q3S256 = 2
 MOE_FMT_NL4_32 = 3
+MOE_FMT_Q2S256 = 4
+MOE_FMT_Q2_32 = 5
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_HIP"}
@@ -106,9 +108,9 @@ def _u16(t):
     return t
 
 
-def desc(hidden, inter, n_experts, top_k, shared_inter=0):
-    return LayerDesc(hidden, inter, n_experts, top_k, shared_inter, MOE_FMT_Q3S256,
-                     MOE_FMT_NL4_32)
+def desc(hidden, inter, n_experts, top_k, shared_inter=0, upgate_fmt=MOE_FMT_Q3S256,
+         down_fmt=MOE_FMT_NL4_32):
+    return LayerDesc(hidden, inter, n_experts, top_k, shared_inter, upgate_fmt, down_fmt)
 
 
 def weights(experts, expert_stride, router_w=None, router_b=None, shared_upgate=None,

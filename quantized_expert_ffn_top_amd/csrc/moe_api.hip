@@ -63,9 +63,15 @@ struct Ws {
     int max_tiles;
 };
 
-// The layer runs the bandwidth path for T <= kDecMaxT tokens when its up|gate
-// kernel can stage two items of the hidden size; otherwise the grouped GEMMs.
-bool dec_path(int T, int H, int E) { return T <= kDecMaxT && upgate_dec_supported(H, T, E); }
+// The layer runs the bandwidth path for T <= kDecMaxT tokens when its experts
+// are Q3S-256 up|gate and NL4-32 down and its up|gate kernel can stage two
+// items of the hidden size; otherwise the grouped GEMMs.
+bool std_formats(const moe_layer_desc* d) {
+    return d->upgate_fmt == MOE_FMT_Q3S256 && d->down_fmt == MOE_FMT_NL4_32;
+}
+bool dec_path(int T, int H, int E, bool std_fmt) {
+    return std_fmt && T <= kDecMaxT && upgate_dec_supported(H, T, E);
+}
 
 // tiles of the expert kernels: one per active expert (bandwidth path) or per
 // kGemmBM rows of an expert (grouped GEMM)
@@ -75,7 +81,7 @@ int max_tiles_for(int T, int E, int k, bool dec) {
     return (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
 }
 
-Ws layout(int H, int I, int E, int k, int Is, int T) {
+Ws layout(int H, int I, int E, int k, int Is, int T, bool std_fmt) {
     Ws s{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -85,10 +91,11 @@ Ws layout(int H, int I, int E, int k, int Is, int T) {
     };
     const size_t n = (size_t)T * k;
     const int tdec = T < kDecMaxT ? T : kDecMaxT;
-    s.max_tiles = max_tiles_for(T, E, k, dec_path(T, H, E));
+    const bool dec = dec_path(T, H, E, std_fmt);
+    s.max_tiles = max_tiles_for(T, E, k, dec);
     s.x16 = take((size_t)T * H * 2);
     s.shp = take((size_t)(H / kShKChunk) * tdec * 2 * (Is > 0 ? Is : 1) * 4);
-    s.logits = take((size_t)(dec_path(T, H, E) ? kDecLogitParts : 1) * T * E * 4);
+    s.logits = take((size_t)(dec ? kDecLogitParts : 1) * T * E * 4);
     s.ids = take(n * 4);
     s.w = take(n * 4);
     s.offsets = take((size_t)(E + 1) * 4);
@@ -118,13 +125,20 @@ moe_status check_desc(const moe_layer_desc* d) {
         return fail(MOE_ERR_SHAPE, "top_k must be in [1, min(n_experts, 32)]");
     if (d->shared_inter < 0 || d->shared_inter > 4096 || d->shared_inter % 64)
         return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64 <= 4096");
-    if (d->upgate_fmt != MOE_FMT_Q3S256 || d->down_fmt != MOE_FMT_NL4_32)
-        return fail(MOE_ERR_FORMAT, "routed experts must be Q3S256 up|gate and NL4_32 down");
+    if (d->upgate_fmt != MOE_FMT_Q3S256 && d->upgate_fmt != MOE_FMT_Q2S256 &&
+        d->upgate_fmt != MOE_FMT_NL4_32)
+        return fail(MOE_ERR_FORMAT, "routed up|gate must be Q3S256, Q2S256 or NL4_32");
+    if (d->down_fmt != MOE_FMT_NL4_32 && d->down_fmt != MOE_FMT_Q2_32)
+        return fail(MOE_ERR_FORMAT, "routed down must be NL4_32 or Q2_32");
     return MOE_OK;
 }
 
+// bytes of the up|gate matrix of a record (the down matrix follows it)
+int64_t upgate_bytes(const moe_layer_desc* d) {
+    return fmt_matrix_bytes(d->upgate_fmt, 2 * d->inter, d->hidden);
+}
 int64_t record_bytes(const moe_layer_desc* d) {
-    return (int64_t)2 * d->inter * (d->hidden / 256) * 104 + (int64_t)d->hidden * (d->inter / 32) * 18;
+    return upgate_bytes(d) + fmt_matrix_bytes(d->down_fmt, d->hidden, d->inter);
 }
 
 moe_status check_weights(const moe_layer_desc* d, const moe_layer_weights* w, bool need_router,
@@ -182,7 +196,8 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max) {
     if (check_desc(desc) != MOE_OK || T_max < 1 || T_max > kMaxT) return 0;
-    return layout(desc->hidden, desc->inter, desc->n_experts, desc->top_k, desc->shared_inter, T_max).total;
+    return layout(desc->hidden, desc->inter, desc->n_experts, desc->top_k, desc->shared_inter, T_max,
+                  std_formats(desc)).total;
 }
 
 moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
@@ -262,7 +277,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
         return fail(MOE_ERR_ALIGN, "x must be 16-byte aligned");
     const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k,
               Is = desc->shared_inter;
-    const Ws L = layout(H, I, E, k, Is, T);
+    const Ws L = layout(H, I, E, k, Is, T, std_formats(desc));
     if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
     const int n = T * k;
     const int gemm_tiles = (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
@@ -282,8 +297,10 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     launch_to_f16(x, x16, (int64_t)T * H, st);
     launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
     if (do_sh) launch_gemm_shared(x, T, H, sug, sdn, Is, ash, shared_y, st);
-    launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16, st);
-    launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, y_perm, nullptr, st);
+    launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16,
+                       desc->upgate_fmt, st);
+    launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, upgate_bytes(desc),
+                     desc->down_fmt, y_perm, nullptr, st);
     return launched("moe_expert_ffn");
 }
 
@@ -336,7 +353,8 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         return fail(MOE_ERR_ALIGN, "x and y must be 16-byte aligned");
     const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k,
               Is = desc->shared_inter;
-    const Ws L = layout(H, I, E, k, Is, T);
+    const bool std_fmt = std_formats(desc);
+    const Ws L = layout(H, I, E, k, Is, T, std_fmt);
     if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace too small");
     int n_cu = 0;
     s = check_device(&n_cu);
@@ -364,7 +382,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
     int32_t* hist = at<int32_t>(ws, L.hist);
 
     mk->mark();
-    if (dec_path(T, H, E)) {
+    if (dec_path(T, H, E, std_fmt)) {
         // stage 1 always runs: router logits (none given), shared up|gate
         // partials (shared expert present) and the fp16 copy of x
         launch_dec_stage1(x, T, H, E, logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
@@ -400,11 +418,13 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
             launch_gemm_shared(x, T, H, sug, sdn, Is, ash, ysh, st);
             mk->mark();
         }
-        launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16, st);
+        launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16,
+                           desc->upgate_fmt, st);
         mk->mark();
         // the unweighted rows go through memory as fp16 (one rounding,
         // relative error <= 2^-11) on this path: half the bytes written and read
-        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I, nullptr,
+        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I,
+                         upgate_bytes(desc), desc->down_fmt, nullptr,
                          reinterpret_cast<uint16_t*>(yp), st);
         mk->mark();
         launch_combine16(reinterpret_cast<const uint16_t*>(yp), inv, wv, T, k, H,
@@ -450,9 +470,10 @@ moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, fl
                           void* stream) {
     g_last_error.clear();
     if (!blocks || !out) return fail(MOE_ERR_NULL, "null argument");
-    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32)
-        return fail(MOE_ERR_FORMAT, "moe_dequantize supports Q3S256 and NL4_32");
-    const int64_t unit = fmt == MOE_FMT_Q3S256 ? 256 : 32;
+    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32 && fmt != MOE_FMT_Q2S256 &&
+        fmt != MOE_FMT_Q2_32)
+        return fail(MOE_ERR_FORMAT, "moe_dequantize supports Q3S256, NL4_32, Q2S256 and Q2_32");
+    const int64_t unit = fmt_block_weights(fmt);
     if (n_weights < unit || n_weights % unit)
         return fail(MOE_ERR_SHAPE, "n_weights must be a positive multiple of the block size");
     if (!al16(blocks) || !al4(out)) return fail(MOE_ERR_ALIGN, "blocks must be 16-byte aligned");

@@ -28,10 +28,26 @@ __constant__ const int8_t kC3[8] = {-127, -67, -31, 0, 23, 48, 78, 127};
 __constant__ const int8_t kT4[16] = {-127, -88, -66, -50, -36, -23, -11, 0,
                                      10, 20, 31, 43, 56, 71, 91, 127};
 
+// 2-bit codebook of the 2.5-bpw up/gate codec, by the same rule.
+__constant__ const int8_t kC2[4] = {-127, 0, 54, 127};
+
 constexpr int kQ3Bytes = 104;
 constexpr int kQ3Weights = 256;
 constexpr int kNL4Bytes = 18;
 constexpr int kNL4Weights = 32;
+constexpr int kQ2SBytes = 80;
+constexpr int kQ2Bytes = 10;
+
+// Format numbers (the C ABI's moe_format) and their block sizes.
+constexpr int kFmtQ3S256 = 2, kFmtNL4 = 3, kFmtQ2S256 = 4, kFmtQ2 = 5;
+__host__ __device__ constexpr int fmt_block_weights(int f) { return (f == kFmtQ3S256 || f == kFmtQ2S256) ? 256 : 32; }
+__host__ __device__ constexpr int fmt_block_bytes(int f) {
+    return f == kFmtQ3S256 ? kQ3Bytes : f == kFmtNL4 ? kNL4Bytes : f == kFmtQ2S256 ? kQ2SBytes : kQ2Bytes;
+}
+// bytes of a [rows][cols] matrix, blocks along cols
+__host__ __device__ constexpr int64_t fmt_matrix_bytes(int f, int rows, int cols) {
+    return (int64_t)rows * (cols / fmt_block_weights(f)) * fmt_block_bytes(f);
+}
 
 // ---------------------------------------------------------------- scalars
 
@@ -300,6 +316,13 @@ __device__ __forceinline__ float q3_value(float d, int s, int q) {
 }
 __device__ __forceinline__ float nl4_value(float d, int q) {
     return d * (float)kT4[q] * 0.0078125f;
+}
+// Exact fp32 value d * s * C2[q] / 128 (Q2S-256) and d * (q - 2) (Q2-32).
+__device__ __forceinline__ float q2s_value(float d, int s, int q) {
+    return (d * (float)s) * (float)kC2[q] * 0.0078125f;
+}
+__device__ __forceinline__ float q2_value(float d, int q) {
+    return d * (float)(q - 2);
 }
 
 }  // namespace moe

@@ -69,14 +69,18 @@ void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* til
 // ---- grouped-GEMM path (moe_kernels_gemm.hip)
 void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
                         const float* bias, float* logits, hipStream_t st);
+// fmt: the up|gate format (Q3S-256, Q2S-256 or NL4-32)
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
-                        const uint16_t* x16, int H, int I, uint16_t* a16_perm, hipStream_t st);
-// y_perm16 non-null: the unweighted rows are stored as fp16 there (the
-// layer's own combine reads them); else fp32 to y_perm.
+                        const uint16_t* x16, int H, int I, uint16_t* a16_perm, int fmt,
+                        hipStream_t st);
+// dn_off: byte offset of the down matrix in an expert record; fmt: its format
+// (NL4-32 or Q2-32).  y_perm16 non-null: the unweighted rows are stored as
+// fp16 there (the layer's own combine reads them); else fp32 to y_perm.
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, float* y_perm, uint16_t* y_perm16, hipStream_t st);
+                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
+                      hipStream_t st);
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
                         const uint16_t* sh_down, int Is, uint16_t* a_sh, float* y_sh,
                         hipStream_t st);

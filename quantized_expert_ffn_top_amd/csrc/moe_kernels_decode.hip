@@ -879,7 +879,7 @@ static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, 
                                 (size_t)route_scratch_bytes(T, E));
     static bool attr = false;                      // opt in to more than 64 KB of LDS once
     if (!attr) {
-        hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
+        (void)hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024 - kUgStaticLds);
         attr = true;

@@ -1,9 +1,12 @@
 // Grouped-GEMM path of the layer (prefill-sized batches).  One kernel
-// template, five uses:
+// template, eight uses:
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
 //           (fp16), B = Q3S-256 weights, epilogue SwiGLU
+//   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
+//           mixed-format layers)
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
 //           weights, epilogue fp32 (or fp16) store (permuted rows)
+//   DN_Q2   the same with Q2-32 weights
 //   UG_BF16 shared up|gate (bf16 x bf16), epilogue SwiGLU
 //   DN_BF16 shared down (bf16 x bf16), epilogue fp32 store
 //   ROUTER  router logits (bf16 x bf16), epilogue fp32 store + bias
@@ -17,7 +20,8 @@
 //      one of two LDS stages one step ahead (XOR-swizzled 16-byte chunks);
 //      one barrier per K step.
 //   B, quantized: the packed bytes of the wave's 64 weight rows for one
-//      period (a Q3 block = 4 K steps, or four NL4 blocks = 2 K steps) are
+//      period (a 256-weight block = 4 K steps, or four 32-weight blocks = 2
+//      K steps) are
 //      loaded coalesced, a period ahead, into a per-wave LDS area; each lane
 //      reads back the bytes of its own MFMA fragment (one 32-weight
 //      sub-block or block of one row per 32-column half) and decodes them
@@ -28,10 +32,15 @@
 // k = 32h .. 32h + 31) so that a lane's fragment is one contiguous sub-block;
 // A is read from LDS in the same order.
 //
-// Numerics: Q3S weights enter the matrix cores as s*c (an fp16 integer,
-// |s*c| <= 1016, exact) and d/128 is applied in fp32 to the partial sum of
-// each 256-weight block, so up|gate use the exact weights.  NL4 weights enter
-// as fp16_rne(d * T4[q] / 128) (one rounding, relative error <= 2^-11).
+// Numerics: Q3S and Q2S weights enter the matrix cores as s*c (an fp16
+// integer, |s*c| <= 1016, exact) and d/128 is applied in fp32 to the partial
+// sum of each 256-weight block, so those weights are exact.  NL4 down weights
+// enter as fp16_rne(d * T4[q] / 128) (one rounding, relative error <= 2^-11);
+// Q2 weights as d * (q - 2), exact in fp16.  NL4 up|gate weights stay exact
+// too (a rounding there would move the bf16 rounding of the SwiGLU output):
+// that mode keeps the natural K order, so the two MFMAs of a chunk pair cover
+// one 32-weight block, B = T4[q] (exact), and d/128 goes on the block's fp32
+// partial sums.
 //
 // Layer: "Avalon" README, opening paragraphs; model card "Qwen3.8-Flash-Next
 // - Avalon GGUF", "Files / Main model" (codecs, up | gate | down packing).
@@ -44,7 +53,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int N> struct Cnt { static constexpr int value = N; };
 
-enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_BF16 = 2, DN_BF16 = 3, ROUTER = 4 };
+enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_BF16 = 2, DN_BF16 = 3, ROUTER = 4,
+                UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7 };
+// quantized B formats of the routed modes
+enum BFmt { BF_NONE, BF_Q3, BF_Q2S, BF_NL4, BF_Q2 };
+template <int MODE> constexpr int bfmt() {
+    return MODE == UG_Q3 ? BF_Q3 : MODE == UG_Q2S ? BF_Q2S : (MODE == DN_NL4 || MODE == UG_NL4) ? BF_NL4
+           : MODE == DN_Q2 ? BF_Q2 : BF_NONE;
+}
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int kStages = 2;               // A stages in LDS
@@ -70,10 +86,11 @@ struct GemmArgs {
     int K;                   // reduction length
     int half_n;              // up|gate: rows of the up half (I or I_s)
     int H, I;                // layer shape (routed record layout)
+    int64_t dn_off;          // routed down: byte offset of the down matrix in a record
     const float* bias;       // router bias or null
     uint16_t* out16;         // a16_perm / a_sh
     float* out32;            // y_perm / y_sh / logits
-    uint16_t* y16;           // DN_NL4: y_perm as fp16 instead (null: fp32 to out32)
+    uint16_t* y16;           // routed down: y_perm as fp16 instead (null: fp32 to out32)
     int ldo;                 // output row length
     int npb;                 // routed: N tiles per block (consecutive, same M tile)
 };
@@ -92,6 +109,16 @@ template <int P> __device__ __forceinline__ uint32_t q3_lut_addr(const uint32_t 
     else x = q[w] << (7 - b);
     return (x & 0x1F80u) | cb;
 }
+// LDS address of the nibble-table entry for the 4-bit field at bit P of a
+// 64-bit index word (two 2-bit indices): the field lands at address bits
+// 7..10, ORed into cb.
+template <int P> __device__ __forceinline__ uint32_t nib_lut_addr(const uint32_t (&q)[2], uint32_t cb) {
+    constexpr int w = P >> 5, b = P & 31;
+    uint32_t x;
+    if constexpr (b >= 7) x = q[w] >> (b - 7);
+    else x = q[w] << (7 - b);
+    return (x & 0x780u) | cb;
+}
 // Table addresses of the four pairs of chunk KK (weights 8 KK .. 8 KK + 7).
 template <int KK>
 __device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t cb, uint32_t (&aa)[4]) {
@@ -103,10 +130,13 @@ __device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t 
 
 template <int MODE>
 __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(GemmArgs g) {
-    constexpr bool kQ3 = MODE == UG_Q3;
-    constexpr bool kNL = MODE == DN_NL4;
-    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_BF16;
-    constexpr bool kRouted = MODE == UG_Q3 || MODE == DN_NL4;
+    constexpr int kBF = bfmt<MODE>();
+    constexpr bool kQ3 = kBF == BF_Q3;
+    constexpr bool kNL = kBF == BF_NL4;
+    constexpr bool kB256 = kBF == BF_Q3 || kBF == BF_Q2S;     // 256-weight blocks: d on the partial sums
+    constexpr bool kNat = MODE == UG_NL4;                      // natural K order, d per 32-weight block
+    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_BF16 || MODE == UG_Q2S || MODE == UG_NL4;
+    constexpr bool kRouted = kBF != BF_NONE;
     constexpr int TBM = tile_rows<MODE>();
     constexpr int kAL = TBM * 8 / 256;              // A 16-byte loads per lane per K step
     constexpr int kSMX = TBM / 32;                  // 32-row groups per tile
@@ -114,10 +144,13 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     __shared__ u32x4 As[kStages][TBM * 8];
     // Decode tables, replicated so that random indices spread over the banks:
     // Q3 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
-    // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8).
+    // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8);
+    // Q2S nibble -> (C2[lo], C2[hi]) and Q2 nibble -> (lo - 2, hi - 2), 32
+    // copies (entry * 32 + lane % 32).
     __shared__ __attribute__((aligned(8192))) uint32_t lut[kRouted ? kLutDw : 1];
-    constexpr int kPer = kQ3 ? 4 : 2;               // quantized B: K steps per period
-    constexpr int kRowB = kQ3 ? 104 : 72;           // bytes of a weight row per period
+    constexpr int kPer = kB256 ? 4 : 2;             // quantized B: K steps per period
+    // bytes of a weight row per period
+    constexpr int kRowB = kBF == BF_Q3 ? 104 : kBF == BF_Q2S ? 80 : kBF == BF_NL4 ? 72 : 40;
     constexpr int kUPR = kRowB / 8;                 // 8-byte units per row = per lane
     __shared__ __attribute__((aligned(16))) uint8_t Bq[4][kRouted ? 64 * kRowB : 8];
 
@@ -154,7 +187,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         const int r = (kAL * w + i) * 8 + (lane >> 3);
         const int rc = min(r, rows - 1);
         int64_t src;
-        if (MODE == UG_Q3) src = (int64_t)(g.perm[row0 + rc] / g.k);
+        if (kRouted && kSwi) src = (int64_t)(g.perm[row0 + rc] / g.k);
         else src = row0 + rc;
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         asrc[i] = g.A + src * g.lda + c * 8;
@@ -197,13 +230,13 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     // a row's last block (NL4, odd step count) stay inside the expert record
     // or return zeros (buffer loads) and are never used.
     __amdgpu_buffer_rsrc_t wsrc;
-    int ug_rb = 0, dn_rb = 0, ug = 0;
+    int rb_w = 0, mbase = 0;                         // row bytes, matrix offset in the record
     if constexpr (kRouted) {
         const uint8_t* W = g.experts + (int64_t)e * g.estride;
         wsrc = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)g.estride, 0x00020000);
-        ug_rb = (g.H / kQ3Weights) * kQ3Bytes;
-        dn_rb = (g.I / kNL4Weights) * kNL4Bytes;
-        ug = 2 * g.I * ug_rb;
+        constexpr int nwb = kB256 ? 256 : 32, nbb = kRowB / (kB256 ? 1 : 4);
+        rb_w = (g.K / nwb) * nbb;
+        mbase = kSwi ? 0 : (int)g.dn_off;
     }
     // byte offset in the record of unit i of this lane, N tile nt, period 0
     auto unit_off = [&](int nt, int i) {
@@ -215,7 +248,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         } else {
             wr = min(nt * BN + 64 * w + r, g.N - 1);
         }
-        return (kQ3 ? wr * ug_rb : ug + wr * dn_rb) + 8 * part;
+        return mbase + wr * rb_w + 8 * part;
     };
     struct RawP {
         u32x2 u[kUPR];
@@ -231,8 +264,23 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     };
     // The lane's raw bytes of step kt from the period area: Q3 q[sn][0..2] =
     // the 12 index bytes of sub-block 2 (kt % 4) + h, q[sn][3..4] = the tail;
-    // NL4 q[sn][0..4] = the 20 dword-aligned bytes holding block 2 (kt % 2) + h.
-    auto read_raw = [&](int kt, uint32_t (&q)[2][5]) {
+    // Q2S q[sn][0..1] = the 8 index bytes of sub-block 2 (kt % 4) + h,
+    // q[sn][3..4] = d and the sub-scales; NL4 q[sn][0..4] = the 20
+    // dword-aligned bytes holding block b = 2 (kt % 2) + h; Q2 q[sn][0..2] =
+    // the 12 dword-aligned bytes holding block b (d at byte 2h).
+    constexpr int kRawDw = 5;
+    // natural order: only block j = 2 (kt % 2) + jb of the step (20
+    // dword-aligned bytes, d at byte 2 jb), read before its two chunks
+    auto read_blk = [&](int kt, int jb, uint32_t (&q)[2][kRawDw]) {
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) {
+            const uint8_t* rb = &Bq[w][(32 * sn + l32) * kRowB];
+            const uint32_t* ip = reinterpret_cast<const uint32_t*>(rb + kNL4Bytes * (2 * (kt & 1) + jb) - 2 * jb);
+#pragma unroll
+            for (int u = 0; u < 5; ++u) q[sn][u] = ip[u];
+        }
+    };
+    auto read_raw = [&](int kt, uint32_t (&q)[2][kRawDw]) {
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
             const uint8_t* rb = &Bq[w][(32 * sn + l32) * kRowB];
@@ -244,10 +292,21 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                 const u32x2 t = *reinterpret_cast<const u32x2*>(rb + 96);
                 q[sn][3] = t[0];
                 q[sn][4] = t[1];
-            } else {
+            } else if constexpr (kBF == BF_Q2S) {
+                const u32x2 ix = *reinterpret_cast<const u32x2*>(rb + 8 * (2 * (kt & 3) + hh));
+                q[sn][0] = ix[0];
+                q[sn][1] = ix[1];
+                const u32x2 t = *reinterpret_cast<const u32x2*>(rb + 64);
+                q[sn][3] = t[0];
+                q[sn][4] = t[1];
+            } else if constexpr (kNL) {
                 const uint32_t* ip = reinterpret_cast<const uint32_t*>(rb + kNL4Bytes * (2 * (kt & 1) + hh) - 2 * hh);
 #pragma unroll
                 for (int u = 0; u < 5; ++u) q[sn][u] = ip[u];
+            } else {
+                const uint32_t* ip = reinterpret_cast<const uint32_t*>(rb + kQ2Bytes * (2 * (kt & 1) + hh) - 2 * hh);
+#pragma unroll
+                for (int u = 0; u < 3; ++u) q[sn][u] = ip[u];
             }
         }
     };
@@ -269,21 +328,44 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         }
     };
 
-    // LDS byte address of a table entry = cb | entry << 7 (Q3) or << 5 (NL4).
-    const uint32_t cb = lds_addr(lut) | (kQ3 ? (uint32_t)l32 * 4u : (uint32_t)(lane & 7) * 4u);
+    // LDS byte address of a table entry = cb | entry << 7 (32 copies) or << 5
+    // (NL4, 8 copies).
+    const uint32_t cb = lds_addr(lut) | (kNL ? (uint32_t)(lane & 7) * 4u : (uint32_t)l32 * 4u);
 
     // Fragments of one K step: f[sn][kk] = weights k = 32h + 8kk .. +7 of
-    // column half sn; Q3: dl[sn] = d / 128 of the lane's column in this block.
+    // column half sn; 256-weight blocks: dl[sn] = d / 128 of the lane's
+    // column in this block.
     struct Frag {
         u32x4 f[2][4];
         float dl[2];
+        float db[2][2];      // natural order: d / 128 of [half][block of the step]
     };
     // Chunk kk of both halves from the step's raw bytes.
-    auto decode_kk = [&](int kt, const uint32_t (&R)[2][5], Frag& F, auto kkc) {
+    auto decode_kk = [&](int kt, const uint32_t (&R)[2][kRawDw], Frag& F, auto kkc) {
         constexpr int kk = decltype(kkc)::value;
 #pragma unroll
         for (int sn = 0; sn < 2; ++sn) {
-            if constexpr (kQ3) {
+            if constexpr (kNat) {
+                // chunk kk = weights 16 (kk % 2) + 8h .. +7 of block j = kk / 2:
+                // index bytes 2 + 2j + 8 (kk % 2) + 4h of its 20 raw bytes
+                constexpr int j = kk >> 1, c = kk & 1;
+                const uint32_t* Rb = &R[sn][0];                // block j's bytes (read_blk)
+                if (c == 0) {
+                    const uint32_t dbits = j ? (Rb[0] >> 16) : (Rb[0] & 0xffffu);
+                    F.db[sn][j] = f16_bits_to_f32(dbits) * 0.0078125f;
+                }
+                uint32_t nb;
+                if constexpr (j == 0) {
+                    const uint32_t lo = hh ? Rb[2 * c + 1] : Rb[2 * c], hi = hh ? Rb[2 * c + 2] : Rb[2 * c + 1];
+                    nb = __builtin_amdgcn_perm(hi, lo, 0x05040302u);
+                } else {
+                    nb = hh ? Rb[2 * c + 2] : Rb[2 * c + 1];
+                }
+                const uint32_t aa[4] = {((nb << 5) & 0x1FE0u) | cb, ((nb >> 3) & 0x1FE0u) | cb,
+                                        ((nb >> 11) & 0x1FE0u) | cb, ((nb >> 19) & 0x1FE0u) | cb};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) F.f[sn][kk][p] = lds_ld(aa[p]);   // (T4[lo], T4[hi]), exact
+            } else if constexpr (kQ3) {
                 const uint64_t tail = ((uint64_t)R[sn][4] << 32) | R[sn][3];
                 const _Float16 s = (_Float16)(float)q3_tail_s(tail, 2 * (kt & 3) + hh);
                 const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(R[sn][3] & 0xffffu));
@@ -307,20 +389,45 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
                     F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * d2);
+            } else {
+                // two 2-bit indices per table entry: chunk kk is bits 16 kk ..
+                // 16 kk + 15 of the 64-bit index word
+                uint32_t ix[2];
+                _Float16 m;                                // multiplier of the table pairs
+                if constexpr (kBF == BF_Q2S) {
+                    const uint64_t tail = ((uint64_t)R[sn][4] << 32) | R[sn][3];
+                    m = (_Float16)(float)q3_tail_s(tail, 2 * (kt & 3) + hh);
+                    if (kk == 0) F.dl[sn] = f16_bits_to_f32(R[sn][3] & 0xffffu) * 0.0078125f;
+                    ix[0] = R[sn][0];
+                    ix[1] = R[sn][1];
+                } else {
+                    // h = 0: d in bytes 0-1, indices in bytes 2..9;
+                    // h = 1: d in bytes 2-3, indices in bytes 4..11.
+                    const uint32_t dbits = __builtin_amdgcn_perm(0u, R[sn][0], hh ? 0x0c0c0302u : 0x0c0c0100u);
+                    m = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+                    ix[0] = __builtin_amdgcn_perm(R[sn][1], R[sn][0], hh ? 0x07060504u : 0x05040302u);
+                    ix[1] = __builtin_amdgcn_perm(R[sn][2], R[sn][1], hh ? 0x07060504u : 0x05040302u);
+                }
+                const h2g m2 = {m, m};
+                const uint32_t aa[4] = {nib_lut_addr<16 * kk + 0>(ix, cb), nib_lut_addr<16 * kk + 4>(ix, cb),
+                                        nib_lut_addr<16 * kk + 8>(ix, cb), nib_lut_addr<16 * kk + 12>(ix, cb)};
+#pragma unroll
+                for (int p = 0; p < 4; ++p)               // exact: small integers times m
+                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * m2);
             }
         }
     };
 
     // acc: the output sums; Q3: tmp holds the current 256-weight block's sums
     // of x * s * c, added to acc times d / 128 at the block's end.
-    f32x16 acc[kSMX][2], tmp[kQ3 ? kSMX : 1][2];
+    f32x16 acc[kSMX][2], tmp[kB256 ? kSMX : 1][2];
 #pragma unroll
     for (int a = 0; a < kSMX; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    if constexpr (kQ3) {
+    if constexpr (kB256) {
 #pragma unroll
         for (int a = 0; a < kSMX; ++a)
 #pragma unroll
@@ -335,20 +442,20 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         constexpr int SM = decltype(smc)::value;
         u32x4 fa[SM];
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) fa[sm] = As[st][aslot(32 * sm + l32, 4 * hh + kk)];
+        for (int sm = 0; sm < SM; ++sm) fa[sm] = As[st][aslot(32 * sm + l32, kNat ? 2 * kk + hh : 4 * hh + kk)];
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm)
 #pragma unroll
             for (int sn = 0; sn < 2; ++sn) {
-                if constexpr (kQ3) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], tmp[sm][sn]);
+                if constexpr (kB256) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], tmp[sm][sn]);
                 else if constexpr (kRouted) acc[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], acc[sm][sn]);
                 else acc[sm][sn] = mfma32_bf16(fa[sm], fb[sn][kk], acc[sm][sn]);
             }
     };
-    // Q3, end of a 256-weight block: acc += tmp * d / 128, tmp = 0.
+    // 256-weight blocks, at a block's end: acc += tmp * d / 128, tmp = 0.
     auto apply_d = [&](const Frag& F, auto smc) {
         constexpr int SM = decltype(smc)::value;
-        if constexpr (kQ3) {
+        if constexpr (kB256) {
 #pragma unroll
             for (int sm = 0; sm < SM; ++sm)
 #pragma unroll
@@ -359,6 +466,28 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                         tmp[sm][sn][r] = 0.f;
                     }
         }
+    };
+
+    // Natural order, block j of a step (chunks 2j and 2j + 1, decoded into
+    // F): per 32-row group and half, the two MFMAs chain into a fresh
+    // partial, then acc += partial * d / 128 of the block.
+    auto nat_block = [&](int st, const Frag& F, auto jc, auto smc) {
+        constexpr int j = decltype(jc)::value, SM = decltype(smc)::value;
+        u32x4 fa[SM][2];
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) fa[sm][c] = As[st][aslot(32 * sm + l32, 2 * (2 * j + c) + hh)];
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+            for (int sn = 0; sn < 2; ++sn) {
+                f32x16 t = {};
+                t = mfma32_f16(fa[sm][0], F.f[sn][2 * j], t);
+                t = mfma32_f16(fa[sm][1], F.f[sn][2 * j + 1], t);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[sm][sn][r] += t[r] * F.db[sn][j];
+            }
     };
 
     // ---- epilogue of N tile nt.  Lane l, register r of group (sm, sn): row
@@ -387,7 +516,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                         float v = acc[sm][sn][r];
                         if (MODE == ROUTER && g.bias) v += g.bias[br];
                         const int64_t o = (int64_t)(row0 + m) * g.ldo + br;
-                        if (MODE == DN_NL4 && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
+                        if (kRouted && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
                         else g.out32[o] = v;
                     }
                 }
@@ -412,10 +541,18 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
             if (kQ3) {
                 const int en = i >> 5;
                 v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
-            } else {
+            } else if (kNat) {
+                const int en = i >> 3;
+                v = pack2(f32_to_f16_bits((float)kT4[en & 15]), f32_to_f16_bits((float)kT4[en >> 4]));
+            } else if (kNL) {
                 const int en = i >> 3;
                 v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.0078125f),
                           f32_to_f16_bits((float)kT4[en >> 4] * 0.0078125f));
+            } else {
+                const int en = (i >> 5) & 15;              // 16 entries; the rest repeats
+                const int lo = en & 3, hi = en >> 2;
+                if (kBF == BF_Q2S) v = pack2(f32_to_f16_bits((float)kC2[lo]), f32_to_f16_bits((float)kC2[hi]));
+                else v = pack2(f32_to_f16_bits((float)(lo - 2)), f32_to_f16_bits((float)(hi - 2)));
             }
             lut[i] = v;
         }
@@ -440,7 +577,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                 const int st = kt & 1;
                 put_a(st ^ 1, Ra);
                 if (opens) put_period(P);
-                if constexpr (kQ3) {                 // a single N tile
+                if constexpr (kB256) {               // a single N tile
                     load_a(min(kt + 3, nk - 1), Ra);
                     if (opens) load_period(nt, kt / kPer + 1, P);
                 } else {
@@ -451,20 +588,31 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                         else load_period(min(nt + 1, NT - 1), 0, P);
                     }
                 }
-                uint32_t q[2][5];
-                read_raw(kt, q);
-                decode_kk(kt, q, F, Cnt<0>{});
-                mma_kk(st, 0, F.f, smc);
-                decode_kk(kt, q, F, Cnt<1>{});
-                mma_kk(st, 1, F.f, smc);
-                decode_kk(kt, q, F, Cnt<2>{});
-                mma_kk(st, 2, F.f, smc);
-                decode_kk(kt, q, F, Cnt<3>{});
-                mma_kk(st, 3, F.f, smc);
+                uint32_t q[2][kRawDw];
+                if constexpr (kNat) {
+                    read_blk(kt, 0, q);
+                    decode_kk(kt, q, F, Cnt<0>{});
+                    decode_kk(kt, q, F, Cnt<1>{});
+                    nat_block(st, F, Cnt<0>{}, smc);
+                    read_blk(kt, 1, q);
+                    decode_kk(kt, q, F, Cnt<2>{});
+                    decode_kk(kt, q, F, Cnt<3>{});
+                    nat_block(st, F, Cnt<1>{}, smc);
+                } else {
+                    read_raw(kt, q);
+                    decode_kk(kt, q, F, Cnt<0>{});
+                    mma_kk(st, 0, F.f, smc);
+                    decode_kk(kt, q, F, Cnt<1>{});
+                    mma_kk(st, 1, F.f, smc);
+                    decode_kk(kt, q, F, Cnt<2>{});
+                    mma_kk(st, 2, F.f, smc);
+                    decode_kk(kt, q, F, Cnt<3>{});
+                    mma_kk(st, 3, F.f, smc);
+                }
                 __syncthreads();
             };
             Frag F;
-            if constexpr (kQ3) {
+            if constexpr (kB256) {
                 // one N tile per block (48 steps at H = 3072); K = H is a multiple
                 // of 256: a period per four steps, d applied after the fourth
                 for (int kt = 0; kt < nk; kt += 4) {
@@ -553,24 +701,31 @@ void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* 
 
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
-                        const uint16_t* x16, int H, int I, uint16_t* a16_perm, hipStream_t st) {
+                        const uint16_t* x16, int H, int I, uint16_t* a16_perm, int fmt,
+                        hipStream_t st) {
     GemmArgs a{};
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.perm = perm; a.k = k; a.A = x16; a.lda = H;
     a.N = 2 * I; a.K = H; a.half_n = I; a.H = H; a.I = I; a.out16 = a16_perm; a.ldo = I;
     a.npb = 1;
-    k_gemm<UG_Q3><<<gemm_grid((swi_tiles(I) + a.npb - 1) / a.npb, max_tiles), 256, 0, st>>>(a);
+    const unsigned grid = gemm_grid((swi_tiles(I) + a.npb - 1) / a.npb, max_tiles);
+    if (fmt == kFmtQ3S256) k_gemm<UG_Q3><<<grid, 256, 0, st>>>(a);
+    else if (fmt == kFmtQ2S256) k_gemm<UG_Q2S><<<grid, 256, 0, st>>>(a);
+    else k_gemm<UG_NL4><<<grid, 256, 0, st>>>(a);
 }
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, float* y_perm, uint16_t* y_perm16, hipStream_t st) {
+                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
+                      hipStream_t st) {
     GemmArgs a{};
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
-    a.out32 = y_perm; a.y16 = y_perm16; a.ldo = H;
+    a.dn_off = dn_off; a.out32 = y_perm; a.y16 = y_perm16; a.ldo = H;
     a.npb = (I / BK) % 2 == 0 ? 4 : 1;               // tiles chain only with an even step count
-    k_gemm<DN_NL4><<<gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles), 256, 0, st>>>(a);
+    const unsigned grid = gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles);
+    if (fmt == kFmtNL4) k_gemm<DN_NL4><<<grid, 256, 0, st>>>(a);
+    else k_gemm<DN_Q2><<<grid, 256, 0, st>>>(a);
 }
 
 void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,

@@ -45,6 +45,39 @@ __global__ void k_dequant_nl4(const uint8_t* __restrict__ blocks, int64_t n_blk,
     }
 }
 
+// One thread per 32-weight sub-block of a Q2S-256 block (80 bytes: sub-block
+// j's 8 index bytes at 8j, d and the sub-scales at 64, the Q3S tail layout).
+__global__ void k_dequant_q2s(const uint8_t* __restrict__ blocks, int64_t n_sub,
+                              float* __restrict__ out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_sub) return;
+    const uint8_t* b = blocks + (i >> 3) * kQ2SBytes;
+    const int j = (int)(i & 7);
+    const uint64_t idx = *reinterpret_cast<const uint64_t*>(b + 8 * j);
+    const uint64_t tail = *reinterpret_cast<const uint64_t*>(b + 64);
+    const float d = q3_tail_d(tail);
+    const int s = q3_tail_s(tail, j);
+    float* o = out + i * 32;
+#pragma unroll
+    for (int w = 0; w < 32; ++w) o[w] = q2s_value(d, s, (int)((idx >> (2 * w)) & 3u));
+}
+
+// One thread per Q2-32 block (10 bytes, 2-byte aligned: read bytewise).
+__global__ void k_dequant_q2(const uint8_t* __restrict__ blocks, int64_t n_blk,
+                             float* __restrict__ out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_blk) return;
+    const uint8_t* b = blocks + i * kQ2Bytes;
+    const float d = f16_bits_to_f32((uint32_t)b[0] | ((uint32_t)b[1] << 8));
+    float* o = out + i * 32;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const uint32_t byte = b[2 + w];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[4 * w + t] = q2_value(d, (int)((byte >> (2 * t)) & 3u));
+    }
+}
+
 // ---------------------------------------------------------------- staging
 
 // x bf16 -> fp16 (the matrix-core operand type of the quantized experts).
@@ -376,13 +409,12 @@ __global__ void k_rmsnorm_residual(float* __restrict__ h, const float* __restric
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, hipStream_t st) {
-    if (fmt == 2) {
-        int64_t n_sub = n_weights / 32;
-        k_dequant_q3s<<<cdiv(n_sub, 256), 256, 0, st>>>((const uint8_t*)blocks, n_sub, out);
-    } else {
-        int64_t n_blk = n_weights / 32;
-        k_dequant_nl4<<<cdiv(n_blk, 256), 256, 0, st>>>((const uint8_t*)blocks, n_blk, out);
-    }
+    const int64_t n32 = n_weights / 32;              // sub-blocks / blocks of 32 weights
+    const uint8_t* b = (const uint8_t*)blocks;
+    if (fmt == kFmtQ3S256) k_dequant_q3s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
+    else if (fmt == kFmtNL4) k_dequant_nl4<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
+    else if (fmt == kFmtQ2S256) k_dequant_q2s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
+    else k_dequant_q2<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
 }
 
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st) {

@@ -61,7 +61,8 @@ def _w(experts=P, stride=45056, router=P, shared=(None, None)):
 @pytest.mark.parametrize("case,status", [
     (dict(hidden=100), 2), (dict(hidden=256 * 33 + 0, inter=96), 2), (dict(inter=32), 2),
     (dict(n_experts=0), 2), (dict(top_k=17, n_experts=16), 2), (dict(shared_inter=100), 2),
-    (dict(upgate_fmt=1), 3), (dict(down_fmt=2), 3),
+    (dict(upgate_fmt=1), 3), (dict(down_fmt=2), 3), (dict(upgate_fmt=5), 3),
+    (dict(down_fmt=4), 3), (dict(upgate_fmt=6), 3), (dict(down_fmt=0), 3),
 ])
 def test_layer_forward_rejects_bad_shapes(case, status):
     base = dict(hidden=256, inter=128, n_experts=16, top_k=2, shared_inter=0, upgate_fmt=2,
@@ -111,3 +112,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libmoe.so")
     with pytest.raises(RuntimeError):
         L.load()
+
+
+@pytest.mark.parametrize("ug,dn", [(2, 3), (4, 5), (3, 3), (2, 5), (4, 3), (3, 5)])
+def test_workspace_size_for_every_supported_format_pair(ug, dn):
+    """All up|gate x down pairs of the mixed-format layers are accepted (pure
+    host call); pairs that would use the bandwidth kernels need the larger
+    router-partials layout at small T."""
+    d = Q.desc(3072, 512, 512, 10, 512, ug, dn)
+    for T in (1, 8, 17, 9536):
+        assert Q.moe_workspace_size(d, T) > 0
+    d_bad = Q.desc(3072, 512, 512, 10, 512, dn if dn == 5 else 1, ug if ug == 2 else 4)
+    assert Q.moe_workspace_size(d_bad, 8) == 0

@@ -53,7 +53,8 @@ def test_tiny_layer(T):
 def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
     lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev())
     x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
-    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
+               sh.down_fmt)
     wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
                     lay.shared_down)
     y, ids, w = _run_layer(d, wts, x)
@@ -117,6 +118,43 @@ def test_limit_shape_layer(T, sh):
 @pytest.mark.parametrize("T", [17, 64])
 def test_real_small_gemm_layer(T):
     _real_case(T, seed=7)
+
+
+# Mixed-format layers (the 2.5-bpw / 4-bit NL up|gate and 2-bit down codecs):
+# every up|gate x down pair at a small shape with a shared expert, on both
+# sides of the token count where the standard formats switch kernels (these
+# formats take the grouped GEMMs at every T), and an odd down K (I = 3 * 64:
+# the last K period of the 2-bit rows is half).
+F = synth
+PAIRS = [(F.FMT_Q2S256, F.FMT_Q2_32), (F.FMT_NL4_32, F.FMT_NL4_32), (F.FMT_Q3S256, F.FMT_Q2_32),
+         (F.FMT_Q2S256, F.FMT_NL4_32), (F.FMT_NL4_32, F.FMT_Q2_32)]
+
+
+@pytest.mark.parametrize("ug,dn", PAIRS, ids=["q2s_q2", "nl4_nl4", "q3s_q2", "q2s_nl4", "nl4_q2"])
+@pytest.mark.parametrize("T", [5, 40])
+def test_mixed_format_layer(T, ug, dn):
+    _real_case(T, seed=9, sh=synth.Shape(512, 128, 24, 3, 64, ug, dn))
+
+
+@pytest.mark.parametrize("ug,dn", [(F.FMT_Q2S256, F.FMT_Q2_32), (F.FMT_NL4_32, F.FMT_Q2_32)])
+def test_mixed_format_odd_down_k(ug, dn):
+    _real_case(33, seed=10, sh=synth.Shape(512, 192, 24, 3, 64, ug, dn))
+
+
+@pytest.mark.parametrize("ug,dn", [(F.FMT_Q2S256, F.FMT_Q2_32), (F.FMT_NL4_32, F.FMT_NL4_32)])
+@pytest.mark.parametrize("T", [8, 64])
+def test_mixed_format_real_layer(T, ug, dn):
+    _real_case(T, seed=11, sh=synth.Shape(3072, 512, 512, 10, 512, ug, dn))
+
+
+@pytest.mark.parametrize("ug,dn", [(F.FMT_Q2S256, F.FMT_Q2_32), (F.FMT_NL4_32, F.FMT_NL4_32)])
+def test_mixed_format_prefill_chunk_sampled(ug, dn):
+    """9536-token chunk (the equal-size prefill batch of the mixed-format
+    stack), Zipf(0.8) routing, sampled tokens including the last."""
+    rng = np.random.default_rng(2)
+    sample = np.sort(rng.choice(9536, size=4, replace=False))
+    sample[-1] = 9535
+    _real_case(9536, seed=12, zipf_s=0.8, sample=sample, sh=synth.Shape(3072, 512, 512, 10, 512, ug, dn))
 
 
 def test_real_prefill_zipf_sampled():
