@@ -20,7 +20,15 @@ algorithmic bytes are those of the experts the batch actually routes to.
 cpu_baseline: the CPU oracle (fp64 NumPy, dequantising from the packed bytes)
 on one T = 8 decode layer of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+--stack-prefill runs the mixed-format workload instead and prints its own
+JSON line: one 9536-token chunk through 48 layers whose routed experts use the
+model card's per-layer formats (up|gate Q3S-256 / Q2S-256 / NL4-32, down
+NL4-32 / Q2-32; seeded order), Zipf(0.8) routing, RMSNorm + residual between
+layers, all 48 layers resident in HBM (about 51 GB).  A step is one pass
+through the 48 layers; the roofline object is for the routed up|gate GEMMs
+(MFMA-bound), their time summed over the layers of a pass.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill]
 """
 
 import argparse
@@ -82,6 +90,8 @@ def parse():
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--stack-prefill", action="store_true",
+                   help="the 48-layer mixed-format 9536-token prefill chunk instead")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only the workload read by rocprofv3 counter passes: decode T=8 "
                         "layers rotated as in the timed loop")
@@ -122,6 +132,9 @@ def main():
         print("# copy probe: 4 copies of %d bytes" % src.numel(), file=sys.stderr)
         return
     Q.load()
+    if args.stack_prefill:
+        stack_prefill(args, Q, synth, torch, np, dev)
+        return
     sh = synth.REAL
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
 
@@ -261,6 +274,111 @@ def main():
                    "tokens": 8, "layers_rotated": args.layers},
         "roofline": roof, "cpu_baseline": cpu, "results": results,
     }
+    print(json.dumps(line))
+
+
+def stack_prefill(args, Q, synth, torch, np, dev):
+    """48 mixed-format layers, one 9536-token chunk (see the module header)."""
+    wl = synth.WORKLOADS["stack_prefill"]
+    T, seed, nl = wl.tokens[0], wl.seed, wl.layers
+    t0 = time.time()
+    layers, descs, wts, gammas = [], [], [], []
+    for l in range(nl):
+        sh = synth.stack_shape(seed, l)
+        lay = synth.real_layer(sh, seed, l, zipf_s=wl.zipf_s, device=dev)
+        layers.append(lay)
+        descs.append(Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter,
+                            sh.upgate_fmt, sh.down_fmt))
+        wts.append(Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b,
+                             lay.shared_ug, lay.shared_down))
+        gammas.append(synth.norm_gain(sh.hidden, seed, l).to(dev))
+    torch.cuda.synchronize()
+    gb = sum(L.experts.numel() for L in layers) / 1e9
+    print("# stack: generated %d layers (%.1f GB of packed experts) in %.1f s" % (
+        nl, gb, time.time() - t0), file=sys.stderr)
+    ws = torch.empty(max(Q.moe_workspace_size(dd, T) for dd in descs), dtype=torch.uint8, device=dev)
+    x0 = synth.tokens_bf16(T, H, seed).float().to(dev)
+    h = torch.empty_like(x0)
+    normed = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(timed_events=None):
+        h.copy_(x0)
+        marks = []
+        for l in range(nl):
+            Q.moe_rmsnorm_residual(h, None, gammas[l], 1e-6, normed)
+            if timed_events is None:
+                Q.moe_layer_forward(descs[l], wts[l], normed, y, ws)
+            else:
+                marks.append(Q.moe_layer_forward_timed(descs[l], wts[l], normed, y, ws,
+                                                       [ev.cuda_event for ev in timed_events[l]]))
+            Q.moe_rmsnorm_residual(h, y, None, 1e-6, None)
+        return marks
+
+    for _ in range(max(1, args.warmup // 8)):
+        one_pass()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 16)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert bool(torch.isfinite(h).all())
+
+    # per-kernel times of one pass, grouped by the layer's up|gate and down formats
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(nl)]
+    for row in evs:
+        for ev in row:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    marks = one_pass(evs)
+    torch.cuda.synchronize()
+    names = ["router", "topk", "to_f16", "permute", "shared", "upgate", "down", "combine"]
+    fmt_name = {2: "q3s256", 3: "nl4_32", 4: "q2s256", 5: "q2_32"}
+    ug_t, dn_t, ug_by, dn_by, tot = {}, {}, {}, {}, {}
+    for l in range(nl):
+        dur = [evs[l][j].elapsed_time(evs[l][j + 1]) for j in range(marks[l] - 1)]
+        for nm, t in zip(names, dur):
+            tot[nm] = tot.get(nm, 0.0) + t
+        u, dn = descs[l].upgate_fmt, descs[l].down_fmt
+        ug_t.setdefault(fmt_name[u], []).append(dur[5])
+        dn_t.setdefault(fmt_name[dn], []).append(dur[6])
+    ug_flops = 2.0 * T * K * 2 * I * H            # per layer
+    dn_flops = 2.0 * T * K * I * H
+    per_fmt = {"upgate": {f: {"layers": len(v), "us_mean": round(1e3 * np.mean(v), 1),
+                               "TFLOPs": round(ug_flops / (np.mean(v) * 1e-3) / 1e12, 1)}
+                          for f, v in ug_t.items()},
+               "down": {f: {"layers": len(v), "us_mean": round(1e3 * np.mean(v), 1),
+                             "TFLOPs": round(dn_flops / (np.mean(v) * 1e-3) / 1e12, 1)}
+                        for f, v in dn_t.items()}}
+    ug_sum = sum(sum(v) for v in ug_t.values())
+    ach = ug_flops * nl / (ug_sum * 1e-3) / 1e12
+    flops = FLOP_PER_TOKEN * T * nl
+    line = {
+        "metric": "MoE-stack prefill tokens/s (48 mixed-format layers, one 9536-token chunk)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, args.warmup // 8), "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "q3s/q2s/nl4/q2 weights, fp16/bf16 mfma, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "48 MoE layers H=3072, E=512 (top-10) + 1 shared bf16 expert, "
+                               "I=512, per-layer expert formats, 9536 tokens, Zipf(0.8), "
+                               "RMSNorm + residual", "tokens": T, "layers": nl,
+                   "packed_expert_GB": round(gb, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_gemm routed up|gate (Q3S / Q2S / NL4 modes), summed over a pass"},
+        "cpu_baseline": None,
+        "results": {"algorithmic_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                    "kernel_ms_per_pass": {k: round(v, 3) for k, v in tot.items()},
+                    "per_format": per_fmt},
+    }
+    print("# stack prefill: %.2f ms per 48-layer pass, per format %s" % (ms, per_fmt), file=sys.stderr)
     print(json.dumps(line))
 
 

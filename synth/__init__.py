@@ -20,6 +20,12 @@ the "Avalon" README, "Speed"):
           bias giving Zipf(1.0) popularity; experts by seeded code sampling.
 * stack   48 decode-shaped layers, T=3, RMSNorm gain N(1, 0.1), eps 1e-6.
 * prefill T=8192, decode shapes; Zipf(1.0) bias or no bias (uniform).
+* stack_prefill  48 decode-shaped layers of mixed expert formats, one
+          9536-token chunk, Zipf(0.8), RMSNorm + residual between layers.
+          Up|gate: 17 layers Q3S-256, 20 Q2S-256, 11 NL4-32; down: 39 NL4-32,
+          9 Q2-32 (the model card's per-layer counts, "Files / Main model");
+          which layer gets which format is a seeded permutation of each list
+          (the page gives the counts, not the order).
 
 Code sampling (how expert bytes are drawn at real shape): every byte of an
 expert record is a counter-hash output, then the fields that must hold a
@@ -116,6 +122,8 @@ WORKLOADS = {
     "stack": Workload("stack", REAL, (3,), layers=48, seed=4),
     "prefill": Workload("prefill", REAL, (8192,), seed=3),
     "prefill_uniform": Workload("prefill_uniform", REAL, (8192,), seed=3, zipf_s=0.0),
+    "stack_prefill": Workload("stack_prefill", REAL, (9536,), layers=48, seed=13, zipf_s=0.8,
+                              note="mixed expert formats per layer (stack_formats)"),
 }
 
 
@@ -222,13 +230,28 @@ def expert_record(shape, seed, layer, e, device="cpu", mode="rtn"):
     return rec
 
 
-def expert_bank(shape, seed, layer, device="cpu", mode="rtn", chunk=64):
-    """All E expert records of a layer: uint8 [E][expert_bytes] on `device`.
-    Rows are generated in chunks of experts to bound temporary memory."""
+def expert_bank(shape, seed, layer, device="cpu", mode="rtn", chunk=32):
+    """All E expert records of a layer: uint8 [E][expert_bytes] on `device`,
+    equal byte for byte to expert_record(e) for every e.  Rows are generated
+    `chunk` experts at a time to bound temporary memory."""
     E, nb = shape.n_experts, shape.expert_bytes
+    nw = (nb + 3) // 4
     out = torch.empty((E, nb), dtype=torch.uint8, device=device)
-    for e in range(E):
-        out[e] = expert_record(shape, seed, layer, e, device, mode)
+    i = torch.arange(nw, dtype=torch.int64, device=device)[None, :]
+    for e0 in range(0, E, chunk):
+        es = range(e0, min(E, e0 + chunk))
+        k1 = torch.tensor([key(seed, layer, 2 * e + 1) for e in es], dtype=torch.int64, device=device)
+        k2 = torch.tensor([key(seed, layer, 2 * e + 2) for e in es], dtype=torch.int64, device=device)
+        w = fmix32(fmix32(i + k1[:, None]) ^ k2[:, None]).to(torch.int32)
+        rec = w.view(torch.uint8).reshape(len(es), 4 * nw)[:, :nb]
+        ug = rec[:, :shape.upgate_bytes].reshape(-1, BLOCKS[shape.upgate_fmt][1])
+        dn = rec[:, shape.upgate_bytes:].reshape(-1, BLOCKS[shape.down_fmt][1])
+        for fmt, blk in ((shape.upgate_fmt, ug), (shape.down_fmt, dn)):
+            fixed = blk.clone()
+            _fix_fields(fmt, fixed.view(-1), mode)
+            blk.copy_(fixed)
+        out[e0:e0 + len(es)] = torch.cat([ug.reshape(len(es), -1), dn.reshape(len(es), -1)], dim=1)
+        del w, rec
     return out
 
 
@@ -317,6 +340,25 @@ class Layer:
     seed: int = 0
     layer: int = 0
     extra: dict = field(default_factory=dict)
+
+
+STACK_UG_FORMATS = (FMT_Q3S256,) * 17 + (FMT_Q2S256,) * 20 + (FMT_NL4_32,) * 11
+STACK_DN_FORMATS = (FMT_NL4_32,) * 39 + (FMT_Q2_32,) * 9
+
+
+def stack_formats(seed, layers=48):
+    """(up|gate format, down format) of each layer of the mixed-format stack:
+    the counts above, placed by two seeded permutations."""
+    rng = np.random.default_rng(key(seed, 0, 80))
+    ug = [STACK_UG_FORMATS[i] for i in rng.permutation(48)]
+    dn = [STACK_DN_FORMATS[i] for i in rng.permutation(48)]
+    return list(zip(ug, dn))[:layers]
+
+
+def stack_shape(seed, layer):
+    """Real shape with the formats of one layer of the mixed-format stack."""
+    ug, dn = stack_formats(seed)[layer]
+    return Shape(REAL.hidden, REAL.inter, REAL.n_experts, REAL.top_k, REAL.shared_inter, ug, dn)
 
 
 def real_layer(shape, seed, layer, zipf_s=1.0, device="cpu", mode="rtn", experts=True):

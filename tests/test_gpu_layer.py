@@ -217,3 +217,52 @@ def test_stack_three_layers_teacher_forced():
                                                          shared=real_shared_np(lay))["y"])
         Q.moe_rmsnorm_residual(h, y, None, 1e-6, None)
     assert_close(h.cpu().numpy(), h_ref, "stack end-to-end")
+
+
+def test_mixed_stack_prefill_sampled():
+    """The mixed-format stack (per-layer formats of the model card, seeded
+    order), one 9536-token chunk, Zipf(0.8), RMSNorm (eps 1e-6) + residual:
+    layers 0..13 run in order on the GPU; on the first layer of each of the
+    six (up|gate, down) format pairs, sampled tokens are compared with the
+    oracle fed the GPU's layer input (teacher forcing)."""
+    wl = synth.WORKLOADS["stack_prefill"]
+    T, seed = wl.tokens[0], wl.seed
+    fm = synth.stack_formats(seed)
+    check = {}
+    for l, p in enumerate(fm):
+        check.setdefault(p, l)
+    last = max(check.values())
+    checked = set(check.values())
+    assert len(checked) == 6 and last < 16
+    rows = np.array([0, 4097, 9535])
+    h = synth.tokens_bf16(T, synth.REAL.hidden, seed).float().to(dev())
+    normed = torch.empty((T, synth.REAL.hidden), dtype=torch.bfloat16, device=dev())
+    y = torch.empty((T, synth.REAL.hidden), dtype=torch.float32, device=dev())
+    ids = torch.empty((T, synth.REAL.top_k), dtype=torch.int32, device=dev())
+    ws = None
+    for l in range(last + 1):
+        sh = synth.stack_shape(seed, l)
+        lay = synth.real_layer(sh, seed, l, zipf_s=wl.zipf_s, device=dev())
+        gamma = synth.norm_gain(sh.hidden, seed, l).to(dev())
+        d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
+                   sh.down_fmt)
+        if ws is None or ws.numel() < Q.moe_workspace_size(d, T):
+            ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+        Q.moe_rmsnorm_residual(h, None, gamma, 1e-6, normed)
+        wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                        lay.shared_down)
+        Q.moe_layer_forward(d, wts, normed, y, ws, topk_ids_out=ids)
+        torch.cuda.synchronize()
+        if l in checked:
+            xin = bf16_np(normed[rows])
+            L = OM.router_logits(xin, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+            got_ids = ids[rows].cpu().numpy()
+            assert ids_valid_topk(got_ids, L, sh.top_k)
+            cache = ExpertCache(sh, lambda e, l=l, sh=sh: synth.expert_record(sh, seed, l, e).numpy())
+            ref = OM.layer_forward(xin, sh.top_k, cache, sh.n_experts, logits=L,
+                                   shared=real_shared_np(lay), force_ids=got_ids)
+            assert_close(y[rows].cpu().numpy(), ref["y"],
+                         "stack layer %d formats %s" % (l, (sh.upgate_fmt, sh.down_fmt)))
+        Q.moe_rmsnorm_residual(h, y, None, 1e-6, None)
+        del lay, wts
+    assert torch.isfinite(h).all()
