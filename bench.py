@@ -304,16 +304,20 @@ def stack_prefill(args, Q, synth, torch, np, dev):
     stream = torch.cuda.current_stream(dev)
 
     def one_pass(timed_events=None):
+        # h += MoE_l(norm_l(h)); the residual add of layer l and the norm of
+        # layer l + 1 are one call
         h.copy_(x0)
         marks = []
+        Q.moe_rmsnorm_residual(h, None, gammas[0], 1e-6, normed)
         for l in range(nl):
-            Q.moe_rmsnorm_residual(h, None, gammas[l], 1e-6, normed)
             if timed_events is None:
                 Q.moe_layer_forward(descs[l], wts[l], normed, y, ws)
             else:
                 marks.append(Q.moe_layer_forward_timed(descs[l], wts[l], normed, y, ws,
                                                        [ev.cuda_event for ev in timed_events[l]]))
-            Q.moe_rmsnorm_residual(h, y, None, 1e-6, None)
+            last = l + 1 == nl
+            Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
+                                   None if last else normed)
         return marks
 
     for _ in range(max(1, args.warmup // 8)):

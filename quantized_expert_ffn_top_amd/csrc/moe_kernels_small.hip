@@ -229,7 +229,8 @@ __global__ void k_perm_count(const int32_t* __restrict__ ids, int T, int k, int 
 }
 
 // One workgroup of 1024 threads: chunk bases per expert (exclusive running
-// sums, offsets added), expert offsets, and the BM-row tile list.
+// sums within the expert; the scatter adds the expert's offset), expert
+// offsets, and the BM-row tile list.
 __global__ void __launch_bounds__(1024) k_perm_scan(int32_t* __restrict__ hist, int nch, int E,
                                                     int BM, int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ tiles,
@@ -239,12 +240,12 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int32_t* __restrict__ hist, 
     int run = 0;
     if (e < E) {
         int c = 0;
-        for (; c + 8 <= nch; c += 8) {
-            int v[8];
+        for (; c + 32 <= nch; c += 32) {                  // 32 loads in flight
+            int v[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(c + u) * E + e];
+            for (int u = 0; u < 32; ++u) v[u] = hist[(int64_t)(c + u) * E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 hist[(int64_t)(c + u) * E + e] = run;
                 run += v[u];
             }
@@ -266,7 +267,6 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int32_t* __restrict__ hist, 
             tiles[3 * (t0 + i) + 1] = off + i * BM;
             tiles[3 * (t0 + i) + 2] = min(BM, run - i * BM);
         }
-        for (int c = 0; c < nch; ++c) hist[(int64_t)c * E + e] += off;
     }
     if (e == 0) {
         offsets[E] = tot;
@@ -275,8 +275,8 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int32_t* __restrict__ hist, 
 }
 
 __global__ void k_perm_scatter(const int32_t* __restrict__ ids, int T, int k, int E,
-                               const int32_t* __restrict__ base, int32_t* __restrict__ perm,
-                               int32_t* __restrict__ inv) {
+                               const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
     __shared__ unsigned long long mask[1024];
     const int lane = threadIdx.x;
     for (int e = lane; e < E; e += 64) mask[e] = 0ull;
@@ -291,7 +291,7 @@ __global__ void k_perm_scatter(const int32_t* __restrict__ ids, int T, int k, in
     for (int j = 0; j < k; ++j) {
         const int f = t * k + j;
         const int e = ids[f];
-        const int p = b[e] + __popcll(mask[e] & lt);
+        const int p = offsets[e] + b[e] + __popcll(mask[e] & lt);
         perm[p] = f;
         inv[f] = p;
     }
@@ -437,7 +437,7 @@ void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32
     const int nch = (int)cdiv(T, 64);
     k_perm_count<<<nch, 64, 0, st>>>(ids, T, k, E, hist);
     k_perm_scan<<<1, 1024, 0, st>>>(hist, nch, E, BM, offsets, tiles, ntiles);
-    k_perm_scatter<<<nch, 64, 0, st>>>(ids, T, k, E, hist, perm, inv);
+    k_perm_scatter<<<nch, 64, 0, st>>>(ids, T, k, E, hist, offsets, perm, inv);
 }
 
 void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, int32_t* ntiles,
