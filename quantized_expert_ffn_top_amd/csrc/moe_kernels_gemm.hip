@@ -496,6 +496,11 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         constexpr int SM = decltype(smc)::value;
         const int br0 = brow_of(nt, 0), br1 = brow_of(nt, 1);
         const bool oc0 = ocol_of(nt, 0), oc1 = ocol_of(nt, 1);
+        // the tile's first row, opaque to loop-invariant code motion: the
+        // output addresses are formed at their stores, not kept in registers
+        // across the N-tile loop
+        int r0 = row0;
+        __asm__ volatile("" : "+s"(r0));
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
 #pragma unroll
@@ -507,7 +512,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                     const float u = acc[sm][0][r], gv = acc[sm][1][r];
                     const uint32_t bf = f32_to_bf16(gv / (1.0f + expf(-gv)) * u);
                     const uint16_t v = kRouted ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
-                    g.out16[(int64_t)(row0 + m) * g.ldo + br0] = v;
+                    g.out16[(int64_t)(r0 + m) * g.ldo + br0] = v;
                 } else {
 #pragma unroll
                     for (int sn = 0; sn < 2; ++sn) {
@@ -515,7 +520,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                         const int br = sn ? br1 : br0;
                         float v = acc[sm][sn][r];
                         if (MODE == ROUTER && g.bias) v += g.bias[br];
-                        const int64_t o = (int64_t)(row0 + m) * g.ldo + br;
+                        const int64_t o = (int64_t)(r0 + m) * g.ldo + br;
                         if (kRouted && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
                         else g.out32[o] = v;
                     }
