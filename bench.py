@@ -28,7 +28,12 @@ layers, all 48 layers resident in HBM (about 51 GB).  A step is one pass
 through the 48 layers; the roofline object is for the routed up|gate GEMMs
 (MFMA-bound), their time summed over the layers of a pass.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill]
+--stack-decode runs the speculative-verify step instead (its own JSON line):
+3 tokens (1 + 2 drafts) through 48 decode-shaped Q3S-256 / NL4-32 layers, each
+independently seeded with a fresh Zipf(1.0) bias, RMSNorm + residual between
+layers, all 53 GB of experts resident.  A step is one 48-layer pass.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill | --stack-decode]
 """
 
 import argparse
@@ -92,6 +97,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--stack-prefill", action="store_true",
                    help="the 48-layer mixed-format 9536-token prefill chunk instead")
+    p.add_argument("--stack-decode", action="store_true",
+                   help="the 48-layer 3-token speculative-verify step instead")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only the workload read by rocprofv3 counter passes: decode T=8 "
                         "layers rotated as in the timed loop")
@@ -134,6 +141,9 @@ def main():
     Q.load()
     if args.stack_prefill:
         stack_prefill(args, Q, synth, torch, np, dev)
+        return
+    if args.stack_decode:
+        stack_decode(args, Q, synth, torch, np, dev)
         return
     sh = synth.REAL
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
@@ -383,6 +393,83 @@ def stack_prefill(args, Q, synth, torch, np, dev):
                     "per_format": per_fmt},
     }
     print("# stack prefill: %.2f ms per 48-layer pass, per format %s" % (ms, per_fmt), file=sys.stderr)
+    print(json.dumps(line))
+
+
+def stack_decode(args, Q, synth, torch, np, dev):
+    """48 decode-shaped layers, 3 tokens per step (see the module header)."""
+    wl = synth.WORKLOADS["stack"]
+    T, seed, nl = wl.tokens[0], wl.seed, wl.layers
+    sh = synth.REAL
+    t0 = time.time()
+    layers = [synth.real_layer(sh, seed, l, zipf_s=wl.zipf_s, device=dev) for l in range(nl)]
+    wts = [Q.weights(L.experts, sh.expert_bytes, L.router_w, L.router_b, L.shared_ug, L.shared_down)
+           for L in layers]
+    gammas = [synth.norm_gain(sh.hidden, seed, l).to(dev) for l in range(nl)]
+    torch.cuda.synchronize()
+    gb = sum(L.experts.numel() for L in layers) / 1e9
+    print("# stack decode: generated %d layers (%.1f GB of packed experts) in %.1f s" % (
+        nl, gb, time.time() - t0), file=sys.stderr)
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev)
+    x0 = synth.tokens_bf16(T, H, seed).float().to(dev)
+    h = torch.empty_like(x0)
+    normed = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(count=False):
+        h.copy_(x0)
+        us = []
+        Q.moe_rmsnorm_residual(h, None, gammas[0], 1e-6, normed)
+        for l in range(nl):
+            if count:
+                Q.moe_layer_forward(d, wts[l], normed, y, ws, topk_ids_out=ids)
+                us.append(int(torch.unique(ids).numel()))
+            else:
+                Q.moe_layer_forward(d, wts[l], normed, y, ws)
+            last = l + 1 == nl
+            Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
+                                   None if last else normed)
+        return us
+
+    us = one_pass(count=True)
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert bool(torch.isfinite(h).all())
+    U = float(np.mean(us))
+    step_bytes = sum(layer_bytes(T, u) for u in us)
+    line = {
+        "metric": "speculative-verify step tokens/s (48 decode layers, 3 tokens)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "q3s/nl4 weights, fp16/bf16 mfma, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": "48 MoE layers H=3072, E=512 (Q3S-256 up|gate, NL4-32 down), top-10 "
+                               "+ 1 shared bf16 expert, I=512, 3 tokens (1 + 2 drafts), Zipf(1.0) "
+                               "per layer, RMSNorm + residual", "tokens": T, "layers": nl,
+                   "packed_expert_GB": round(gb, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole step (all kernels of the 48 layers), algorithmic bytes"},
+        "cpu_baseline": None,
+        "results": {"distinct_experts_mean": U, "step_bytes": int(step_bytes),
+                    "us_per_layer": round(ms * 1e3 / nl, 2)},
+    }
+    print("# stack decode: %.3f ms per 48-layer step, U = %.1f, %.0f GB/s" % (
+        ms, U, step_bytes / (ms * 1e-3) / 1e9), file=sys.stderr)
     print(json.dumps(line))
 
 
