@@ -521,9 +521,9 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     // registers, decodes item i from stage (i - i0) % 2 and writes its partial
     // sums; after the
     // barrier waves 0-3 finish item i while the others go on.  Items i + 2
-    // and i + 3 are in flight during the decode of item i (past the end the
-    // last item is loaded again and not used; a block without items loads
-    // item min(i0, n_items - 1)).
+    // and i + 3 are in flight during the decode of item i; the last steps
+    // load nothing past the block's items (a block without items loads item
+    // min(i0, n_items - 1) in the prologue).
     issue(i0, P0);
     issue(i0 + 1, P1);
     // the table, while the first items load
@@ -543,19 +543,24 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
         __builtin_amdgcn_sched_barrier(0);
         decode(it, (it - i0) & 1);
     };
-    for (int it = i0; it < i1; it += 6) {
+    auto step_last = [&](int it, Buf& B) {                  // no item it + 3 to load
+        put((it + 1 - i0) & 1, B);
+        __builtin_amdgcn_sched_barrier(0);
+        decode(it, (it - i0) & 1);
+    };
+    int it = i0;
+    for (; it + 4 < i1; it += 2) {
         step(it, P1);
-        if (it + 1 >= i1) break;
         step(it + 1, P0);
-        if (it + 2 >= i1) break;
-        step(it + 2, P1);
-        if (it + 3 >= i1) break;
-        step(it + 3, P0);
-        if (it + 4 >= i1) break;
-        step(it + 4, P1);
-        if (it + 5 >= i1) break;
-        step(it + 5, P0);
     }
+    // the last (up to four) items: loads only for items that exist
+#define MOE_LAST(J, B)                                                          \
+    if (it + J < i1) {                                                          \
+        if (it + J + 3 < i1) step(it + J, B);                                   \
+        else step_last(it + J, B);                                              \
+    }
+    MOE_LAST(0, P1) MOE_LAST(1, P0) MOE_LAST(2, P1) MOE_LAST(3, P0)
+#undef MOE_LAST
 
     if (shp) {                                              // shared expert: sum partials, SwiGLU
         for (int i = blockIdx.x * NT + tid; i < T * Is; i += G * NT) {
