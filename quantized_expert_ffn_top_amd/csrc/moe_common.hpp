@@ -197,7 +197,8 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
     return v;
 }
 
-// Exact top-k of one row of E logits by one wave64 (E <= 1024, k <= 32).
+// Round-based exact top-k of one row of E logits by one wave64 (E <= 1024,
+// k <= 32; the fallback of wave_topk for rows with many equal logits).
 // Lane j < k returns (id_j, L_j) in selection order; other lanes return
 // (-1, 0).  `get(e)` yields the fp32 logit of expert e (lane l holds experts
 // l, l+64, ...).  Each lane first sorts its Q candidates by (logit desc,
@@ -274,13 +275,144 @@ __device__ __forceinline__ void wave_topk_q(Get get, int E, int k, int& out_id, 
     }
 }
 
+// Value of `v` held by lane ^ D, D = 1, 2, ..., 32.  Every move runs with all
+// lanes active (a move placed under a lane condition would read inactive
+// lanes as zero), then the lane picks its partner's copy.
+#define MOE_DPPU(v, ctrl) ((uint32_t)__builtin_amdgcn_mov_dpp((int)(v), (ctrl), 0xF, 0xF, true))
+template <int D>
+__device__ __forceinline__ uint32_t xor_partner(uint32_t v) {
+    const int lane = __lane_id();
+    if constexpr (D == 1) {
+        return MOE_DPPU(v, 0xB1);                  // quad_perm [1,0,3,2]
+    } else if constexpr (D == 2) {
+        return MOE_DPPU(v, 0x4E);                  // quad_perm [2,3,0,1]
+    } else if constexpr (D == 4) {
+        const uint32_t from_m4 = MOE_DPPU(v, 0x124), from_p4 = MOE_DPPU(v, 0x12C);   // row_ror 4 / 12
+        return (lane & 4) ? from_m4 : from_p4;
+    } else if constexpr (D == 8) {
+        return MOE_DPPU(v, 0x128);                 // row_ror 8
+    } else if constexpr (D == 16) {                // odd rows swap with even rows
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {                                       // upper half swaps with lower half
+        static_assert(D == 32, "xor partner distance");
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+}
+#undef MOE_DPPU
+
+// One compare-exchange step of a bitonic sorting network over the wave:
+// merge blocks of S lanes, partner lane ^ D; blocks with lane & S == 0 come
+// out in descending order (the whole wave for S = 64).
+template <int S, int D>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v) {
+    const int lane = __lane_id();
+    const uint32_t o = xor_partner<D>(v);
+    const bool keep_max = ((lane & D) == 0) == ((lane & S) == 0);
+    return keep_max ? max(v, o) : min(v, o);
+}
+
+// The 64 lane values in descending order (lane 0 holds the largest).
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v) {
+    v = bitonic_step<2, 1>(v);
+    v = bitonic_step<4, 2>(v);
+    v = bitonic_step<4, 1>(v);
+    v = bitonic_step<8, 4>(v);
+    v = bitonic_step<8, 2>(v);
+    v = bitonic_step<8, 1>(v);
+    v = bitonic_step<16, 8>(v);
+    v = bitonic_step<16, 4>(v);
+    v = bitonic_step<16, 2>(v);
+    v = bitonic_step<16, 1>(v);
+    v = bitonic_step<32, 16>(v);
+    v = bitonic_step<32, 8>(v);
+    v = bitonic_step<32, 4>(v);
+    v = bitonic_step<32, 2>(v);
+    v = bitonic_step<32, 1>(v);
+    v = bitonic_step<64, 32>(v);
+    v = bitonic_step<64, 16>(v);
+    v = bitonic_step<64, 8>(v);
+    v = bitonic_step<64, 4>(v);
+    v = bitonic_step<64, 2>(v);
+    v = bitonic_step<64, 1>(v);
+    return v;
+}
+
+// LDS scratch of the wave top-k: 64 candidates and 32 results, 8 bytes each.
+constexpr int kTopkScratch = 96;
+
+// The same top-k as wave_topk_q, by a threshold and exact ranks.  tau = the
+// k-th largest of the 64 lanes' largest keys: k distinct keys are >= tau, so
+// every one of the k best is among the candidates (keys >= tau).  Those are
+// written to LDS as (key, 0xFFFF - expert) pairs, whose u64 order is the
+// routing order, and each candidate's rank is the number of candidates above
+// it; the candidate of rank j goes to lane j.  More than 64 candidates (many
+// equal logits): the round-based selection instead.  scr: kTopkScratch u64 of
+// this wave's LDS.
+template <int Q, typename Get>
+__device__ __forceinline__ void wave_topk_rank(Get get, int E, int k, uint64_t* scr, int& out_id,
+                                               float& out_val) {
+    const int lane = __lane_id();
+    uint32_t key[Q];
+    bool real[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const int e = lane + 64 * i;
+        real[i] = e < E;
+        key[i] = real[i] ? order_key(get(e)) : 0u;
+    }
+    uint32_t h = key[0];
+#pragma unroll
+    for (int i = 1; i < Q; ++i) h = max(h, key[i]);
+    const uint32_t tau = __builtin_amdgcn_readlane(wave_sort_desc_u32(h), k - 1);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) c += (real[i] && key[i] >= tau) ? 1 : 0;
+    const int incl = wave_incl_scan_dpp(c);
+    const int C = __builtin_amdgcn_readlane(incl, 63);
+    if (C > 64) {
+        wave_topk_q<Q>(get, E, k, out_id, out_val);
+        return;
+    }
+    int pos = incl - c;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        if (real[i] && key[i] >= tau) {
+            scr[pos] = ((uint64_t)key[i] << 32) | (uint32_t)(0xFFFFu - (uint32_t)(lane + 64 * i));
+            ++pos;
+        }
+    }
+    const uint64_t mine = lane < C ? scr[lane] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < C; j += 8) {                // 8 broadcast reads in flight
+        uint64_t c8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c8[u] = scr[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (j + u < C && c8[u] > mine) ? 1 : 0;
+    }
+    uint64_t* res = scr + 64;
+    if (lane < C && rank < k) res[rank] = mine;
+    out_id = -1;
+    out_val = 0.f;
+    if (lane < k) {
+        const uint64_t r = res[lane];
+        out_id = (int)(0xFFFFu - (uint32_t)r);
+        out_val = order_key_value((uint32_t)(r >> 32));
+    }
+}
+
+// Exact top-k of one row of E logits by one wave64 (E <= 1024, k <= 32);
+// lane j < k returns (id_j, L_j) in routing order.  scr: kTopkScratch u64 of
+// LDS owned by this wave.
 template <typename Get>
-__device__ __forceinline__ void wave_topk(Get get, int E, int k, int& out_id, float& out_val) {
-    if (E <= 64) wave_topk_q<1>(get, E, k, out_id, out_val);
-    else if (E <= 128) wave_topk_q<2>(get, E, k, out_id, out_val);
-    else if (E <= 256) wave_topk_q<4>(get, E, k, out_id, out_val);
-    else if (E <= 512) wave_topk_q<8>(get, E, k, out_id, out_val);
-    else wave_topk_q<16>(get, E, k, out_id, out_val);
+__device__ __forceinline__ void wave_topk(Get get, int E, int k, uint64_t* scr, int& out_id, float& out_val) {
+    if (E <= 64) wave_topk_rank<1>(get, E, k, scr, out_id, out_val);
+    else if (E <= 128) wave_topk_rank<2>(get, E, k, scr, out_id, out_val);
+    else if (E <= 256) wave_topk_rank<4>(get, E, k, scr, out_id, out_val);
+    else if (E <= 512) wave_topk_rank<8>(get, E, k, scr, out_id, out_val);
+    else wave_topk_rank<16>(get, E, k, scr, out_id, out_val);
 }
 
 // Softmax over the k selected logits held by lanes 0..k-1 (lane 0 = max).

@@ -165,9 +165,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
 // memory (ids, w, the optional copies, offsets [E+1], perm, inv, tiles,
 // ntiles).  The logits are np planes [np][T][E] summed in plane order, plus
 // `bias` when given (np = 1, no bias: the logits as they are).  scr: >=
-// route_scratch_bytes(T, E) of LDS (the sums are staged there before the
-// top-k reads them).
-__host__ __device__ constexpr int route_scratch_bytes(int T, int E) { return 10752 + T * E * 4; }
+// route_scratch_bytes(T, E, NT / 64) of LDS (the sums are staged there before
+// the top-k reads them; then each wave's top-k scratch).
+__host__ __device__ constexpr int route_log_end(int T, int E) { return (10752 + T * E * 4 + 7) & ~7; }
+__host__ __device__ constexpr int route_scratch_bytes(int T, int E, int waves) {
+    return route_log_end(T, E) + waves * kTopkScratch * 8;
+}
 
 template <int NT>
 __device__ __forceinline__ void route_block(const float* __restrict__ logits, int np,
@@ -182,6 +185,7 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
     int* s_ids = reinterpret_cast<int*>(scr + 8192);               // [512]
     int* s_scan = reinterpret_cast<int*>(scr + 10240);             // [40]
     float* s_log = reinterpret_cast<float*>(scr + 10752);          // [T][E]
+    uint64_t* s_tk = reinterpret_cast<uint64_t*>(scr + route_log_end(T, E)) + (threadIdx.x >> 6) * kTopkScratch;
     const int tid = threadIdx.x, lane = __lane_id(), wid = threadIdx.x >> 6;
     for (int e = tid; e < 1024; e += NT) s_mask[e] = 0u;
     const int nl = T * E;
@@ -210,7 +214,7 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
         const float* row = s_log + t * E;
         int id;
         float v;
-        wave_topk([&](int e) { return row[e]; }, E, k, id, v);
+        wave_topk([&](int e) { return row[e]; }, E, k, s_tk, id, v);
         const float wt = wave_softmax_selected(v, k);
         if (lane < k) {
             s_ids[t * k + lane] = id;
@@ -881,7 +885,7 @@ static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, 
                          int I, uint16_t* a16_perm, const float* shp, int nkc, int Is,
                          uint16_t* a_sh, const RouteOut& ro) {
     const size_t dyn = std::max((size_t)ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H),
-                                (size_t)route_scratch_bytes(T, E));
+                                (size_t)route_scratch_bytes(T, E, WAVES));
     static bool attr = false;                      // opt in to more than 64 KB of LDS once
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
@@ -927,7 +931,8 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* log
 }
 
 bool upgate_dec_supported(int H, int T, int E) {
-    const int dyn = std::max(ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H), route_scratch_bytes(T, E));
+    const int dyn = std::max(ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H),
+                             route_scratch_bytes(T, E, ug_waves(H)));
     return H / 128 <= 8 * 4 && kUgStaticLds + dyn <= 160 * 1024;
 }
 

@@ -101,12 +101,13 @@ __global__ void k_to_f16(const uint16_t* __restrict__ x, uint16_t* __restrict__ 
 __global__ void k_topk(const float* __restrict__ logits, int T, int E, int k,
                        int32_t* __restrict__ ids, float* __restrict__ w,
                        int32_t* __restrict__ ids2, float* __restrict__ w2) {
+    __shared__ uint64_t scr[4][kTopkScratch];
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= T) return;
     const float* row = logits + (int64_t)t * E;
     int id;
     float v;
-    wave_topk([&](int e) { return row[e]; }, E, k, id, v);
+    wave_topk([&](int e) { return row[e]; }, E, k, scr[threadIdx.x >> 6], id, v);
     float wt = wave_softmax_selected(v, k);
     const int lane = __lane_id();
     if (lane < k) {

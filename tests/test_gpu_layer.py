@@ -80,6 +80,41 @@ def test_real_decode_layer(T):
     _real_case(T, seed=2)
 
 
+def test_real_decode_layer_logit_ties():
+    """Given logits full of equal values through the routing inside the
+    bandwidth path's up|gate kernel (E = 512, k = 10): the ids must be the
+    exact top-k by (logit descending, expert ascending), on rows that take
+    the threshold-and-rank selection and on rows that fall back to the
+    round-based one (more than 64 logits at the threshold)."""
+    sh = synth.REAL
+    T, E, k = 8, sh.n_experts, sh.top_k
+    rng = np.random.default_rng(11)
+    L = rng.normal(size=(T, E)).astype(np.float32)
+    L[1, :] = 0.25                                           # all equal
+    L[2, :] = rng.integers(0, 8, size=E)                     # eight values
+    L[3, [40, 7, 300, 511]] = L[3].max() + 1.0               # a four-way tie at the top
+    lead = np.argsort(-L[4], kind="stable")[:12]
+    L[4, lead] = L[4, lead[0]]                               # twelve equal leaders
+    L[5, :] = rng.integers(0, 16, size=E) * 0.5              # sixteen values
+    L[6, :] = 0.0
+    L[6, ::3] = -0.0                                         # -0 ties +0
+    L[6, 100] = 1.0
+    L[7, :] = -np.arange(E, dtype=np.float32)                # strictly decreasing
+    lay = synth.real_layer(sh, 3, 0, device=dev())
+    x = synth.tokens_bf16(T, sh.hidden, 3).to(dev())
+    d = Q.desc(sh.hidden, sh.inter, E, k, sh.shared_inter, sh.upgate_fmt, sh.down_fmt)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    y, ids, w = _run_layer(d, wts, x, logits=torch.from_numpy(L).to(dev()))
+    L64 = L.astype(np.float64)
+    assert np.array_equal(ids, OM.topk_ids(L64, k))
+    assert ids[6].tolist() == [100, 0, 1, 2, 3, 4, 5, 6, 7, 8]
+    cache = ExpertCache(sh, lambda e: synth.expert_record(sh, 3, 0, e).numpy())
+    ref = OM.layer_forward(bf16_np(x), k, cache, E, logits=L64, shared=real_shared_np(lay))
+    assert np.abs(w - ref["w"]).max() <= 1e-6
+    assert_close(y, ref["y"], "logit ties T=%d" % T)
+
+
 # Edge shape for both paths: I = 3 * 64 (an odd count of 64-wide K steps in
 # the down projection, a partial last up|gate output tile), 24 experts (not a
 # multiple of the 16-expert router tile), top-3, a 64-wide shared expert.
