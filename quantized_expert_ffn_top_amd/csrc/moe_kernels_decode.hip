@@ -631,6 +631,8 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     float* __restrict__ y_perm, float* __restrict__ y_sh) {
     __shared__ __attribute__((aligned(32768))) uint32_t lut[kNl4LutDw];   // byte bits OR onto the address
     __shared__ uint32_t stg[kDnWaves][16 * kDnStageDw];
+    __shared__ int s_claim[kDnWaves];                       // slices taken, per group of waves
+    __shared__ int s_spare[kDnWaves][64];                   // the other lanes' claims land here
     const int tid = threadIdx.x, lane = __lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
@@ -640,9 +642,10 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         const uint32_t val = pack2(f32_to_f16_bits(t4_entry(v & 15)), f32_to_f16_bits(t4_entry(v >> 4)));
         reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
     }
+    if (lane == 0) s_claim[w] = 0;
     __syncthreads();
 
-    // this wave's expert and slices
+    // this wave's expert (its team: the waves dealt to it)
     const bool has_sh = sh_down != nullptr;
     const int total = 2 * nt + (has_sh ? 7 : 0);
     const int GW = gridDim.x * kDnWaves, gw = blockIdx.x * kDnWaves + w;
@@ -654,7 +657,29 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const int nsl = H / 16;
     const int s0 = (int)((int64_t)(gw - ws) * nsl / (we - ws));
     const int s1 = (int)((int64_t)(gw - ws + 1) * nsl / (we - ws));
-    if (s0 >= s1) return;
+    // When the wave keeps all of K in registers, the waves of the team in
+    // this block share their slices [g0, g1) through an LDS counter (owned by
+    // the group's first wave, wf) and take them one at a time, so that the
+    // group finishes together whichever of its waves runs faster; otherwise
+    // each wave keeps its share [s0, s1).
+    const int bw = blockIdx.x * kDnWaves;
+    const int wf = max(ws, bw) - bw, wl = min(we, bw + kDnWaves) - 1 - bw;
+    const int g0 = (int)((int64_t)(bw + wf - ws) * nsl / (we - ws));
+    const int g1 = (int)((int64_t)(bw + wl + 1 - ws) * nsl / (we - ws));
+    // lane 0 receives the count of slices taken so far.  Every lane adds, to
+    // its own word but lane 0: an address that differs across the wave keeps
+    // the add a plain LDS atomic (the same address everywhere would become one
+    // add broadcast at once, with the wait for it right there).
+    auto claim = [&]() -> int {
+        int* p = lane == 0 ? &s_claim[wf] : &s_spare[w][lane];
+        return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    // the claimed slice as a scalar (nsl: none left), read here and not earlier
+    auto take = [&](int v) {
+        __asm__ volatile("" : "+v"(v));
+        const int c = __builtin_amdgcn_readfirstlane(v);
+        return c < g1 - g0 ? g0 + c : nsl;
+    };
 
     if (t == nt) {                                          // shared expert, bf16
         const bool vt = r < T;
@@ -672,7 +697,8 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         if (nks <= kDnShSteps) {
             // A in registers; a slice's whole K (<= 1 KB per lane group row)
             // loaded at once, the next slice in flight during the steps.  Steps
-            // past Is load nothing (out-of-range buffer offsets read zero).
+            // past Is and slices past the last load nothing (out-of-range
+            // buffer offsets read zero).
             const __amdgpu_buffer_rsrc_t bsrc = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(sh_down), 0, H * Is * 2, 0x00020000);
             u32x4 a[kDnShSteps], B0[kDnShSteps], B1[kDnShSteps];
@@ -680,7 +706,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
             for (int i = 0; i < kDnShSteps; ++i)
                 a[i] = (vt && i < nks) ? ld16(arow + 32 * i) : u32x4{0u, 0u, 0u, 0u};
             auto load_b = [&](int sl, u32x4* B) {
-                const uint32_t rowo = (uint32_t)(((16 * min(sl, s1 - 1) + r) * Is + 8 * g) * 2);
+                const uint32_t rowo = sl < nsl ? (uint32_t)(((16 * sl + r) * Is + 8 * g) * 2) : 0x80000000u;
 #pragma unroll
                 for (int i = 0; i < kDnShSteps; ++i)
                     B[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -692,13 +718,22 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
                 for (int i = 0; i < kDnShSteps; ++i) acc = mfma16_bf16(a[i], B[i], acc);
                 store(sl, acc);
             };
-            load_b(s0, B0);
-            for (int sl = s0; sl < s1; sl += 2) {
-                load_b(sl + 1, B1);
-                steps(sl, B0);
-                if (sl + 1 >= s1) break;
-                load_b(sl + 2, B0);
-                steps(sl + 1, B1);
+            // each claim is made before the loads of the step ahead of its use
+            const int p0 = claim();
+            int pend = claim();
+            int sa = take(p0);
+            load_b(sa, B0);
+            while (sa < nsl) {
+                const int sb = take(pend);
+                pend = claim();
+                load_b(sb, B1);
+                steps(sa, B0);
+                if (sb >= nsl) return;
+                const int sc = take(pend);
+                pend = claim();
+                load_b(sc, B0);
+                steps(sb, B1);
+                sa = sc;
             }
             return;
         }
@@ -751,15 +786,12 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         uint32_t v[kDnLoads];
     };
     Buf P0, P1;
-    // unit q = (slice s0 + q / nkc, chunk q % nkc); past the end the last unit is loaded again
-    const int nu = (s1 - s0) * nkc;
-    // the expert's down rows as a buffer: 32-bit lane offsets, the unit's start in a scalar
+    // the expert's down rows as a buffer: 32-bit lane offsets, the unit's start
+    // in a scalar (out of range past the last slice: nothing loaded)
     const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(W), 0, H * rb, 0x00020000);
-    auto issue = [&](int q, Buf& B) {
-        q = min(q, nu - 1);
-        const int sl = s0 + q / nkc, c = q - (q / nkc) * nkc;
-        const int soff = 16 * sl * rb + 288 * c;
+    auto issue = [&](int sl, int c, Buf& B) {               // chunk c of slice sl
+        const int soff = sl < nsl ? 16 * sl * rb + 288 * c : 0x7ff00000;
         const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
         const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
 #pragma unroll
@@ -774,8 +806,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
             B.v[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, go, soff, 0);
         }
     };
-    auto put = [&](int q, const Buf& B) {
-        const int c = min(q, nu - 1) % nkc;
+    auto put = [&](int c, const Buf& B) {
         const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
         const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
 #pragma unroll
@@ -790,8 +821,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     };
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto decode = [&](int q) {
-        const int sl = s0 + q / nkc, c = q - (q / nkc) * nkc;
+    auto decode = [&](int sl, int c) {
         if (!ONEK) load_a(c);
         const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
         const uint32_t* wr = st + r * kDnStageDw;
@@ -831,7 +861,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
                 }
             }
         }
-        if (c == nkc - 1) {                                 // slice done: rows m = 4g + i
+        if (ONEK || c == nkc - 1) {                         // slice done: rows m = 4g + i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * g + i;
@@ -841,25 +871,56 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
             }
         }
     };
-
-    // two units in flight while one is decoded
-    issue(0, P0);
-    issue(1, P1);
-    auto step = [&](int q, Buf& B) {
-        put(q, B);
+    // one unit: stage the unit in B, load the unit two ahead into B, decode
+    auto step = [&](int sl, int c, Buf& B, int sl2, int c2) {
+        put(c, B);
         __builtin_amdgcn_sched_barrier(0);
-        issue(q + 2, B);
+        issue(sl2, c2, B);
         __builtin_amdgcn_sched_barrier(0);
-        decode(q);
+        decode(sl, c);
     };
-    for (int q = 0; q < nu; q += 4) {
-        step(q, P0);
-        if (q + 1 >= nu) break;
-        step(q + 1, P1);
-        if (q + 2 >= nu) break;
-        step(q + 2, P0);
-        if (q + 3 >= nu) break;
-        step(q + 3, P1);
+
+    if constexpr (ONEK) {
+        // claimed slices, two units in flight while one is decoded; each claim
+        // is made before the loads of the step ahead of its use
+        const int p0 = claim(), p1 = claim();
+        int pend = claim();
+        int sa = take(p0);
+        int sb = take(p1);
+        // the two units' loads in order (interleaved, the loop's waits for
+        // the first would also wait for the second)
+        issue(sa, 0, P0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(sb, 0, P1);
+        __builtin_amdgcn_sched_barrier(0);
+        // (the exits return: a break that joins the loop's back edge would
+        // make the waits for a buffer's loads cover the other buffer's too)
+        while (sa < nsl) {
+            const int sc = take(pend);
+            pend = claim();
+            step(sa, 0, P0, sc, 0);
+            if (sb >= nsl) return;
+            const int sd = take(pend);
+            pend = claim();
+            step(sb, 0, P1, sd, 0);
+            sa = sc;
+            sb = sd;
+        }
+    } else {
+        if (s0 >= s1) return;
+        // unit q = (slice s0 + q / nkc, chunk q % nkc); nothing loaded past the last
+        const int nu = (s1 - s0) * nkc;
+        auto unit_sl = [&](int q) { return q < nu ? s0 + q / nkc : nsl; };
+        auto unit_c = [&](int q) { return q < nu ? q % nkc : 0; };
+        issue(unit_sl(0), unit_c(0), P0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(unit_sl(1), unit_c(1), P1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < nu; q += 2) {
+            step(unit_sl(q), unit_c(q), P0, unit_sl(q + 2), unit_c(q + 2));
+            if (q + 1 >= nu) break;
+            step(unit_sl(q + 1), unit_c(q + 1), P1, unit_sl(q + 3), unit_c(q + 3));
+        }
     }
 }
 
