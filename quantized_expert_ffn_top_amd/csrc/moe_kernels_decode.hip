@@ -363,6 +363,13 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int tid = threadIdx.x, lane = __lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
+    // the decode table first, while the routing's logit loads are in flight
+    // (the routing's barriers make it visible)
+    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
+        const int v = i >> 3;
+        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
+        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
+    }
     // routing (every block; block 0 publishes it), in the partial-sum space
     route_block<NT>(logits, np, lbias, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids, ro.w,
                     ro.ids_out, ro.w_out, ro.offsets, ro.perm, ro.inv, ro.tiles, ro.ntiles);
@@ -530,13 +537,6 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     // min(i0, n_items - 1) in the prologue).
     issue(i0, P0);
     issue(i0 + 1, P1);
-    // the table, while the first items load
-    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
-        const int v = i >> 3;
-        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
-        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
-    }
-    __syncthreads();                                        // table written
     put(0, P0);
     issue(i0 + 2, P0);
     __syncthreads();                                        // stage 0 written
