@@ -29,11 +29,12 @@ through the 48 layers; the roofline object is for the routed up|gate GEMMs
 (MFMA-bound), their time summed over the layers of a pass.
 
 --stack-decode runs the speculative-verify step instead (its own JSON line):
-3 tokens (1 + 2 drafts) through 48 decode-shaped Q3S-256 / NL4-32 layers, each
-independently seeded with a fresh Zipf(1.0) bias, RMSNorm + residual between
-layers, all 53 GB of experts resident.  A step is one 48-layer pass.
+1 + K tokens (K drafts, --spec K, default 2) through 48 decode-shaped
+Q3S-256 / NL4-32 layers, each independently seeded with a fresh Zipf(1.0)
+bias, RMSNorm + residual between layers, all 53 GB of experts resident.  A
+step is one 48-layer pass.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill | --stack-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill | --stack-decode [--spec K]]
 """
 
 import argparse
@@ -98,7 +99,9 @@ def parse():
     p.add_argument("--stack-prefill", action="store_true",
                    help="the 48-layer mixed-format 9536-token prefill chunk instead")
     p.add_argument("--stack-decode", action="store_true",
-                   help="the 48-layer 3-token speculative-verify step instead")
+                   help="the 48-layer speculative-verify step instead")
+    p.add_argument("--spec", type=int, default=2,
+                   help="draft tokens of the verify step (tokens = 1 + spec, at most 15)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="run only the workload read by rocprofv3 counter passes: decode T=8 "
                         "layers rotated as in the timed loop")
@@ -211,7 +214,7 @@ def main():
         return
 
     results = {"decode": {}, "prefill": None}
-    for T in (1, 3, 8):
+    for T in (1, 3, 5, 8):
         x = synth.tokens_bf16(T, sh.hidden, 2, 0).to(dev)
         us = distinct_experts(T, x)
         ms = time_steps(T, x, args.steps, args.warmup, args.layers)
@@ -260,7 +263,7 @@ def main():
     # roofline of the dominant kernel of the headline workload (decode T=8)
     dec8 = results["decode"][8]
     kd8, U8 = dec8.pop("_kd"), dec8.pop("_U")
-    for T in (1, 3):
+    for T in (1, 3, 5):
         results["decode"][T].pop("_kd")
         results["decode"][T].pop("_U")
     ub = upgate_bytes(8, U8)
@@ -397,9 +400,12 @@ def stack_prefill(args, Q, synth, torch, np, dev):
 
 
 def stack_decode(args, Q, synth, torch, np, dev):
-    """48 decode-shaped layers, 3 tokens per step (see the module header)."""
+    """48 decode-shaped layers, 1 + spec tokens per step (see the module header)."""
     wl = synth.WORKLOADS["stack"]
-    T, seed, nl = wl.tokens[0], wl.seed, wl.layers
+    seed, nl = wl.seed, wl.layers
+    if not 0 <= args.spec <= 15:
+        sys.exit("--spec must be in [0, 15] (the bandwidth path takes up to 16 tokens)")
+    T = 1 + args.spec
     sh = synth.REAL
     t0 = time.time()
     layers = [synth.real_layer(sh, seed, l, zipf_s=wl.zipf_s, device=dev) for l in range(nl)]
@@ -451,14 +457,14 @@ def stack_decode(args, Q, synth, torch, np, dev):
     U = float(np.mean(us))
     step_bytes = sum(layer_bytes(T, u) for u in us)
     line = {
-        "metric": "speculative-verify step tokens/s (48 decode layers, 3 tokens)",
+        "metric": "speculative-verify step tokens/s (48 decode layers, %d tokens)" % T,
         "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "q3s/nl4 weights, fp16/bf16 mfma, fp32 accumulate", "data": "synthetic",
         "config": {"workload": "48 MoE layers H=3072, E=512 (Q3S-256 up|gate, NL4-32 down), top-10 "
-                               "+ 1 shared bf16 expert, I=512, 3 tokens (1 + 2 drafts), Zipf(1.0) "
-                               "per layer, RMSNorm + residual", "tokens": T, "layers": nl,
+                               "+ 1 shared bf16 expert, I=512, %d tokens (1 + %d drafts), Zipf(1.0) "
+                               "per layer, RMSNorm + residual" % (T, T - 1), "tokens": T, "layers": nl,
                    "packed_expert_GB": round(gb, 2)},
         "roofline": {"bound": "hbm", "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

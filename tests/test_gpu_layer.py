@@ -75,7 +75,7 @@ def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
     return y, ids
 
 
-@pytest.mark.parametrize("T", [1, 3, 8, 16])
+@pytest.mark.parametrize("T", [1, 3, 5, 8, 16])
 def test_real_decode_layer(T):
     _real_case(T, seed=2)
 
