@@ -16,7 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["moe_api.hip", "moe_kernels_small.hip", "moe_kernels_decode.hip",
-           "moe_kernels_gemm.hip"]
+           "moe_kernels_gemm.hip", "moe_blas.hip"]
+# the plain bf16 GEMMs of the grouped-GEMM path use rocBLAS
+LINK = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -48,7 +50,7 @@ def build(verbose=False):
                 if verbose and out.strip():
                     print(out)
         tmp_lib = os.path.join(tmp, "libmoe.so")
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs)
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs + LINK)
         shutil.copyfile(tmp_lib, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
     finally:

@@ -1,5 +1,6 @@
 // Grouped-GEMM path of the layer (prefill-sized batches).  One kernel
-// template, eight uses:
+// template, five uses (the routed experts; the router and the shared expert
+// are plain bf16 GEMMs, done by the library in moe_blas.hip):
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
 //           (fp16), B = Q3S-256 weights, epilogue SwiGLU
 //   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
@@ -7,9 +8,6 @@
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
 //           weights, epilogue fp32 (or fp16) store (permuted rows)
 //   DN_Q2   the same with Q2-32 weights
-//   UG_BF16 shared up|gate (bf16 x bf16), epilogue SwiGLU
-//   DN_BF16 shared down (bf16 x bf16), epilogue fp32 store
-//   ROUTER  router logits (bf16 x bf16), epilogue fp32 store + bias
 //
 // Tile 64 token rows x 256 weight rows, K steps of 64; four waves, wave w
 // owns 64 weight rows (SwiGLU modes: 32 up rows and the 32 gate rows of the
@@ -26,8 +24,6 @@
 //      reads back the bytes of its own MFMA fragment (one 32-weight
 //      sub-block or block of one row per 32-column half) and decodes them
 //      with a replicated LDS table chunk by chunk between the MFMAs.
-//   B, bf16: each lane loads its fragments (32 values of one row per half)
-//      two steps ahead.
 // The MFMA's reduction order within a K step is permuted (lane half h takes
 // k = 32h .. 32h + 31) so that a lane's fragment is one contiguous sub-block;
 // A is read from LDS in the same order.
@@ -53,8 +49,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int N> struct Cnt { static constexpr int value = N; };
 
-enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_BF16 = 2, DN_BF16 = 3, ROUTER = 4,
-                UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7 };
+// (the numbers are the kernels' names in traces: k_gemm<0>, <1>, <5>, <6>, <7>)
+enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7 };
 // quantized B formats of the routed modes
 enum BFmt { BF_NONE, BF_Q3, BF_Q2S, BF_NL4, BF_Q2 };
 template <int MODE> constexpr int bfmt() {
@@ -64,10 +60,7 @@ template <int MODE> constexpr int bfmt() {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int kStages = 2;               // A stages in LDS
-// Token rows per tile: routed modes 64 (two blocks per CU, ragged expert
-// tails); the dense bf16 modes (shared expert, router) 128 (one block per
-// CU: every weight fragment serves twice the rows).
-template <int MODE> constexpr int tile_rows() { return (MODE == 2 || MODE == 3) ? 2 * BM : BM; }
+// Token rows per tile: 64 (two blocks per CU, ragged expert tails).
 constexpr int kLutDw = 2048;             // decode table dwords (8 KB)
 
 struct GemmArgs {
@@ -81,15 +74,13 @@ struct GemmArgs {
     const uint16_t* A;       // x16 / a16_perm / x / a_sh
     int lda;                 // row length of A (elements) = K
     int T;                   // tokens (shared / router row count)
-    const uint16_t* Bw;      // bf16 weights (shared / router)
     int N;                   // output columns (GEMM N)
     int K;                   // reduction length
     int half_n;              // up|gate: rows of the up half (I or I_s)
     int H, I;                // layer shape (routed record layout)
     int64_t dn_off;          // routed down: byte offset of the down matrix in a record
-    const float* bias;       // router bias or null
     uint16_t* out16;         // a16_perm / a_sh
-    float* out32;            // y_perm / y_sh / logits
+    float* out32;            // y_perm
     uint16_t* y16;           // routed down: y_perm as fp16 instead (null: fp32 to out32)
     int ldo;                 // output row length
     int npb;                 // routed: N tiles per block (consecutive, same M tile)
@@ -129,15 +120,15 @@ __device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t 
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(GemmArgs g) {
+__global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr int kBF = bfmt<MODE>();
     constexpr bool kQ3 = kBF == BF_Q3;
     constexpr bool kNL = kBF == BF_NL4;
     constexpr bool kB256 = kBF == BF_Q3 || kBF == BF_Q2S;     // 256-weight blocks: d on the partial sums
     constexpr bool kNat = MODE == UG_NL4;                      // natural K order, d per 32-weight block
-    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_BF16 || MODE == UG_Q2S || MODE == UG_NL4;
-    constexpr bool kRouted = kBF != BF_NONE;
-    constexpr int TBM = tile_rows<MODE>();
+    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_Q2S || MODE == UG_NL4;
+    static_assert(kBF != BF_NONE, "a routed mode");
+    constexpr int TBM = BM;
     constexpr int kAL = TBM * 8 / 256;              // A 16-byte loads per lane per K step
     constexpr int kSMX = TBM / 32;                  // 32-row groups per tile
 
@@ -147,35 +138,31 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8);
     // Q2S nibble -> (C2[lo], C2[hi]) and Q2 nibble -> (lo - 2, hi - 2), 32
     // copies (entry * 32 + lane % 32).
-    __shared__ __attribute__((aligned(8192))) uint32_t lut[kRouted ? kLutDw : 1];
+    __shared__ __attribute__((aligned(8192))) uint32_t lut[kLutDw];
     constexpr int kPer = kB256 ? 4 : 2;             // quantized B: K steps per period
     // bytes of a weight row per period
     constexpr int kRowB = kBF == BF_Q3 ? 104 : kBF == BF_Q2S ? 80 : kBF == BF_NL4 ? 72 : 40;
     constexpr int kUPR = kRowB / 8;                 // 8-byte units per row = per lane
-    __shared__ __attribute__((aligned(16))) uint8_t Bq[4][kRouted ? 64 * kRowB : 8];
+    __shared__ __attribute__((aligned(16))) uint8_t Bq[4][64 * kRowB];
 
     const int tid = threadIdx.x, lane = __lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
     // ---- tile coordinates (XCD-aware: the N tiles of one M tile share an
-    // XCD).  A routed block takes npb consecutive N tiles [nt0, nt1) of its M
-    // tile, one after the other, with the loads running on across them.
+    // XCD).  A block takes npb consecutive N tiles [nt0, nt1) of its M tile,
+    // one after the other, with the loads running on across them.
     const int NT = kSwi ? (g.half_n + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-    const int npb = kRouted ? g.npb : 1;
+    const int npb = g.npb;
     const int NGr = (NT + npb - 1) / npb;
     const int bid = blockIdx.x, xcd = bid & 7, li = bid >> 3;
     const int mt = (li / NGr) * 8 + xcd, nt0 = (li % NGr) * npb, nt1 = min(nt0 + npb, NT);
     int row0, rows, e = 0;
-    if (kRouted) {
+    {
         if (mt >= *g.ntiles) return;
         e = g.tiles[3 * mt];
         row0 = g.tiles[3 * mt + 1];
         rows = g.tiles[3 * mt + 2];
-    } else {
-        row0 = mt * TBM;
-        if (row0 >= g.T) return;
-        rows = min(TBM, g.T - row0);
     }
 
     // ---- A: lane's load i (0..kAL-1) is row (kAL w + i) * 8 + lane / 8,
@@ -187,7 +174,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         const int r = (kAL * w + i) * 8 + (lane >> 3);
         const int rc = min(r, rows - 1);
         int64_t src;
-        if (kRouted && kSwi) src = (int64_t)(g.perm[row0 + rc] / g.k);
+        if (kSwi) src = (int64_t)(g.perm[row0 + rc] / g.k);
         else src = row0 + rc;
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         asrc[i] = g.A + src * g.lda + c * 8;
@@ -231,7 +218,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     // or return zeros (buffer loads) and are never used.
     __amdgpu_buffer_rsrc_t wsrc;
     int rb_w = 0, mbase = 0;                         // row bytes, matrix offset in the record
-    if constexpr (kRouted) {
+    {
         const uint8_t* W = g.experts + (int64_t)e * g.estride;
         wsrc = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)g.estride, 0x00020000);
         constexpr int nwb = kB256 ? 256 : 32, nbb = kRowB / (kB256 ? 1 : 4);
@@ -311,22 +298,6 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
         }
     };
 
-    // ---- bf16 B: each lane loads its own fragments (32 values of one row
-    // per half: full 128-byte row segments per wave load) two steps ahead.
-    struct RawBF {
-        u32x4 v[2][4];
-    };
-    const uint8_t* bfrow[2];
-#pragma unroll
-    for (int sn = 0; sn < 2; ++sn) bfrow[sn] = reinterpret_cast<const uint8_t*>(g.Bw + (int64_t)brow_of(nt0, sn) * g.K);
-    auto load_bf = [&](int kt, RawBF& R) {
-#pragma unroll
-        for (int sn = 0; sn < 2; ++sn) {
-            const u32x4* vp = reinterpret_cast<const u32x4*>(bfrow[sn] + (kt * BK + 32 * hh) * 2);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) R.v[sn][kk] = vp[kk];
-        }
-    };
 
     // LDS byte address of a table entry = cb | entry << 7 (32 copies) or << 5
     // (NL4, 8 copies).
@@ -448,8 +419,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
 #pragma unroll
             for (int sn = 0; sn < 2; ++sn) {
                 if constexpr (kB256) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], tmp[sm][sn]);
-                else if constexpr (kRouted) acc[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], acc[sm][sn]);
-                else acc[sm][sn] = mfma32_bf16(fa[sm], fb[sn][kk], acc[sm][sn]);
+                else acc[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], acc[sm][sn]);
             }
     };
     // 256-weight blocks, at a block's end: acc += tmp * d / 128, tmp = 0.
@@ -511,7 +481,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                     if (!oc0) continue;
                     const float u = acc[sm][0][r], gv = acc[sm][1][r];
                     const uint32_t bf = f32_to_bf16(gv / (1.0f + expf(-gv)) * u);
-                    const uint16_t v = kRouted ? (uint16_t)f32_to_f16_bits(bf16_to_f32(bf)) : (uint16_t)bf;
+                    const uint16_t v = (uint16_t)f32_to_f16_bits(bf16_to_f32(bf));
                     g.out16[(int64_t)(r0 + m) * g.ldo + br0] = v;
                 } else {
 #pragma unroll
@@ -519,9 +489,8 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                         if (!(sn ? oc1 : oc0)) continue;
                         const int br = sn ? br1 : br0;
                         float v = acc[sm][sn][r];
-                        if (MODE == ROUTER && g.bias) v += g.bias[br];
                         const int64_t o = (int64_t)(r0 + m) * g.ldo + br;
-                        if (kRouted && g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
+                        if (g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
                         else g.out32[o] = v;
                     }
                 }
@@ -535,12 +504,10 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     // the freed registers; then, quantized: if step kt opens a period, its
     // bytes (loaded a period ago) go to the wave's area and the next period is
     // loaded; the lane's raw bytes of step kt are read, and per chunk kk the
-    // fragments are decoded and the MFMAs issued.  bf16: the MFMAs read the B
-    // registers of step kt directly, then B(kt + 2) is loaded into them.
-    // Barrier.  Past the last step, loads repeat the last step or read unused
+    // fragments are decoded and the MFMAs issued.  Barrier.  Past the last step, loads repeat the last step or read unused
     // bytes.
     const int nk = g.K / BK;
-    if constexpr (kRouted) {
+    {
         for (int i = tid; i < kLutDw; i += 256) {
             uint32_t v;
             if (kQ3) {
@@ -569,7 +536,7 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
     load_a(2 % nk, A0);
 
     auto run = [&](auto smc) {
-        if constexpr (kRouted) {
+        {
             // N tiles nt0 .. nt1 - 1 back to back: nk is even (or npb = 1), so the
             // A stages, A register slots and B periods carry on across tiles; A
             // rows are the same for every N tile, so A is loaded at k mod K.
@@ -647,42 +614,14 @@ __global__ void __launch_bounds__(256, tile_rows<MODE>() == BM ? 2 : 1) k_gemm(G
                     epilogue(nt, smc);
                 }
             }
-        } else {
-            RawBF B0, B1;
-            load_bf(0, B0);
-            load_bf(min(1, nk - 1), B1);
-            __syncthreads();                         // stage 0 written
-            // Ra: A(kt + 1); Rc: B(kt)
-            auto step = [&](int kt, RawA& Ra, RawBF& Rc) {
-                const int st = kt & 1;
-                put_a(st ^ 1, Ra);
-                load_a(min(kt + 3, nk - 1), Ra);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) mma_kk(st, kk, Rc.v, smc);
-                load_bf(min(kt + 2, nk - 1), Rc);
-                __syncthreads();
-            };
-            int kt = 0;
-            for (; kt + 2 <= nk; kt += 2) {
-                step(kt, A1, B0);
-                step(kt + 1, A0, B1);
-            }
-            if (kt < nk) step(kt, A1, B0);
-            epilogue(nt0, smc);
         }
     };
     // The loop is instantiated per count of live 32-row groups (ragged
     // expert tails skip the MFMAs of groups past their rows).
     const int nsm = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
-    if constexpr (kSMX == 4) {
-        if (nsm == 4) run(Cnt<4>{});
-        else if (nsm == 3) run(Cnt<3>{});
-        else if (nsm == 2) run(Cnt<2>{});
-        else run(Cnt<1>{});
-    } else {
-        if (nsm == 2) run(Cnt<2>{});
-        else run(Cnt<1>{});
-    }
+    static_assert(kSMX == 2, "64-row tiles");
+    if (nsm == 2) run(Cnt<2>{});
+    else run(Cnt<1>{});
 
 }
 
@@ -694,15 +633,6 @@ static unsigned gemm_grid(int n_tiles, int m_tiles) {
 }
 static int swi_tiles(int half_n) { return (half_n + BN / 2 - 1) / (BN / 2); }
 static int col_tiles(int n) { return (n + BN - 1) / BN; }
-
-void launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
-                        const float* bias, float* logits, hipStream_t st) {
-    GemmArgs a{};
-    a.A = x; a.lda = H; a.T = T; a.Bw = w_r; a.N = E; a.K = H; a.bias = bias;
-    a.out32 = logits; a.ldo = E;
-    const int mtiles = (T + BM - 1) / BM;
-    k_gemm<ROUTER><<<gemm_grid(col_tiles(E), mtiles), 256, 0, st>>>(a);
-}
 
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
@@ -731,19 +661,6 @@ void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* ti
     const unsigned grid = gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles);
     if (fmt == kFmtNL4) k_gemm<DN_NL4><<<grid, 256, 0, st>>>(a);
     else k_gemm<DN_Q2><<<grid, 256, 0, st>>>(a);
-}
-
-void launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
-                        const uint16_t* sh_down, int Is, uint16_t* a_sh, float* y_sh,
-                        hipStream_t st) {
-    const int mtiles = (T + 2 * BM - 1) / (2 * BM);
-    GemmArgs a{};
-    a.A = x; a.lda = H; a.T = T; a.Bw = sh_ug; a.N = 2 * Is; a.K = H; a.half_n = Is;
-    a.out16 = a_sh; a.ldo = Is;
-    k_gemm<UG_BF16><<<gemm_grid(swi_tiles(Is), mtiles), 256, 0, st>>>(a);
-    GemmArgs b{};
-    b.A = a_sh; b.lda = Is; b.T = T; b.Bw = sh_down; b.N = H; b.K = Is; b.out32 = y_sh; b.ldo = H;
-    k_gemm<DN_BF16><<<gemm_grid(col_tiles(H), mtiles), 256, 0, st>>>(b);
 }
 
 }  // namespace moe
