@@ -377,7 +377,7 @@ __global__ void k_combine(const YT* __restrict__ y_perm, const int32_t* __restri
 
 // ---------------------------------------------------------------- RMSNorm
 
-// One workgroup (256 threads) per token row.
+// One workgroup (256 threads) per token row; the general form (any H).
 __global__ void k_rmsnorm_residual(float* __restrict__ h, const float* __restrict__ delta,
                                    const float* __restrict__ gamma, float eps, int H,
                                    uint16_t* __restrict__ normed) {
@@ -403,6 +403,62 @@ __global__ void k_rmsnorm_residual(float* __restrict__ h, const float* __restric
     uint16_t* nrow = normed + (int64_t)blockIdx.x * H;
     for (int i = threadIdx.x; i < H; i += blockDim.x)
         nrow[i] = (uint16_t)f32_to_bf16(gamma[i] * (row[i] * r));
+}
+
+// The same for rows of H = 4m <= 1024 NV floats with 16-byte aligned operands:
+// each thread keeps its NV float4 of the row in registers between the sum of
+// squares and the scaling, so the row is read once and written once (with the
+// bf16 output as 8-byte stores).
+template <int NV, bool DELTA>
+__global__ void __launch_bounds__(256) k_rmsnorm_residual_v(float* __restrict__ h, const float* __restrict__ delta,
+                                                            const float* __restrict__ gamma, float eps, int H,
+                                                            uint16_t* __restrict__ normed) {
+    __shared__ float s_red[4];
+    const int n4 = H >> 2;
+    float4* row = reinterpret_cast<float4*>(h + (int64_t)blockIdx.x * H);
+    float4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        v[j] = i < n4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (DELTA) {
+        const float4* drow = reinterpret_cast<const float4*>(delta + (int64_t)blockIdx.x * H);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = threadIdx.x + 256 * j;
+            if (i < n4) {
+                const float4 d = drow[i];
+                v[j].x += d.x;
+                v[j].y += d.y;
+                v[j].z += d.z;
+                v[j].w += d.w;
+                row[i] = v[j];
+            }
+        }
+    }
+    if (!normed) return;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ss = wave_sum_f32(ss);
+    if (__lane_id() == 0) s_red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    const float4* g4 = reinterpret_cast<const float4*>(gamma);
+    uint2* nrow = reinterpret_cast<uint2*>(normed + (int64_t)blockIdx.x * H);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i < n4) {
+            const float4 g = g4[i];
+            uint2 o;
+            o.x = f32_to_bf16(g.x * (v[j].x * r)) | (f32_to_bf16(g.y * (v[j].y * r)) << 16);
+            o.y = f32_to_bf16(g.z * (v[j].z * r)) | (f32_to_bf16(g.w * (v[j].w * r)) << 16);
+            nrow[i] = o;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -460,7 +516,18 @@ void launch_combine16(const uint16_t* y_perm16, const int32_t* inv, const float*
 
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st) {
-    k_rmsnorm_residual<<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    const bool vec = (H & 3) == 0 && H <= 8192 && a16(h) && (!delta || a16(delta)) &&
+                     (!normed || (a16(gamma) && ((uintptr_t)normed & 7) == 0));
+    if (!vec) {
+        k_rmsnorm_residual<<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+    } else if (H <= 4096) {
+        if (delta) k_rmsnorm_residual_v<4, true><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+        else k_rmsnorm_residual_v<4, false><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+    } else {
+        if (delta) k_rmsnorm_residual_v<8, true><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+        else k_rmsnorm_residual_v<8, false><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+    }
 }
 
 }  // namespace moe
