@@ -149,17 +149,23 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // ---- tile coordinates (XCD-aware: the N tiles of one M tile share an
-    // XCD).  A block takes npb consecutive N tiles [nt0, nt1) of its M tile,
-    // one after the other, with the loads running on across them.
+    // ---- tile coordinates (XCD-aware).  Blocks are dealt to the 8 XCDs in
+    // turn (XCD = block id mod 8); XCD x takes the contiguous M tiles
+    // [x mpx, (x + 1) mpx), mpx = ceil(ntiles / 8), in order, so the M tiles of
+    // one expert (and the N tiles of one M tile) run together under one L2 and
+    // share its copy of the expert's weights.  A block takes npb consecutive N
+    // tiles [nt0, nt1) of its M tile, one after the other, with the loads
+    // running on across them.  The grid holds 8 ceil(max_tiles / 8) NGr
+    // blocks, so every (M tile, N group) pair is covered once.
     const int NT = kSwi ? (g.half_n + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     const int npb = g.npb;
     const int NGr = (NT + npb - 1) / npb;
     const int bid = blockIdx.x, xcd = bid & 7, li = bid >> 3;
-    const int mt = (li / NGr) * 8 + xcd, nt0 = (li % NGr) * npb, nt1 = min(nt0 + npb, NT);
+    const int ntl = *g.ntiles, mpx = (ntl + 7) >> 3;
+    const int mt = xcd * mpx + li / NGr, nt0 = (li % NGr) * npb, nt1 = min(nt0 + npb, NT);
     int row0, rows, e = 0;
     {
-        if (mt >= *g.ntiles) return;
+        if (li / NGr >= mpx || mt >= ntl) return;
         e = g.tiles[3 * mt];
         row0 = g.tiles[3 * mt + 1];
         rows = g.tiles[3 * mt + 2];
