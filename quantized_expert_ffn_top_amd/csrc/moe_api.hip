@@ -199,8 +199,19 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max) {
     if (check_desc(desc) != MOE_OK || T_max < 1 || T_max > kMaxT) return 0;
-    return layout(desc->hidden, desc->inter, desc->n_experts, desc->top_k, desc->shared_inter, T_max,
-                  std_formats(desc)).total;
+    // The bandwidth path (T <= kDecMaxT) lays the workspace out differently
+    // from the grouped GEMMs (router partial planes, one tile per expert), so
+    // the layout size is not monotone in T: take the largest over every
+    // batch a call may bring.
+    size_t m = 0;
+    auto at_T = [&](int T) {
+        const size_t s = layout(desc->hidden, desc->inter, desc->n_experts, desc->top_k,
+                                desc->shared_inter, T, std_formats(desc)).total;
+        if (s > m) m = s;
+    };
+    for (int T = 1; T <= T_max && T <= kDecMaxT; ++T) at_T(T);
+    at_T(T_max);
+    return m;
 }
 
 moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,

@@ -34,8 +34,8 @@ particular range are overwritten bit-wise --
   a valid index stream); d (bytes 96..97) = 0x2000 | 10 random bits, i.e. a
   binary16 in [2^-7, 2^-6), the scale a round-to-nearest encoding of
   N(0, 0.02) weights produces; sub-scale bytes 98..101 get nibbles 4..7
-  ("rtn" mode, the range round-to-nearest gives) or any nibble ("full" mode,
-  negative sub-scales included); bytes 102..103 = 0.
+  ("rtn" mode, the range round-to-nearest gives) or any nibble ("full" and
+  "wide" modes, negative and zero sub-scales included); bytes 102..103 = 0.
   NL4-32 block: d (bytes 0..1) = 0x2800 | 10 random bits, a binary16 in
   [2^-5, 2^-4); index bytes uniform random.
   Q2S-256 block (mixed-format layers): index bytes [0,64) uniform random; d
@@ -44,7 +44,11 @@ particular range are overwritten bit-wise --
   Q2-32 block: d (bytes 0..1) = 0x2400 | 10 random bits, in [2^-6, 2^-5);
   index bytes uniform random.
   (Each d range is the one a round-to-nearest encoding of N(0, 0.02) weights
-  gives for that codec.)
+  gives for that codec.)  "wide" mode instead draws each block's d binade
+  from four (WIDE_D_EXPONENTS: subnormal or zero, [2^-10, 2^-9), the
+  round-to-nearest binade, a large one), picked by two of d's own random
+  mantissa bits, so that the decoders see the whole range of the field;
+  "small" mode puts every d in [2^-12, 2^-11).
 The counter hash is MurmurHash3's 32-bit finaliser (fmix32, Austin Appleby,
 public domain), applied twice with per-(seed, layer, expert) keys.
 """
@@ -180,44 +184,60 @@ def hash_bytes(k1, k2, nbytes, device="cpu"):
 # expert records by code sampling
 # --------------------------------------------------------------------------
 
-def _fix_q3s_fields(blk, mode):
-    """blk: uint8 [n, 104] view; set d, sub-scale and reserved fields."""
-    blk[:, 97] = (blk[:, 97] & 0x03) | 0x20
+MODES = ("rtn", "full", "wide", "small")
+
+# binary16 exponent fields of d in "wide" mode, per codec: a subnormal (or
+# zero) d, d in [2^-10, 2^-9), the binade a round-to-nearest encoding of
+# N(0, 0.02) weights gives, and a large binade (the largest that keeps the
+# SwiGLU outputs and the down rows of N(0, 1) tokens far below 65504).
+WIDE_D_EXPONENTS = {FMT_Q3S256: (0, 5, 8, 12), FMT_NL4_32: (0, 5, 10, 13),
+                    FMT_Q2S256: (0, 5, 7, 12), FMT_Q2_32: (0, 5, 9, 12)}
+# exponent field of d in "small" mode, every codec: d in [2^-12, 2^-11), where
+# d * |table entry| / 128 of the smaller entries falls below binary16's
+# smallest normal
+SMALL_D_EXPONENT = 3
+# exponent field of d in "rtn" and "full" mode
+RTN_D_EXPONENT = {FMT_Q3S256: 8, FMT_NL4_32: 10, FMT_Q2S256: 7, FMT_Q2_32: 9}
+
+
+def _set_d(hi, fmt, mode):
+    """hi: uint8 view of the high byte of d (random on entry).  Keeps the two
+    mantissa bits it holds and writes the exponent field: the codec's
+    round-to-nearest binade, or in "wide" mode one of WIDE_D_EXPONENTS picked
+    by those two mantissa bits."""
+    low = hi & 0x03
+    if mode == "wide":
+        ex = torch.tensor(WIDE_D_EXPONENTS[fmt], dtype=torch.uint8, device=hi.device)
+        hi.copy_(low | (ex[low.long()] << 2))
+    elif mode == "small":
+        hi.copy_(low | (SMALL_D_EXPONENT << 2))
+    else:
+        hi.copy_(low | (RTN_D_EXPONENT[fmt] << 2))
+
+
+def _set_subscales(sb, mode):
+    """sb: uint8 [n, 4] view of the eight sub-scale nibbles: 4..7 in "rtn"
+    mode (the range round-to-nearest gives), any nibble (-8..7) otherwise
+    ("full", "wide", "small")."""
     if mode == "rtn":
-        blk[:, 98:102] = (blk[:, 98:102] & 0x33) | 0x44
-    elif mode != "full":
-        raise ValueError("mode must be 'rtn' or 'full'")
-    blk[:, 102:104] = 0
-
-
-def _fix_nl4_fields(blk):
-    blk[:, 1] = (blk[:, 1] & 0x03) | 0x28
-
-
-def _fix_q2s_fields(blk, mode):
-    """blk: uint8 [n, 80] view; set d, sub-scale and reserved fields."""
-    blk[:, 65] = (blk[:, 65] & 0x03) | 0x1C
-    if mode == "rtn":
-        blk[:, 66:70] = (blk[:, 66:70] & 0x33) | 0x44
-    elif mode != "full":
-        raise ValueError("mode must be 'rtn' or 'full'")
-    blk[:, 70:80] = 0
-
-
-def _fix_q2_fields(blk):
-    blk[:, 1] = (blk[:, 1] & 0x03) | 0x24
+        sb.copy_((sb & 0x33) | 0x44)
 
 
 def _fix_fields(fmt, raw, mode):
+    """Set the d, sub-scale and reserved fields of every block of one codec."""
+    if mode not in MODES:
+        raise ValueError("mode must be one of %s" % (MODES,))
     blk = raw.view(-1, BLOCKS[fmt][1])
     if fmt == FMT_Q3S256:
-        _fix_q3s_fields(blk, mode)
+        _set_d(blk[:, 97], fmt, mode)
+        _set_subscales(blk[:, 98:102], mode)
+        blk[:, 102:104] = 0
     elif fmt == FMT_Q2S256:
-        _fix_q2s_fields(blk, mode)
-    elif fmt == FMT_NL4_32:
-        _fix_nl4_fields(blk)
-    else:
-        _fix_q2_fields(blk)
+        _set_d(blk[:, 65], fmt, mode)
+        _set_subscales(blk[:, 66:70], mode)
+        blk[:, 70:80] = 0
+    else:                                           # NL4-32, Q2-32: d first
+        _set_d(blk[:, 1], fmt, mode)
 
 
 def expert_record(shape, seed, layer, e, device="cpu", mode="rtn"):

@@ -48,6 +48,27 @@ def test_workspace_size_monotone_and_rejects_bad_desc():
     assert Q.moe_workspace_size(d, 0) == 0
 
 
+@pytest.mark.parametrize("shape", [
+    (3072, 512, 512, 1, 0), (3072, 512, 512, 4, 0), (3072, 512, 512, 10, 512),
+    (256, 64, 1024, 1, 0), (256, 64, 1024, 32, 0), (8192, 64, 16, 2, 64), (512, 192, 24, 3, 64)])
+@pytest.mark.parametrize("T_max", [1, 5, 16, 17, 20, 64])
+def test_workspace_size_bounds_every_smaller_batch(shape, T_max):
+    """moe_workspace_size(desc, T_max) is enough for every T <= T_max: the
+    layer call's own workspace check (a host check that runs before any
+    device call) accepts that size for each T, so the call gets past it and
+    stops only at the device check (no GPU here)."""
+    H, I, E, k, Is = shape
+    d = Q.desc(H, I, E, k, Is)
+    size = Q.moe_workspace_size(d, T_max)
+    assert size > 0
+    rec = 2 * I * (H // 256) * 104 + H * (I // 32) * 18
+    w = _w(stride=(rec + 15) // 16 * 16, shared=(P, P) if Is else (None, None))
+    for T in range(1, T_max + 1):
+        st = _fwd(d, w, T=T, ws_bytes=size)
+        assert st not in (0, 5), (T, st)
+        assert _fwd(d, w, T=T, ws_bytes=256) == 5
+
+
 def _fwd(d, w, T=4, ws_bytes=1 << 30, x=P, y=P2, logits=None):
     lib = Q.load()
     return lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), x, T, logits, y, None, None,

@@ -50,8 +50,8 @@ def test_tiny_layer(T):
     assert_close(y, ref["y"], "tiny T=%d" % T)
 
 
-def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
-    lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev())
+def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL, mode="rtn"):
+    lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev(), mode=mode)
     x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
                sh.down_fmt)
@@ -65,14 +65,84 @@ def _real_case(T, seed, zipf_s=1.0, sample=None, sh=synth.REAL):
     mism = np.where((np.sort(ids, axis=1) != np.sort(ref_ids, axis=1)).any(axis=1))[0]
     assert len(mism) <= max(1, T // 1000), "routing differs on %d tokens" % len(mism)
     rows = np.arange(T) if sample is None else np.asarray(sample)
-    cache = ExpertCache(sh, lambda e: synth.expert_record(sh, seed, 0, e).numpy())
+    cache = ExpertCache(sh, lambda e: synth.expert_record(sh, seed, 0, e, mode=mode).numpy())
     ref = OM.layer_forward(xs[rows], sh.top_k, cache, sh.n_experts, logits=L[rows],
                            shared=real_shared_np(lay) if sh.shared_inter else None,
                            force_ids=ids[rows])
     assert np.abs(w[rows] - ref["w"]).max() <= 1e-5
-    assert_close(y[rows], ref["y"], "real T=%d" % T)
+    assert_close(y[rows], ref["y"], "real T=%d %s" % (T, mode))
     assert np.all(np.isfinite(y))
     return y, ids
+
+
+# The decoders on the whole range of their fields: every sub-scale nibble
+# (-8..7, zero included) and, per block, d from four binades (subnormal or
+# zero, [2^-10, 2^-9), the round-to-nearest binade, a large one) -- "wide";
+# or every d in [2^-12, 2^-11), where the small table entries times d fall
+# below fp16's normal range -- "small".  Both regimes of the standard formats
+# (T <= 16: bandwidth kernels; T >= 17: grouped GEMMs) and every mode of the
+# mixed formats.
+@pytest.mark.parametrize("mode", ["wide", "small"])
+@pytest.mark.parametrize("T", [1, 8, 17, 64])
+def test_real_layer_full_field_range(T, mode):
+    _real_case(T, seed=21, mode=mode)
+
+
+@pytest.mark.parametrize("ug,dn", [(2, 3), (4, 5), (3, 3), (2, 5), (4, 3), (3, 5)],
+                         ids=["q3s_nl4", "q2s_q2", "nl4_nl4", "q3s_q2", "q2s_nl4", "nl4_q2"])
+@pytest.mark.parametrize("mode", ["wide", "small"])
+@pytest.mark.parametrize("T", [5, 40])
+def test_mixed_format_layer_full_field_range(T, mode, ug, dn):
+    _real_case(T, seed=22, sh=synth.Shape(512, 128, 24, 3, 64, ug, dn), mode=mode)
+
+
+def _prefill_all_tokens(T, seed, zipf_s, mode="rtn", sh=synth.REAL):
+    """Every output row of a prefill-sized layer against the oracle, whose
+    routed experts run one at a time in a process pool (tests/_oracle_pool)."""
+    import sys
+    import time
+    from tests import _oracle_pool
+    t0 = time.time()
+
+    def note(what):
+        print("[prefill all tokens] T=%d zipf %.1f: %s, %.1f s" % (T, zipf_s, what, time.time() - t0),
+              file=sys.__stderr__, flush=True)
+
+    note("start")
+    lay = synth.real_layer(sh, seed, 0, zipf_s=zipf_s, device=dev(), mode=mode)
+    x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
+               sh.down_fmt)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    note("inputs on the GPU")
+    y, ids, w = _run_layer(d, wts, x)
+    note("layer done on the GPU")
+    del lay.experts
+    torch.cuda.empty_cache()
+    xs = bf16_np(x)
+    L = OM.router_logits(xs, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+    assert ids_valid_topk(ids, L, sh.top_k)
+    ref_ids = OM.topk_ids_fast(L, sh.top_k)
+    flips = int((np.sort(ids, axis=1) != np.sort(ref_ids, axis=1)).any(axis=1).sum())
+    assert flips <= max(1, T // 1000), "routing differs on %d tokens" % flips
+    ref_w = OM.softmax_selected(L, ids.astype(np.int64))
+    assert np.abs(w - ref_w).max() <= 1e-5
+    offsets, perm, inv = OM.permute(ids, sh.n_experts)
+    note("routing checked")
+    y_perm = _oracle_pool.routed_outputs(sh, seed, 0, mode, T, offsets, perm, sh.top_k)
+    _, ys = OM.ffn(xs, *real_shared_np(lay))
+    ref = OM.combine(y_perm, inv, ref_w, ys)
+    print("[parity] prefill T=%d zipf %.1f: %d near-tie routing flips" % (T, zipf_s, flips))
+    assert_close(y, ref, "prefill all %d tokens, zipf %.1f %s" % (T, zipf_s, mode))
+    # the tile mapping: every 64-row tile of every expert holds rows within the bar
+    err = np.abs(y - ref).max(axis=1) / np.sqrt((ref * ref).mean())
+    assert err.max() <= 1e-2
+
+
+@pytest.mark.parametrize("zipf_s", [1.0, 0.0], ids=["zipf", "uniform"])
+def test_real_prefill_all_tokens(zipf_s):
+    _prefill_all_tokens(8192, 3, zipf_s)
 
 
 @pytest.mark.parametrize("T", [1, 3, 5, 8, 16])

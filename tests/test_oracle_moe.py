@@ -272,8 +272,56 @@ def test_stack_step_is_residual():
     assert np.array_equal(out, h)
 
 
+def test_stack_step_pre_norm_hand_values():
+    """Pre-norm residual step h + f(bf16(gamma * h / sqrt(mean(h^2) + eps))) with
+    a non-zero layer f(z) = 2 z + 1, on two rows worked out by hand:
+      row 0: h = (2, 2, 2, 2): mean h^2 = 4, sqrt(4 + 1e-6) = 2.00000025, so
+             h / rms = 0.999999875 each, which bf16 rounds to 1; times gamma
+             (1, 0.5, 2, 1.5) -> z = (1, 0.5, 2, 1.5); f(z) = (3, 2, 5, 4);
+             h + f(z) = (5, 4, 7, 6).
+      row 1: h = (3, -3, 3, -3): rms = 3 (to 1e-7), h / rms -> (1, -1, 1, -1);
+             z = (1, -0.5, 2, -1.5); f(z) = (3, 0, 5, -2); h + f(z) = (6, -3, 8, -5).
+    A post-norm step norm(h + f(h)), the step h + f(h) without the norm, and
+    a step that drops gamma or the bf16 rounding all give other values."""
+    h = np.array([[2.0, 2.0, 2.0, 2.0], [3.0, -3.0, 3.0, -3.0]])
+    gamma = np.array([1.0, 0.5, 2.0, 1.5])
+    seen = []
+
+    def f(z):
+        seen.append(np.array(z))
+        return 2.0 * z + 1.0
+
+    out = M.stack_step(h, gamma, 1e-6, f)
+    assert np.array_equal(seen[0], [[1.0, 0.5, 2.0, 1.5], [1.0, -0.5, 2.0, -1.5]])
+    assert np.array_equal(out, [[5.0, 4.0, 7.0, 6.0], [6.0, -3.0, 8.0, -5.0]])
+    # the layer input is rounded to bf16: a gain of 1 + 2^-9 vanishes, 1 + 2^-7 stays
+    z = M.rmsnorm_bf16(np.array([[2.0, 2.0]]), np.array([1.0 + 2.0 ** -9, 1.0 + 2.0 ** -7]), 1e-6)
+    assert np.array_equal(z, [[1.0, 1.0 + 2.0 ** -7]])
+
+
 def test_metrics():
     ref = np.array([3.0, 4.0])
     assert M.rel_l2(ref, ref) == 0.0
     assert abs(M.rel_l2(np.array([3.0, 4.5]), ref) - 0.1) < 1e-15
     assert abs(M.max_abs_over_rms(np.array([3.0, 4.5]), ref) - 0.5 / math.sqrt(12.5)) < 1e-15
+
+
+def test_oracle_pool_matches_serial_expert_ffn():
+    """The process-pool evaluation of the routed experts (used for full-size
+    parity) gives the serial oracle's y_perm (up to the BLAS summation order
+    of a different thread count)."""
+    import synth
+    from oracle import formats as OF
+    from tests import _oracle_pool
+    from tests._helpers import bf16_np
+    sh = synth.Shape(512, 128, 24, 3, 64, 2, 5)
+    T, seed = 40, 5
+    x = bf16_np(synth.tokens_bf16(T, sh.hidden, seed))
+    L = np.random.default_rng(3).normal(size=(T, sh.n_experts))
+    ids = M.topk_ids_fast(L, sh.top_k)
+    offsets, perm, inv = M.permute(ids, sh.n_experts)
+    get = lambda e: OF.expert_matrices(synth.expert_record(sh, seed, 0, e, mode="wide").numpy(),
+                                       sh.hidden, sh.inter, sh.upgate_fmt, sh.down_fmt)
+    _, ref = M.expert_ffn_perm(x, offsets, perm, sh.top_k, get)
+    got = _oracle_pool.routed_outputs(sh, seed, 0, "wide", T, offsets, perm, sh.top_k)
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
