@@ -244,7 +244,8 @@ def main():
         x = synth.tokens_bf16(Tp, sh.hidden, 3, 0).to(dev)
         ms = time_steps(Tp, x, args.prefill_steps, 2, 1)
         kd = time_kernels(Tp, x, 4, 1, 12)
-        names = ["router", "topk", "to_f16", "permute", "shared", "upgate", "down", "combine"]
+        names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate",
+                 "down", "combine"]
         flops = FLOP_PER_TOKEN * Tp
         ug_flops = 2.0 * Tp * K * 2 * I * H
         dn_flops = 2.0 * Tp * K * I * H
@@ -355,7 +356,8 @@ def stack_prefill(args, Q, synth, torch, np, dev):
     torch.cuda.synchronize()
     marks = one_pass(evs)
     torch.cuda.synchronize()
-    names = ["router", "topk", "to_f16", "permute", "shared", "upgate", "down", "combine"]
+    names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate", "down",
+             "combine"]
     fmt_name = {2: "q3s256", 3: "nl4_32", 4: "q2s256", 5: "q2_32"}
     ug_t, dn_t, ug_by, dn_by, tot = {}, {}, {}, {}, {}
     for l in range(nl):

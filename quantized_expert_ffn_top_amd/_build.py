@@ -16,9 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["moe_api.hip", "moe_kernels_small.hip", "moe_kernels_decode.hip",
-           "moe_kernels_gemm.hip", "moe_blas.hip"]
-# the plain bf16 GEMMs of the grouped-GEMM path use rocBLAS
-LINK = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+           "moe_kernels_gemm.hip", "moe_kernels_dense.hip"]
+LINK = []
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

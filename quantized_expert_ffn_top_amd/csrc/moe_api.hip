@@ -59,7 +59,7 @@ size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 // ---- workspace layout for one (shape, T)
 struct Ws {
     size_t x16, shp, logits, ids, w, offsets, perm, inv, tiles, ntiles, a16, a_sh, y_perm,
-        y_sh, hist, sh_ug32, total;
+        y_sh, hist, total;
     int max_tiles;
 };
 
@@ -109,9 +109,6 @@ Ws layout(int H, int I, int E, int k, int Is, int T, bool std_fmt) {
     s.y_perm = take(n * H * 4);
     s.y_sh = take((size_t)T * H * 4);
     s.hist = take((size_t)((T + 63) / 64) * E * 4);
-    // the shared up|gate product (fp32) before its SwiGLU, for the grouped-GEMM
-    // path and moe_expert_ffn (which takes that path at every T)
-    s.sh_ug32 = take(Is <= 0 ? 0 : (size_t)T * 2 * Is * 4);
     s.total = off;
     return s;
 }
@@ -231,8 +228,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
     if (T <= kDecMaxT) {
         launch_dec_stage1(x, T, H, E, w_r, b, logits, nullptr, 0, nullptr, nullptr, 1, st);
     } else {
-        const int bs = launch_gemm_router(x, T, H, E, w_r, b, logits, st);
-        if (bs != 0) return fail(MOE_ERR_HIP, "moe_router_logits: rocBLAS status " + std::to_string(bs));
+        launch_dense_router_shared(x, T, H, E, w_r, b, logits, nullptr, 0, nullptr, st);
     }
     return launched("moe_router_logits");
 }
@@ -312,8 +308,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     launch_to_f16(x, x16, (int64_t)T * H, st);
     launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
     if (do_sh) {
-        const int bs = launch_gemm_shared(x, T, H, sug, sdn, Is, at<float>(ws, L.sh_ug32), ash, shared_y, st);
-        if (bs != 0) return fail(MOE_ERR_HIP, "moe_expert_ffn: rocBLAS status " + std::to_string(bs));
+        launch_dense_router_shared(x, T, H, E, nullptr, nullptr, nullptr, sug, Is, ash, st);
+        launch_dense_shared_down(ash, T, Is, sdn, H, shared_y, st);
     }
     launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16,
                        desc->upgate_fmt, st);
@@ -420,12 +416,14 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
                         Is, yp, ysh, n_cu, st);
         mk->mark();
     } else {
-        const float* L_use = logits_or_null;
-        if (!L_use) {
-            const int bs = launch_gemm_router(x, T, H, E, (const uint16_t*)wts->router_w, wts->router_b, lg, st);
-            if (bs != 0) return fail(MOE_ERR_HIP, "moe_layer_forward: rocBLAS status " + std::to_string(bs));
+        // router logits (none given) and the shared expert's SwiGLU
+        // activations: one launch, both read only x
+        const float* L_use = logits_or_null ? logits_or_null : lg;
+        if (!logits_or_null || has_sh) {
+            launch_dense_router_shared(x, T, H, E,
+                                       logits_or_null ? nullptr : (const uint16_t*)wts->router_w,
+                                       wts->router_b, lg, sug, Is, ash, st);
             mk->mark();
-            L_use = lg;
         }
         launch_topk(L_use, T, E, k, ids, wv, topk_ids_out, topk_w_out, st);
         mk->mark();
@@ -434,8 +432,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         launch_permute_large(ids, T, k, E, kGemmBM, hist, offs, perm, inv, tiles, nt, st);
         mk->mark();
         if (has_sh) {
-            const int bs = launch_gemm_shared(x, T, H, sug, sdn, Is, at<float>(ws, L.sh_ug32), ash, ysh, st);
-            if (bs != 0) return fail(MOE_ERR_HIP, "moe_layer_forward: rocBLAS status " + std::to_string(bs));
+            launch_dense_shared_down(ash, T, Is, sdn, H, ysh, st);
             mk->mark();
         }
         launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16,

@@ -67,10 +67,6 @@ void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* til
                      float* y_perm, float* y_sh, int n_cu, hipStream_t st);
 
 // ---- grouped-GEMM path (moe_kernels_gemm.hip)
-// Router logits and the shared expert of the grouped-GEMM path: library bf16
-// GEMMs (rocBLAS) plus bias / SwiGLU kernels.  Return 0, or the rocBLAS status.
-int launch_gemm_router(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
-                       const float* bias, float* logits, hipStream_t st);
 // fmt: the up|gate format (Q3S-256, Q2S-256 or NL4-32)
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
@@ -83,9 +79,15 @@ void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* ti
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
                       int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
                       hipStream_t st);
-// ug32: fp32 scratch of T * 2 Is (the up|gate product before the SwiGLU)
-int launch_gemm_shared(const uint16_t* x, int T, int H, const uint16_t* sh_ug,
-                       const uint16_t* sh_down, int Is, float* ug32, uint16_t* a_sh, float* y_sh,
-                       hipStream_t st);
+
+// ---- dense bf16 products of the grouped-GEMM path (moe_kernels_dense.hip)
+// One launch: router logits [T][E] (+ bias) if w_r is not null, and the
+// shared expert's SwiGLU activations a_sh bf16 [T][Is] if sh_ug is not null.
+void launch_dense_router_shared(const uint16_t* x, int T, int H, int E, const uint16_t* w_r,
+                                const float* bias, float* logits, const uint16_t* sh_ug, int Is,
+                                uint16_t* a_sh, hipStream_t st);
+// The shared expert's down projection: y_sh fp32 [T][H] = a_sh W_down^T.
+void launch_dense_shared_down(const uint16_t* a_sh, int T, int Is, const uint16_t* sh_down, int H,
+                              float* y_sh, hipStream_t st);
 
 }  // namespace moe

@@ -1,6 +1,6 @@
 // Grouped-GEMM path of the layer (prefill-sized batches).  One kernel
 // template, five uses (the routed experts; the router and the shared expert
-// are plain bf16 GEMMs, done by the library in moe_blas.hip):
+// are dense bf16 products, in moe_kernels_dense.hip):
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
 //           (fp16), B = Q3S-256 weights, epilogue SwiGLU
 //   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
