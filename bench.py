@@ -158,7 +158,7 @@ def main():
     torch.cuda.synchronize()
     print("# generated %d layers in %.1f s" % (args.layers, time.time() - t0), file=sys.stderr)
 
-    ws = torch.empty(Q.moe_workspace_size(d, 8192), dtype=torch.uint8, device=dev)
+    ws = Q.workspace(d, 8192, dev)
     stream = torch.cuda.current_stream(dev)
 
     def distinct_experts(T, x):
@@ -310,7 +310,7 @@ def stack_prefill(args, Q, synth, torch, np, dev):
     gb = sum(L.experts.numel() for L in layers) / 1e9
     print("# stack: generated %d layers (%.1f GB of packed experts) in %.1f s" % (
         nl, gb, time.time() - t0), file=sys.stderr)
-    ws = torch.empty(max(Q.moe_workspace_size(dd, T) for dd in descs), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(Q.moe_workspace_size(dd, T) for dd in descs), dtype=torch.uint8, device=dev)
     x0 = synth.tokens_bf16(T, H, seed).float().to(dev)
     h = torch.empty_like(x0)
     normed = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -419,7 +419,7 @@ def stack_decode(args, Q, synth, torch, np, dev):
     print("# stack decode: generated %d layers (%.1f GB of packed experts) in %.1f s" % (
         nl, gb, time.time() - t0), file=sys.stderr)
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
-    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev)
+    ws = Q.workspace(d, T, dev)
     x0 = synth.tokens_bf16(T, H, seed).float().to(dev)
     h = torch.empty_like(x0)
     normed = torch.empty((T, H), dtype=torch.bfloat16, device=dev)

@@ -128,6 +128,12 @@ def moe_workspace_size(d, T_max):
     return int(load().moe_workspace_size(ctypes.byref(d), T_max))
 
 
+def workspace(d, T_max, device):
+    """A workspace for every batch of up to T_max tokens of layers shaped like
+    d (zero-filled, so that nothing of an earlier allocation leaks in)."""
+    return torch.zeros(moe_workspace_size(d, T_max), dtype=torch.uint8, device=device)
+
+
 def moe_router_logits(x, w_r, b, logits, ws=None):
     T, H = x.shape
     E = w_r.shape[0]

@@ -30,7 +30,7 @@ def _run_layer(d, wts, x, logits=None):
     y = torch.empty((T, d.hidden), dtype=torch.float32, device=dev())
     ids = torch.empty((T, d.top_k), dtype=torch.int32, device=dev())
     w = torch.empty((T, d.top_k), dtype=torch.float32, device=dev())
-    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+    ws = Q.workspace(d, T, dev())
     Q.moe_layer_forward(d, wts, x, y, ws, logits=logits, topk_ids_out=ids, topk_w_out=w)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
@@ -297,7 +297,7 @@ def test_stack_three_layers_teacher_forced():
     h_ref = h.double().cpu().numpy()
     normed = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=dev())
     y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev())
-    ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+    ws = Q.workspace(d, T, dev())
     for l in range(3):
         lay = synth.real_layer(sh, seed, l, zipf_s=1.0, device=dev())
         gamma = synth.norm_gain(sh.hidden, seed, l).to(dev())
@@ -352,7 +352,7 @@ def test_mixed_stack_prefill_sampled():
         d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
                    sh.down_fmt)
         if ws is None or ws.numel() < Q.moe_workspace_size(d, T):
-            ws = torch.empty(Q.moe_workspace_size(d, T), dtype=torch.uint8, device=dev())
+            ws = Q.workspace(d, T, dev())
         Q.moe_rmsnorm_residual(h, None, gamma, 1e-6, normed)
         wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
                         lay.shared_down)
