@@ -203,6 +203,24 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
                                    size_t ws_bytes, void* stream, void* const* events,
                                    int32_t n_events, int32_t* n_marks);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * exactly as moe_layer_forward (same kernels, same results bit for bit), with
+ * no workspace argument: the workspace is an array of
+ * MOE_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU, allocated with
+ * the library's code on that GPU and held until the process ends.  The call
+ * itself allocates nothing.  Returns MOE_ERR_WORKSPACE (launching nothing)
+ * when moe_workspace_size(desc, T) exceeds that size -- at the model's shape
+ * (H = 3072, I = 512, 512 experts, top-10, I_s = 512) every batch up to 256
+ * tokens fits.  All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller; calls on one stream are. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                     const uint16_t* x, int32_t T, const float* logits_or_null,
+                                     float* y, int32_t* topk_ids_out, float* topk_w_out,
+                                     void* stream);
+
 /* Helper, not the method: dequantize n_weights weights of one quantized format
  * (Q3S256, NL4_32, Q2S256 or Q2_32; a whole number of blocks, contiguous) to
  * fp32 `out` with per-block device decoders.  Exact: equal bit for bit to

@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT
 
 EXPORTS = ("moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_timed",
-           "moe_dequantize", "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
+           "moe_layer_forward_noalloc", "moe_dequantize", "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,8 @@ def load():
         "moe_layer_forward_timed": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                           P, I32, P, P, P, P, P, SZ, P, P, I32,
                                           ctypes.POINTER(I32)]),
+        "moe_layer_forward_noalloc": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                            P, I32, P, P, P, P, P]),
         "moe_dequantize": (I32, [I32, P, I64, P, P]),
         "moe_rmsnorm_residual": (I32, [P, P, P, F, I32, I32, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
@@ -191,6 +193,15 @@ def moe_layer_forward_timed(d, w, x, y, ws, events, logits=None, topk_ids_out=No
                                           len(events), ctypes.byref(n)),
            "moe_layer_forward_timed")
     return n.value
+
+
+def moe_layer_forward_noalloc(d, w, x, y, logits=None, topk_ids_out=None, topk_w_out=None):
+    """The layer with the library's own device array as its workspace."""
+    T = x.shape[0]
+    _check(load().moe_layer_forward_noalloc(ctypes.byref(d), ctypes.byref(w), _ptr(x), T,
+                                            _ptr(logits), _ptr(y), _ptr(topk_ids_out),
+                                            _ptr(topk_w_out), _stream(x)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_dequantize(fmt, blocks, n_weights, out):

@@ -483,6 +483,64 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     return s;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace of moe_layer_forward_noalloc: a device array of the library
+// (one per GPU the library runs on, held until the process ends).  Host code
+// never uses its name as an address: the address is looked up once per
+// device with that device current and kept per device.
+constexpr size_t kNoAllocBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocBytes];
+
+std::mutex g_scr_mu;
+void* g_scr_ptr[64];
+
+moe_status scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device id out of range");
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if (!g_scr_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scr_ptr[dev] = p;
+    }
+    *out = g_scr_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                     const uint16_t* x, int32_t T, const float* logits_or_null,
+                                     float* y, int32_t* topk_ids_out, float* topk_w_out,
+                                     void* stream) {
+    g_last_error.clear();
+    moe_status s = check_desc(desc);
+    if (s != MOE_OK) return s;
+    if (T < 1 || T > kMaxT) return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18");
+    const size_t need = moe_workspace_size(desc, T);
+    if (need > kNoAllocBytes)
+        return fail(MOE_ERR_WORKSPACE, "this layer needs " + std::to_string(need) +
+                                            " bytes of workspace at T = " + std::to_string(T) +
+                                            "; the library's array holds " +
+                                            std::to_string(kNoAllocBytes));
+    s = check_device();
+    if (s != MOE_OK) return s;
+    void* ws = nullptr;
+    s = scratch_address(&ws);
+    if (s != MOE_OK) return s;
+    Marks mk{nullptr, 0, 0, nullptr};
+    return layer_forward_impl(desc, wts, x, T, logits_or_null, y, topk_ids_out, topk_w_out, ws,
+                              kNoAllocBytes, stream, &mk);
+}
+
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
                           void* stream) {
     g_last_error.clear();

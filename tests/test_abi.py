@@ -127,6 +127,27 @@ def test_stage_error_paths():
     assert lib.moe_router_logits(None, 4, 256, 16, P, None, P2, None, 0, None) == 1
 
 
+def test_noalloc_rejects_batches_beyond_its_array():
+    """The no-allocation entry point refuses, before any device call, a batch
+    whose workspace exceeds the library's array (MOE_ERR_WORKSPACE), and takes
+    the largest one that fits past that check (stopping at the device check
+    here); bad descriptors are refused as by moe_layer_forward."""
+    lib = Q.load()
+    d = Q.desc(3072, 512, 512, 10, 512)
+    limit = 64 << 20
+    T_fit = max(T for T in range(1, 1024) if Q.moe_workspace_size(d, T) <= limit)
+    assert T_fit >= 256
+    w = _w(stride=2162688, shared=(P, P))
+    call = lambda T: lib.moe_layer_forward_noalloc(ctypes.byref(d), ctypes.byref(w), P, T, None, P2,
+                                                   None, None, None)
+    assert call(T_fit + 1) == 5
+    assert b"workspace" in lib.moe_last_error()
+    assert call(T_fit) not in (0, 5)
+    bad = Q.desc(3000, 512, 512, 10, 512)
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(bad), ctypes.byref(w), P, 4, None, P2, None,
+                                         None, None) == 2
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     import quantized_expert_ffn_top_amd._lib as L
     monkeypatch.setattr(L, "_lib", None)
