@@ -48,6 +48,35 @@ Q2-32 block (32 weights, 10 bytes = 2.5 bits per weight)
   bytes [2, 10)   32 two-bit q, weight i at bits 2i .. 2i+1.
   value of weight i = d * (q_i - 2)  (exact in fp32).
 
+Two more up/gate codecs of the same model card ("Files / Main model": up/gate
+IQ3_K in 10 layers, 3.44 bpw, and IQ4_XS in 1 layer; the card also puts the
+draft head's experts in IQ3_K up/gate with IQ4_NL down, "MTP sidecar").  The
+page gives their names and bit rates only.  Readings taken here -- each the
+plainest layout that fills exactly the stated bit rate with the fields the
+3.25-bpw codec has (a binary16 block scale, signed sub-scales, codebook
+indices):
+
+Q3K-256 block (256 weights, 110 bytes = 3.4375 bits per weight, "3.44")
+  bytes [0, 96)   256 three-bit indices into the Q3S-256 codebook, the same
+                  little-endian stream as Q3S-256.
+  bytes [96, 98)  d, binary16.
+  bytes [98, 110) sixteen signed 6-bit sub-scales, one per 16 weights: the 12
+                  bytes read as a little-endian 96-bit number V, s_j = bits
+                  6j .. 6j+5 of V as a two's-complement field, s_j in
+                  [-32, 31].  (The 0.19 bpw over the 3.25-bpw codec buy twice
+                  as many sub-scales with two more bits each.)
+  value of weight i = d * s_{i // 16} * C3[q_i] / 128  (exact in fp32: |s c|
+  <= 4064 has 12 bits, d 11).
+
+NL4S-256 block (256 weights, 136 bytes = 4.25 bits per weight)
+  bytes [0, 128)  256 four-bit indices into the NL4-32 table, weight i at
+                  bits 4i .. 4i+3 of the little-endian stream (sub-block j =
+                  bytes [16j, 16j+16)).
+  bytes [128,130) d, binary16.
+  bytes [130,136) eight signed 6-bit sub-scales, one per 32 weights, as a
+                  little-endian 48-bit number (s_j = bits 6j .. 6j+5).
+  value of weight i = d * s_{i // 32} * T4[q_i] / 128  (exact in fp32).
+
 Codebooks: sorted, distinct int8 levels placed at normal quantiles
 ("NF"-style), asymmetric with an exact zero: for a b-bit book with n = 2^b
 entries, p = 1 - 1/(2n); the n/2 positive levels are Phi^-1 at
@@ -84,6 +113,13 @@ NL4_TABLE = (-127, -88, -66, -50, -36, -23, -11, 0, 10, 20, 31, 43, 56, 71, 91, 
 Q2S_CODEBOOK = (-127, 0, 54, 127)
 # Format numbers (the library's moe_format values).
 FMT_Q3S256, FMT_NL4_32, FMT_Q2S256, FMT_Q2_32 = 2, 3, 4, 5
+FMT_Q3K256, FMT_NL4S256 = 6, 7
+Q3K_BLOCK_WEIGHTS = 256
+Q3K_BLOCK_BYTES = 110
+Q3K_SUB_WEIGHTS = 16
+NL4S_BLOCK_WEIGHTS = 256
+NL4S_BLOCK_BYTES = 136
+NL4S_SUB_WEIGHTS = 32
 
 
 # --------------------------------------------------------------------------
@@ -275,6 +311,91 @@ def pack_q2_block(d_bits, q):
     return bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF]) + stream.to_bytes(8, "little")
 
 
+def _subscales6(v, n):
+    """n two's-complement 6-bit fields of a non-negative int, field j at
+    bits 6j .. 6j+5."""
+    out = []
+    for j in range(n):
+        f = (v >> (6 * j)) & 0x3F
+        out.append(f - 64 if f >= 32 else f)
+    return out
+
+
+def _pack_subscales6(s, nbytes):
+    v = 0
+    for j, sj in enumerate(s):
+        if not -32 <= sj <= 31:
+            raise ValueError("sub-scale out of range")
+        v |= (int(sj) & 0x3F) << (6 * j)
+    return v.to_bytes(nbytes, "little")
+
+
+def unpack_q3k_block(block):
+    """Fields of one 110-byte Q3K-256 block: (d_bits, s[16], q[256])."""
+    block = bytes(block)
+    if len(block) != Q3K_BLOCK_BYTES:
+        raise ValueError("Q3K-256 block must be 110 bytes")
+    bits = _bit_stream(block[0:96])
+    q = [bits[3 * i] | (bits[3 * i + 1] << 1) | (bits[3 * i + 2] << 2)
+         for i in range(Q3K_BLOCK_WEIGHTS)]
+    d_bits = block[96] | (block[97] << 8)
+    return d_bits, _subscales6(int.from_bytes(block[98:110], "little"), 16), q
+
+
+def dequant_q3k_block(block):
+    """256 weight values of one Q3K-256 block (Python floats, exact)."""
+    d_bits, s, q = unpack_q3k_block(block)
+    d = fp16_bits_to_float(d_bits)
+    return [d * s[i // Q3K_SUB_WEIGHTS] * Q3S_CODEBOOK[q[i]] / 128.0
+            for i in range(Q3K_BLOCK_WEIGHTS)]
+
+
+def pack_q3k_block(d_bits, s, q):
+    """Bytes of one Q3K-256 block from its fields."""
+    if len(s) != 16 or len(q) != Q3K_BLOCK_WEIGHTS:
+        raise ValueError("need 16 sub-scales and 256 indices")
+    stream = 0
+    for i, qi in enumerate(q):
+        if not 0 <= qi < 8:
+            raise ValueError("index out of range")
+        stream |= int(qi) << (3 * i)
+    return (stream.to_bytes(96, "little") + bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF])
+            + _pack_subscales6(s, 12))
+
+
+def unpack_nl4s_block(block):
+    """Fields of one 136-byte NL4S-256 block: (d_bits, s[8], q[256])."""
+    block = bytes(block)
+    if len(block) != NL4S_BLOCK_BYTES:
+        raise ValueError("NL4S-256 block must be 136 bytes")
+    bits = _bit_stream(block[0:128])
+    q = [bits[4 * i] | (bits[4 * i + 1] << 1) | (bits[4 * i + 2] << 2) | (bits[4 * i + 3] << 3)
+         for i in range(NL4S_BLOCK_WEIGHTS)]
+    d_bits = block[128] | (block[129] << 8)
+    return d_bits, _subscales6(int.from_bytes(block[130:136], "little"), 8), q
+
+
+def dequant_nl4s_block(block):
+    """256 weight values of one NL4S-256 block (Python floats, exact)."""
+    d_bits, s, q = unpack_nl4s_block(block)
+    d = fp16_bits_to_float(d_bits)
+    return [d * s[i // NL4S_SUB_WEIGHTS] * NL4_TABLE[q[i]] / 128.0
+            for i in range(NL4S_BLOCK_WEIGHTS)]
+
+
+def pack_nl4s_block(d_bits, s, q):
+    """Bytes of one NL4S-256 block from its fields."""
+    if len(s) != 8 or len(q) != NL4S_BLOCK_WEIGHTS:
+        raise ValueError("need 8 sub-scales and 256 indices")
+    stream = 0
+    for i, qi in enumerate(q):
+        if not 0 <= qi < 16:
+            raise ValueError("index out of range")
+        stream |= int(qi) << (4 * i)
+    return (stream.to_bytes(128, "little") + bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF])
+            + _pack_subscales6(s, 6))
+
+
 # --------------------------------------------------------------------------
 # vectorised (NumPy) codecs; pinned bit-exactly against the scalar ones
 # --------------------------------------------------------------------------
@@ -360,6 +481,85 @@ def dequant_q2(arr):
     """Vectorised Q2-32 dequant: float64 [..., 32] per block."""
     d, q = unpack_q2(arr)
     return d[..., None] * (q - 2).astype(np.float64)
+
+
+def _unpack_subscales6(a, n):
+    """Two's-complement 6-bit fields j = 0..n-1 of little-endian byte rows a
+    [..., ceil(6n/8)] (field j at bits 6j .. 6j+5)."""
+    bits = np.unpackbits(a, axis=-1, bitorder="little").astype(np.int64)
+    bits = bits[..., :6 * n].reshape(a.shape[:-1] + (n, 6))
+    f = sum(bits[..., b] << b for b in range(6))
+    return np.where(f >= 32, f - 64, f)
+
+
+def unpack_q3k(arr):
+    """Vectorised Q3K-256 unpack: (d float64 [...], s int64 [..., 16],
+    q int64 [..., 256])."""
+    a = _as_blocks(arr, Q3K_BLOCK_BYTES)
+    bits = np.unpackbits(a[..., 0:96], axis=-1, bitorder="little")
+    bits = bits.reshape(a.shape[:-1] + (Q3K_BLOCK_WEIGHTS, 3)).astype(np.int64)
+    q = bits[..., 0] | (bits[..., 1] << 1) | (bits[..., 2] << 2)
+    d = np.ascontiguousarray(a[..., 96:98]).view("<f2")[..., 0].astype(np.float64)
+    return d, _unpack_subscales6(a[..., 98:110], 16), q
+
+
+def dequant_q3k(arr):
+    """Vectorised Q3K-256 dequant: float64 [..., 256] per block."""
+    d, s, q = unpack_q3k(arr)
+    c = np.asarray(Q3S_CODEBOOK, dtype=np.float64)[q]
+    return d[..., None] * np.repeat(s, Q3K_SUB_WEIGHTS, axis=-1) * c / 128.0
+
+
+def unpack_nl4s(arr):
+    """Vectorised NL4S-256 unpack: (d float64 [...], s int64 [..., 8],
+    q int64 [..., 256])."""
+    a = _as_blocks(arr, NL4S_BLOCK_BYTES)
+    idx = a[..., 0:128].astype(np.int64)
+    q = np.stack([idx & 0xF, idx >> 4], axis=-1).reshape(a.shape[:-1] + (NL4S_BLOCK_WEIGHTS,))
+    d = np.ascontiguousarray(a[..., 128:130]).view("<f2")[..., 0].astype(np.float64)
+    return d, _unpack_subscales6(a[..., 130:136], 8), q
+
+
+def dequant_nl4s(arr):
+    """Vectorised NL4S-256 dequant: float64 [..., 256] per block."""
+    d, s, q = unpack_nl4s(arr)
+    t = np.asarray(NL4_TABLE, dtype=np.float64)[q]
+    return d[..., None] * np.repeat(s, NL4S_SUB_WEIGHTS, axis=-1) * t / 128.0
+
+
+def _pack_subscales6_vec(s, nbytes):
+    s = np.asarray(s, dtype=np.int64)
+    f = (s & 0x3F).astype(np.uint8)
+    bits = np.stack([(f >> b) & 1 for b in range(6)], axis=-1).reshape(s.shape[:-1] + (-1,))
+    pad = nbytes * 8 - bits.shape[-1]
+    if pad:
+        bits = np.concatenate([bits, np.zeros(s.shape[:-1] + (pad,), dtype=np.uint8)], axis=-1)
+    return np.packbits(bits.astype(np.uint8), axis=-1, bitorder="little")
+
+
+def pack_q3k(d_bits, s, q):
+    """Vectorised pack: d_bits uint16 [...], s int [..., 16], q int [..., 256]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    q = np.asarray(q, dtype=np.int64)
+    lead = d_bits.shape
+    out = np.zeros(lead + (Q3K_BLOCK_BYTES,), dtype=np.uint8)
+    bits = np.stack([(q >> b) & 1 for b in range(3)], axis=-1).reshape(lead + (768,))
+    out[..., 0:96] = np.packbits(bits.astype(np.uint8), axis=-1, bitorder="little")
+    out[..., 96:98] = d_bits[..., None].view(np.uint8).reshape(lead + (2,))
+    out[..., 98:110] = _pack_subscales6_vec(s, 12)
+    return out
+
+
+def pack_nl4s(d_bits, s, q):
+    """Vectorised pack: d_bits uint16 [...], s int [..., 8], q int [..., 256]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    q = np.asarray(q, dtype=np.int64)
+    lead = d_bits.shape
+    out = np.zeros(lead + (NL4S_BLOCK_BYTES,), dtype=np.uint8)
+    out[..., 0:128] = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+    out[..., 128:130] = d_bits[..., None].view(np.uint8).reshape(lead + (2,))
+    out[..., 130:136] = _pack_subscales6_vec(s, 6)
+    return out
 
 
 def dequant_q3s_matrix(raw, rows, cols):
@@ -515,6 +715,43 @@ def quantize_q2(w):
     return pack_q2(d_bits, q)
 
 
+def _quantize_subscaled(w, sub, book):
+    """Round-to-nearest for the 6-bit sub-scaled codecs: per block of
+    w [..., n] with sub-blocks of `sub` weights, sigma_j = absmax_j /
+    (max|book|/128); d = fp16_RNE(max_j sigma_j / 31); s_j =
+    clamp(round_half_even(sigma_j / d), -32, 31); q_i = the book index
+    minimising |w_i - d*s_j*book[q]/128|, ties to the lower index (d = 0 gives
+    s = q = 0).  Returns (d_bits, s, q)."""
+    w = np.asarray(w, dtype=np.float64)
+    lead, n = w.shape[:-1], w.shape[-1]
+    ns = n // sub
+    subw = w.reshape(lead + (ns, sub))
+    cmax = max(abs(c) for c in book) / 128.0
+    sigma = np.abs(subw).max(axis=-1) / cmax
+    d_bits = _fp16_rne_bits(sigma.max(axis=-1) / 31.0)
+    d = d_bits.view(np.float16).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = np.where(d[..., None] > 0, np.rint(sigma / d[..., None]), 0.0)
+    s = np.clip(s, -32, 31).astype(np.int64)
+    cands = (d[..., None, None] * s[..., None].astype(np.float64)
+             * np.asarray(book, dtype=np.float64) / 128.0)
+    dist = np.abs(subw[..., None] - cands[..., None, :])
+    q = np.argmin(dist, axis=-1).reshape(lead + (n,))
+    return d_bits, s, q
+
+
+def quantize_q3k(w):
+    """Round-to-nearest Q3K-256 encoding of weights w [..., 256] (16-weight
+    sub-blocks, the C3 codebook).  Returns uint8 [..., 110]."""
+    return pack_q3k(*_quantize_subscaled(w, Q3K_SUB_WEIGHTS, Q3S_CODEBOOK))
+
+
+def quantize_nl4s(w):
+    """Round-to-nearest NL4S-256 encoding of weights w [..., 256] (32-weight
+    sub-blocks, the T4 table).  Returns uint8 [..., 136]."""
+    return pack_nl4s(*_quantize_subscaled(w, NL4S_SUB_WEIGHTS, NL4_TABLE))
+
+
 def quantize_q3s_matrix(w):
     """Quantise a matrix [rows][cols] (cols % 256 == 0) to Q3S-256 bytes
     [rows][cols/256*104]."""
@@ -534,7 +771,7 @@ def quantize_nl4_matrix(w):
 
 
 # --------------------------------------------------------------------------
-# any of the four codecs by format number
+# any of the codecs by format number
 # --------------------------------------------------------------------------
 
 # format -> (weights per block, bytes per block, vectorised dequant,
@@ -544,8 +781,11 @@ CODECS = {
     FMT_NL4_32: (NL4_BLOCK_WEIGHTS, NL4_BLOCK_BYTES, dequant_nl4, dequant_nl4_block, quantize_nl4),
     FMT_Q2S256: (Q2S_BLOCK_WEIGHTS, Q2S_BLOCK_BYTES, dequant_q2s, dequant_q2s_block, quantize_q2s),
     FMT_Q2_32: (Q2_BLOCK_WEIGHTS, Q2_BLOCK_BYTES, dequant_q2, dequant_q2_block, quantize_q2),
+    FMT_Q3K256: (Q3K_BLOCK_WEIGHTS, Q3K_BLOCK_BYTES, dequant_q3k, dequant_q3k_block, quantize_q3k),
+    FMT_NL4S256: (NL4S_BLOCK_WEIGHTS, NL4S_BLOCK_BYTES, dequant_nl4s, dequant_nl4s_block,
+                  quantize_nl4s),
 }
-UPGATE_FORMATS = (FMT_Q3S256, FMT_Q2S256, FMT_NL4_32)
+UPGATE_FORMATS = (FMT_Q3S256, FMT_Q2S256, FMT_NL4_32, FMT_Q3K256, FMT_NL4S256)
 DOWN_FORMATS = (FMT_NL4_32, FMT_Q2_32)
 
 

@@ -451,3 +451,173 @@ def test_mixed_expert_record(ug, dn):
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
     assert np.array_equal(np.concatenate([a[0], a[1]]), F.dequant_matrix(ug, F.quantize_matrix(ug, wug), 2 * I, H))
+
+
+# ---------------------------------------------------------------- the 6-bit sub-scaled codecs
+# (the model card's IQ3_K and IQ4_XS up/gate names, "Files / Main model", and
+# the draft head's IQ3_K experts, "MTP sidecar"; the layouts are readings,
+# pinned by construction like the codecs above)
+
+def test_q3k_and_nl4s_block_sizes_give_the_stated_bit_rates():
+    assert F.Q3K_BLOCK_BYTES * 8 / 256 == 3.4375         # "3.44 bpw"
+    assert F.NL4S_BLOCK_BYTES * 8 / 256 == 4.25
+
+
+@pytest.mark.parametrize("case", GOLD["q3k_fields"])
+def test_q3k_field_offsets(case):
+    blk = F.pack_q3k_block(int(case["d_bits"], 16), case["s"], [0] * 256)
+    assert len(blk) == F.Q3K_BLOCK_BYTES
+    assert _hex(blk[96:110]) == case["bytes_96_110_hex"]
+    d_bits, s, q = F.unpack_q3k_block(blk)
+    assert d_bits == int(case["d_bits"], 16) and s == case["s"] and q == [0] * 256
+
+
+@pytest.mark.parametrize("case", GOLD["q3s_index_stream"])
+def test_q3k_index_stream_is_the_q3s_stream(case):
+    q = list(case["indices_first8"]) + [0] * 248
+    blk = F.pack_q3k_block(0, [0] * 16, q)
+    assert _hex(blk[:3]) == case["bytes_hex"]
+    assert F.unpack_q3k_block(blk)[2][:8] == case["indices_first8"]
+
+
+@pytest.mark.parametrize("case", GOLD["q3k_values"])
+def test_q3k_known_values(case):
+    blk = F.pack_q3k_block(int(case["d_bits"], 16), [case["s"]] * 16, [case["q"]] * 256)
+    assert all(v == case["value"] for v in F.dequant_q3k_block(blk))
+    assert np.all(F.dequant_q3k(np.frombuffer(blk, np.uint8)[None]) == case["value"])
+
+
+@pytest.mark.parametrize("case", GOLD["nl4s_fields"])
+def test_nl4s_field_offsets(case):
+    q = list(case["indices_first4"]) + [0] * 252
+    blk = F.pack_nl4s_block(int(case["d_bits"], 16), case["s"], q)
+    assert len(blk) == F.NL4S_BLOCK_BYTES
+    assert _hex(blk[0:2]) == case["bytes_0_2_hex"]
+    assert _hex(blk[128:136]) == case["bytes_128_136_hex"]
+    d_bits, s, q2 = F.unpack_nl4s_block(blk)
+    assert d_bits == int(case["d_bits"], 16) and s == case["s"] and q2 == q
+
+
+@pytest.mark.parametrize("case", GOLD["nl4s_values"])
+def test_nl4s_known_values(case):
+    blk = F.pack_nl4s_block(int(case["d_bits"], 16), [case["s"]] * 8, [case["q"]] * 256)
+    assert all(v == case["value"] for v in F.dequant_nl4s_block(blk))
+    assert np.all(F.dequant_nl4s(np.frombuffer(blk, np.uint8)[None]) == case["value"])
+
+
+def test_q3k_every_index_and_subscale_position():
+    s = [-32, 31, -1, 0, 1, 17, -17, 5, -5, 9, 30, -31, 2, -2, 12, -12]
+    q = [(i * 5 + i // 16) % 8 for i in range(256)]
+    vals = F.dequant_q3k_block(F.pack_q3k_block(0x3C00, s, q))
+    for i in range(256):
+        assert vals[i] == s[i // 16] * F.Q3S_CODEBOOK[q[i]] / 128.0
+
+
+def test_nl4s_every_index_and_subscale_position():
+    s = [-32, 31, -1, 0, 1, 17, -17, 5]
+    q = [(i * 7 + i // 32) % 16 for i in range(256)]
+    vals = F.dequant_nl4s_block(F.pack_nl4s_block(0x3C00, s, q))
+    for i in range(256):
+        assert vals[i] == s[i // 32] * F.NL4_TABLE[q[i]] / 128.0
+
+
+def _random_blocks(rng, n, nbytes, d_hi):
+    blk = rng.integers(0, 256, size=(n, nbytes), dtype=np.uint8)
+    blk[:, d_hi] = (blk[:, d_hi] & 0x83) | (rng.integers(0, 30, size=n, dtype=np.uint8) << 2)
+    return blk                                         # finite d of either sign, subnormals included
+
+
+def test_vectorised_matches_scalar_q3k_nl4s():
+    rng = np.random.default_rng(21)
+    for nb, d_hi, deq, deq_blk, unp_blk, unp in (
+            (F.Q3K_BLOCK_BYTES, 97, F.dequant_q3k, F.dequant_q3k_block, F.unpack_q3k_block, F.unpack_q3k),
+            (F.NL4S_BLOCK_BYTES, 129, F.dequant_nl4s, F.dequant_nl4s_block, F.unpack_nl4s_block,
+             F.unpack_nl4s)):
+        blocks = _random_blocks(rng, 40, nb, d_hi)
+        vec = deq(blocks)
+        for b in range(len(blocks)):
+            assert list(vec[b]) == deq_blk(bytes(blocks[b]))
+            _, s, q = unp_blk(bytes(blocks[b]))
+            _, s2, q2 = unp(blocks[b][None])
+            assert list(s2[0]) == s and list(q2[0]) == q
+
+
+def test_q3k_nl4s_dequant_is_exact_in_fp32():
+    rng = np.random.default_rng(22)
+    for v in F.dequant_q3k(_random_blocks(rng, 30, F.Q3K_BLOCK_BYTES, 97)).ravel():
+        assert float(np.float32(v)) == v
+    for v in F.dequant_nl4s(_random_blocks(rng, 30, F.NL4S_BLOCK_BYTES, 129)).ravel():
+        assert float(np.float32(v)) == v
+
+
+def test_q3k_nl4s_packers_roundtrip_fields():
+    rng = np.random.default_rng(23)
+    d = rng.integers(0, 0x7C00, size=5).astype(np.uint16)
+    s16 = rng.integers(-32, 32, size=(5, 16))
+    s8 = rng.integers(-32, 32, size=(5, 8))
+    q8 = rng.integers(0, 8, size=(5, 256))
+    q16 = rng.integers(0, 16, size=(5, 256))
+    v3 = F.pack_q3k(d, s16, q8)
+    v4 = F.pack_nl4s(d, s8, q16)
+    for b in range(5):
+        assert bytes(v3[b]) == F.pack_q3k_block(int(d[b]), list(s16[b]), list(q8[b]))
+        assert F.unpack_q3k_block(bytes(v3[b])) == (int(d[b]), list(s16[b]), list(q8[b]))
+        assert bytes(v4[b]) == F.pack_nl4s_block(int(d[b]), list(s8[b]), list(q16[b]))
+        assert F.unpack_nl4s_block(bytes(v4[b])) == (int(d[b]), list(s8[b]), list(q16[b]))
+
+
+@pytest.mark.parametrize("fmt", [F.FMT_Q3K256, F.FMT_NL4S256])
+def test_subscaled_quantiser_on_grid_roundtrip(fmt):
+    """Weights on one block's grid (largest sub-scale 31, every sub-block
+    holding the largest-magnitude entry so the rule recovers its sub-scale)
+    come back bit for bit."""
+    sub, book = (16, F.Q3S_CODEBOOK) if fmt == F.FMT_Q3K256 else (32, F.NL4_TABLE)
+    ns = 256 // sub
+    d_bits = 0x2400
+    d = float(np.uint16(d_bits).view(np.float16))
+    rng = np.random.default_rng(24)
+    s = list(rng.integers(1, 32, size=ns))
+    s[3] = 31
+    q = rng.integers(0, len(book), size=256)
+    q[::sub] = 0                                          # book[0] = -127: the largest magnitude
+    w = np.array([d * s[i // sub] * book[q[i]] / 128.0 for i in range(256)])
+    blk = F.CODECS[fmt][4](w)
+    unp = F.unpack_q3k_block if fmt == F.FMT_Q3K256 else F.unpack_nl4s_block
+    d2, s2, q2 = unp(bytes(blk))
+    assert (d2, s2, q2) == (d_bits, [int(v) for v in s], list(q))
+
+
+@pytest.mark.parametrize("fmt", [F.FMT_Q3K256, F.FMT_NL4S256])
+def test_subscaled_quantiser_is_nearest_brute_force(fmt):
+    sub, book = (16, F.Q3S_CODEBOOK) if fmt == F.FMT_Q3K256 else (32, F.NL4_TABLE)
+    unp = F.unpack_q3k_block if fmt == F.FMT_Q3K256 else F.unpack_nl4s_block
+    rng = np.random.default_rng(25)
+    w = rng.normal(0, 0.02, size=(4, 256))
+    blks = F.CODECS[fmt][4](w)
+    for b in range(4):
+        d_bits, s, q = unp(bytes(blks[b]))
+        d = F.fp16_bits_to_float(d_bits)
+        sigma_max = max(np.abs(w[b, j * sub:(j + 1) * sub]).max() for j in range(256 // sub)) / (127 / 128)
+        assert d_bits == int(np.float16(sigma_max / 31).view(np.uint16))
+        for i in range(256):
+            lv = [d * s[i // sub] * c / 128.0 for c in book]
+            best = min(range(len(book)), key=lambda t: (abs(w[b, i] - lv[t]), t))
+            assert q[i] == best
+
+
+@pytest.mark.parametrize("ug", [F.FMT_Q3K256, F.FMT_NL4S256])
+def test_subscaled_expert_record(ug):
+    """Records with the 6-bit sub-scaled up|gate codecs (and NL4-32 down, as
+    the draft head's experts): the matrix helpers agree with the scalar block
+    decoders."""
+    H, I = 256, 64
+    rng = np.random.default_rng(26)
+    wug = rng.normal(0, 0.02, size=(2 * I, H))
+    wdn = rng.normal(0, 0.02, size=(H, I))
+    rec = np.concatenate([F.quantize_matrix(ug, wug).ravel(),
+                          F.quantize_matrix(F.FMT_NL4_32, wdn).ravel()])
+    assert rec.size == F.expert_record_bytes(H, I, ug, F.FMT_NL4_32)
+    a = F.expert_matrices(rec, H, I, ug, F.FMT_NL4_32)
+    b = F.expert_matrices_scalar(rec, H, I, ug, F.FMT_NL4_32)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
