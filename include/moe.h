@@ -87,22 +87,36 @@ typedef enum {
  *                  [2,10) 32 2-bit q (weight i at bits 2i..2i+1).  w_i =
  *                  d * (q_i - 2).  (A reading of the model card's Q2_0 down
  *                  layers, which the page names only.)
+ *  MOE_FMT_Q3K256  3.4375-bpw super-blocks of 256 weights, 110 bytes each:
+ *                  [0,96) 256 3-bit indices as in Q3S256; [96,98) fp16 d;
+ *                  [98,110) sixteen signed 6-bit sub-scales, one per 16
+ *                  weights (s_j = bits 6j..6j+5 of that little-endian 96-bit
+ *                  field, two's complement).  w_i = d * s_{i/16} * C3[q_i] / 128.
+ *                  (A reading of the model card's IQ3_K up/gate type, "3.44
+ *                  bpw", and of the draft head's experts, "MTP sidecar".)
+ *  MOE_FMT_NL4S256 4.25-bpw super-blocks of 256 weights, 136 bytes each:
+ *                  [0,128) 256 4-bit indices as in NL4_32; [128,130) fp16 d;
+ *                  [130,136) eight signed 6-bit sub-scales, one per 32 weights.
+ *                  w_i = d * s_{i/32} * T4[q_i] / 128.  (A reading of the model
+ *                  card's IQ4_XS up/gate type, 4.25 bpw.)
  * Matrices are stored [out rows][in] with blocks along the input dimension. */
 typedef enum {
     MOE_FMT_BF16 = 1,
     MOE_FMT_Q3S256 = 2,
     MOE_FMT_NL4_32 = 3,
     MOE_FMT_Q2S256 = 4,
-    MOE_FMT_Q2_32 = 5
+    MOE_FMT_Q2_32 = 5,
+    MOE_FMT_Q3K256 = 6,
+    MOE_FMT_NL4S256 = 7
 } moe_format;
 
 /* Layer shape.  Supported: hidden % 256 == 0 (and <= 8192); inter % 64 == 0
  * (and <= 4096); 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
  * shared_inter == 0 (no shared expert) or shared_inter % 64 == 0 (<= 4096);
- * routed up|gate in MOE_FMT_Q3S256, MOE_FMT_Q2S256 or MOE_FMT_NL4_32 and
- * routed down in MOE_FMT_NL4_32 or MOE_FMT_Q2_32 (the mixed-format layers of
- * the model card use all five combinations' parts); the shared expert and the
- * router are always bf16.  Batches of T <= 16 tokens with Q3S256 / NL4_32
+ * routed up|gate in MOE_FMT_Q3S256, MOE_FMT_Q2S256, MOE_FMT_NL4_32,
+ * MOE_FMT_Q3K256 or MOE_FMT_NL4S256 and routed down in MOE_FMT_NL4_32 or
+ * MOE_FMT_Q2_32 (the model card's mixed-format layers and draft head use
+ * these); the shared expert and the router are always bf16.  Batches of T <= 16 tokens with Q3S256 / NL4_32
  * experts take the bandwidth kernels; every other case the grouped GEMMs. */
 typedef struct {
     int32_t hidden;        /* H                                              */
@@ -222,10 +236,10 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer
                                      void* stream);
 
 /* Helper, not the method: dequantize n_weights weights of one quantized format
- * (Q3S256, NL4_32, Q2S256 or Q2_32; a whole number of blocks, contiguous) to
- * fp32 `out` with per-block device decoders.  Exact: equal bit for bit to
- * d*s*c/128 (Q3S256, Q2S256), d*t/128 (NL4_32) or d*(q-2) (Q2_32).  blocks
- * must be 16-byte aligned. */
+ * (Q3S256, NL4_32, Q2S256, Q2_32, Q3K256 or NL4S256; a whole number of
+ * blocks, contiguous) to fp32 `out` with per-block device decoders.  Exact:
+ * equal bit for bit to d*s*c/128 (Q3S256, Q2S256, Q3K256), d*t/128 (NL4_32),
+ * d*s*t/128 (NL4S256) or d*(q-2) (Q2_32).  blocks must be 16-byte aligned. */
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
                           void* stream);
 

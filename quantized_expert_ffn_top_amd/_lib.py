@@ -19,6 +19,8 @@ MOE_FMT_Q3S256 = 2
 MOE_FMT_NL4_32 = 3
 MOE_FMT_Q2S256 = 4
 MOE_FMT_Q2_32 = 5
+MOE_FMT_Q3K256 = 6
+MOE_FMT_NL4S256 = 7
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_HIP"}

@@ -126,8 +126,9 @@ moe_status check_desc(const moe_layer_desc* d) {
     if (d->shared_inter < 0 || d->shared_inter > 4096 || d->shared_inter % 64)
         return fail(MOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64 <= 4096");
     if (d->upgate_fmt != MOE_FMT_Q3S256 && d->upgate_fmt != MOE_FMT_Q2S256 &&
-        d->upgate_fmt != MOE_FMT_NL4_32)
-        return fail(MOE_ERR_FORMAT, "routed up|gate must be Q3S256, Q2S256 or NL4_32");
+        d->upgate_fmt != MOE_FMT_NL4_32 && d->upgate_fmt != MOE_FMT_Q3K256 &&
+        d->upgate_fmt != MOE_FMT_NL4S256)
+        return fail(MOE_ERR_FORMAT, "routed up|gate must be Q3S256, Q2S256, NL4_32, Q3K256 or NL4S256");
     if (d->down_fmt != MOE_FMT_NL4_32 && d->down_fmt != MOE_FMT_Q2_32)
         return fail(MOE_ERR_FORMAT, "routed down must be NL4_32 or Q2_32");
     return MOE_OK;
@@ -314,7 +315,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16,
                        desc->upgate_fmt, st);
     launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, upgate_bytes(desc),
-                     desc->down_fmt, y_perm, nullptr, st);
+                     desc->down_fmt, y_perm, st);
     return launched("moe_expert_ffn");
 }
 
@@ -438,16 +439,10 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16,
                            desc->upgate_fmt, st);
         mk->mark();
-        // the unweighted rows go through memory as fp16 (one rounding,
-        // relative error <= 2^-11) on this path: half the bytes written and read
+        // the unweighted rows go through memory in fp32 (any magnitude)
         launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I,
-                         upgate_bytes(desc), desc->down_fmt, nullptr,
-                         reinterpret_cast<uint16_t*>(yp), st);
+                         upgate_bytes(desc), desc->down_fmt, yp, st);
         mk->mark();
-        launch_combine16(reinterpret_cast<const uint16_t*>(yp), inv, wv, T, k, H,
-                         has_sh ? ysh : nullptr, y, st);
-        mk->mark();
-        return launched("moe_layer_forward");
     }
     launch_combine(yp, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
     mk->mark();
@@ -546,8 +541,8 @@ moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, fl
     g_last_error.clear();
     if (!blocks || !out) return fail(MOE_ERR_NULL, "null argument");
     if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32 && fmt != MOE_FMT_Q2S256 &&
-        fmt != MOE_FMT_Q2_32)
-        return fail(MOE_ERR_FORMAT, "moe_dequantize supports Q3S256, NL4_32, Q2S256 and Q2_32");
+        fmt != MOE_FMT_Q2_32 && fmt != MOE_FMT_Q3K256 && fmt != MOE_FMT_NL4S256)
+        return fail(MOE_ERR_FORMAT, "moe_dequantize supports Q3S256, NL4_32, Q2S256, Q2_32, Q3K256, NL4S256");
     const int64_t unit = fmt_block_weights(fmt);
     if (n_weights < unit || n_weights % unit)
         return fail(MOE_ERR_SHAPE, "n_weights must be a positive multiple of the block size");

@@ -37,12 +37,17 @@ constexpr int kNL4Bytes = 18;
 constexpr int kNL4Weights = 32;
 constexpr int kQ2SBytes = 80;
 constexpr int kQ2Bytes = 10;
+constexpr int kQ3KBytes = 110;      // Q3K-256: 96 index bytes, fp16 d, 16 six-bit sub-scales
+constexpr int kNL4SBytes = 136;     // NL4S-256: 128 index bytes, fp16 d, 8 six-bit sub-scales
 
 // Format numbers (the C ABI's moe_format) and their block sizes.
-constexpr int kFmtQ3S256 = 2, kFmtNL4 = 3, kFmtQ2S256 = 4, kFmtQ2 = 5;
-__host__ __device__ constexpr int fmt_block_weights(int f) { return (f == kFmtQ3S256 || f == kFmtQ2S256) ? 256 : 32; }
+constexpr int kFmtQ3S256 = 2, kFmtNL4 = 3, kFmtQ2S256 = 4, kFmtQ2 = 5, kFmtQ3K256 = 6, kFmtNL4S256 = 7;
+__host__ __device__ constexpr int fmt_block_weights(int f) {
+    return (f == kFmtQ3S256 || f == kFmtQ2S256 || f == kFmtQ3K256 || f == kFmtNL4S256) ? 256 : 32;
+}
 __host__ __device__ constexpr int fmt_block_bytes(int f) {
-    return f == kFmtQ3S256 ? kQ3Bytes : f == kFmtNL4 ? kNL4Bytes : f == kFmtQ2S256 ? kQ2SBytes : kQ2Bytes;
+    return f == kFmtQ3S256 ? kQ3Bytes : f == kFmtNL4 ? kNL4Bytes : f == kFmtQ2S256 ? kQ2SBytes
+           : f == kFmtQ3K256 ? kQ3KBytes : f == kFmtNL4S256 ? kNL4SBytes : kQ2Bytes;
 }
 // bytes of a [rows][cols] matrix, blocks along cols
 __host__ __device__ constexpr int64_t fmt_matrix_bytes(int f, int rows, int cols) {
@@ -456,5 +461,7 @@ __device__ __forceinline__ float q2s_value(float d, int s, int q) {
 __device__ __forceinline__ float q2_value(float d, int q) {
     return d * (float)(q - 2);
 }
+// Two's-complement 6-bit field at the low bits of f.
+__device__ __forceinline__ int sext6(uint32_t f) { return (int)((f & 63u) ^ 32u) - 32; }
 
 }  // namespace moe

@@ -30,8 +30,6 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
                         hipStream_t st);
 void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
                     const float* shared, float* y, hipStream_t st);
-void launch_combine16(const uint16_t* y_perm16, const int32_t* inv, const float* w, int T, int k,
-                      int H, const float* shared, float* y, hipStream_t st);
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st);
 
@@ -67,18 +65,16 @@ void launch_down_dec(const uint8_t* experts, int64_t estride, const int32_t* til
                      float* y_perm, float* y_sh, int n_cu, hipStream_t st);
 
 // ---- grouped-GEMM path (moe_kernels_gemm.hip)
-// fmt: the up|gate format (Q3S-256, Q2S-256 or NL4-32)
+// fmt: the up|gate format (Q3S-256, Q2S-256, NL4-32, Q3K-256 or NL4S-256)
 void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                         const int32_t* ntiles, int max_tiles, const int32_t* perm, int k,
                         const uint16_t* x16, int H, int I, uint16_t* a16_perm, int fmt,
                         hipStream_t st);
 // dn_off: byte offset of the down matrix in an expert record; fmt: its format
-// (NL4-32 or Q2-32).  y_perm16 non-null: the unweighted rows are stored as
-// fp16 there (the layer's own combine reads them); else fp32 to y_perm.
+// (NL4-32 or Q2-32).  The unweighted rows are stored fp32 to y_perm.
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
-                      hipStream_t st);
+                      int I, int64_t dn_off, int fmt, float* y_perm, hipStream_t st);
 
 // ---- dense bf16 products of the grouped-GEMM path (moe_kernels_dense.hip)
 // One launch: router logits [T][E] (+ bias) if w_r is not null, and the

@@ -6,7 +6,7 @@
 //   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
 //           mixed-format layers)
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
-//           weights, epilogue fp32 (or fp16) store (permuted rows)
+//           weights, epilogue fp32 store (permuted rows)
 //   DN_Q2   the same with Q2-32 weights
 //
 // Tile 64 token rows x 256 weight rows, K steps of 64; four waves, wave w
@@ -31,7 +31,9 @@
 // Numerics: Q3S and Q2S weights enter the matrix cores as s*c (an fp16
 // integer, |s*c| <= 1016, exact) and d/128 is applied in fp32 to the partial
 // sum of each 256-weight block, so those weights are exact.  NL4 down weights
-// enter as fp16_rne(d * T4[q] / 128) (one rounding, relative error <= 2^-11);
+// enter as fp16_rne(16 d * T4[q] / 128) (one rounding, relative error <= 2^-11
+// for every normal d up to 4126; the factor 16 keeps the smallest entries of
+// small-d blocks out of fp16's subnormals and is divided out in the epilogue);
 // Q2 weights as d * (q - 2), exact in fp16.  NL4 up|gate weights stay exact
 // too (a rounding there would move the bf16 rounding of the SwiGLU output):
 // that mode keeps the natural K order, so the two MFMAs of a chunk pair cover
@@ -50,12 +52,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int N> struct Cnt { static constexpr int value = N; };
 
 // (the numbers are the kernels' names in traces: k_gemm<0>, <1>, <5>, <6>, <7>)
-enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7 };
+enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7, UG_Q3K = 8, UG_NL4S = 9 };
 // quantized B formats of the routed modes
-enum BFmt { BF_NONE, BF_Q3, BF_Q2S, BF_NL4, BF_Q2 };
+enum BFmt { BF_NONE, BF_Q3, BF_Q2S, BF_NL4, BF_Q2, BF_Q3K, BF_NL4S };
 template <int MODE> constexpr int bfmt() {
     return MODE == UG_Q3 ? BF_Q3 : MODE == UG_Q2S ? BF_Q2S : (MODE == DN_NL4 || MODE == UG_NL4) ? BF_NL4
-           : MODE == DN_Q2 ? BF_Q2 : BF_NONE;
+           : MODE == DN_Q2 ? BF_Q2 : MODE == UG_Q3K ? BF_Q3K : MODE == UG_NL4S ? BF_NL4S : BF_NONE;
 }
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
@@ -81,7 +83,6 @@ struct GemmArgs {
     int64_t dn_off;          // routed down: byte offset of the down matrix in a record
     uint16_t* out16;         // a16_perm / a_sh
     float* out32;            // y_perm
-    uint16_t* y16;           // routed down: y_perm as fp16 instead (null: fp32 to out32)
     int ldo;                 // output row length
     int npb;                 // routed: N tiles per block (consecutive, same M tile)
 };
@@ -125,8 +126,14 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr bool kQ3 = kBF == BF_Q3;
     constexpr bool kNL = kBF == BF_NL4;
     constexpr bool kB256 = kBF == BF_Q3 || kBF == BF_Q2S;     // 256-weight blocks: d on the partial sums
-    constexpr bool kNat = MODE == UG_NL4;                      // natural K order, d per 32-weight block
-    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_Q2S || MODE == UG_NL4;
+    // 6-bit sub-scaled 256-weight blocks (Q3K-256: sub-blocks of 16, NL4S-256:
+    // of 32), natural K order.  Q3K-256: B = s * c as two exact fp16 parts,
+    // d / 128 on the block's partial sums; NL4S-256: B = the table integers,
+    // d * s / 128 applied in fp32 to each 32-weight sub-block's partial sums
+    constexpr bool kQ3K = kBF == BF_Q3K, kNLS = kBF == BF_NL4S, kSub = kQ3K || kNLS;
+    constexpr bool kNat = MODE == UG_NL4 || kSub;              // natural K order
+    constexpr bool kNLTab = kNL || kNLS;                       // the NL4 table (8 copies)
+    constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_Q2S || MODE == UG_NL4 || kSub;
     static_assert(kBF != BF_NONE, "a routed mode");
     constexpr int TBM = BM;
     constexpr int kAL = TBM * 8 / 256;              // A 16-byte loads per lane per K step
@@ -139,10 +146,13 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // Q2S nibble -> (C2[lo], C2[hi]) and Q2 nibble -> (lo - 2, hi - 2), 32
     // copies (entry * 32 + lane % 32).
     __shared__ __attribute__((aligned(8192))) uint32_t lut[kLutDw];
-    constexpr int kPer = kB256 ? 4 : 2;             // quantized B: K steps per period
-    // bytes of a weight row per period
-    constexpr int kRowB = kBF == BF_Q3 ? 104 : kBF == BF_Q2S ? 80 : kBF == BF_NL4 ? 72 : 40;
-    constexpr int kUPR = kRowB / 8;                 // 8-byte units per row = per lane
+    constexpr int kPer = (kB256 || kSub) ? 4 : 2;   // quantized B: K steps per period
+    // bytes of a weight row per period in LDS (Q3K-256: the 110-byte block
+    // inside the 112-byte dword-aligned window that holds it)
+    constexpr int kRowB = kBF == BF_Q3 ? 104 : kBF == BF_Q2S ? 80 : kBF == BF_NL4 ? 72 : kBF == BF_Q3K ? 112
+                          : kBF == BF_NL4S ? 136 : 40;
+    constexpr int kUB = kQ3K ? 4 : 8;               // bytes per load unit (Q3K-256 windows are 4-aligned)
+    constexpr int kUPR = kRowB / kUB;               // load units per row = per lane
     __shared__ __attribute__((aligned(16))) uint8_t Bq[4][64 * kRowB];
 
     const int tid = threadIdx.x, lane = __lane_id();
@@ -227,7 +237,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     {
         const uint8_t* W = g.experts + (int64_t)e * g.estride;
         wsrc = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)g.estride, 0x00020000);
-        constexpr int nwb = kB256 ? 256 : 32, nbb = kRowB / (kB256 ? 1 : 4);
+        constexpr int nwb = (kB256 || kSub) ? 256 : 32;
+        constexpr int nbb = kQ3K ? kQ3KBytes : kRowB / ((kB256 || kSub) ? 1 : 4);
         rb_w = (g.K / nwb) * nbb;
         mbase = kSwi ? 0 : (int)g.dn_off;
     }
@@ -241,19 +252,43 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         } else {
             wr = min(nt * BN + 64 * w + r, g.N - 1);
         }
+        if constexpr (kQ3K) return mbase + wr * rb_w;   // the row's start (unit part = u % kUPR)
         return mbase + wr * rb_w + 8 * part;
     };
     struct RawP {
-        u32x2 u[kUPR];
+        uint32_t u[kUPR * (kUB / 4)];
     };
     auto load_period = [&](int nt, int p, RawP& R) {
+        // Q3K-256: the units' offsets are formed here each time (28 of them
+        // kept live across the loop would not fit the registers)
+        int ln = lane;
+        if constexpr (kQ3K) __asm__ volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < kUPR; ++i)
-            R.u[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, unit_off(nt, i) + p * kRowB, 0, 0));
+        for (int i = 0; i < kUPR; ++i) {
+            if constexpr (kQ3K) {
+                // the dword-aligned 112-byte window holding block p of the row
+                const int u = ln + 64 * i, r = u / kUPR, part = u - r * kUPR;
+                const int oc = min(nt * (BN / 2) + 32 * w + (r & 31), g.half_n - 1);
+                const int rs = ((r >> 5) ? g.half_n + oc : oc) * rb_w;
+                const int wo = ((rs + kQ3KBytes * p) & ~3) + 4 * part;
+                R.u[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, wo, 0, 0);
+            } else {
+                const u32x2 v = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, unit_off(nt, i) + p * kRowB, 0, 0));
+                R.u[2 * i] = v[0];
+                R.u[2 * i + 1] = v[1];
+            }
+        }
     };
     auto put_period = [&](const RawP& R) {
 #pragma unroll
-        for (int i = 0; i < kUPR; ++i) *reinterpret_cast<u32x2*>(&Bq[w][8 * (lane + 64 * i)]) = R.u[i];
+        for (int i = 0; i < kUPR; ++i) {
+            if constexpr (kQ3K) {
+                *reinterpret_cast<uint32_t*>(&Bq[w][4 * (lane + 64 * i)]) = R.u[i];   // Q3K: kSwi only
+            } else {
+                *reinterpret_cast<u32x2*>(&Bq[w][8 * (lane + 64 * i)]) = u32x2{R.u[2 * i], R.u[2 * i + 1]};
+            }
+        }
     };
     // The lane's raw bytes of step kt from the period area: Q3 q[sn][0..2] =
     // the 12 index bytes of sub-block 2 (kt % 4) + h, q[sn][3..4] = the tail;
@@ -307,7 +342,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 
     // LDS byte address of a table entry = cb | entry << 7 (32 copies) or << 5
     // (NL4, 8 copies).
-    const uint32_t cb = lds_addr(lut) | (kNL ? (uint32_t)(lane & 7) * 4u : (uint32_t)l32 * 4u);
+    const uint32_t cb = lds_addr(lut) | (kNLTab ? (uint32_t)(lane & 7) * 4u : (uint32_t)l32 * 4u);
 
     // Fragments of one K step: f[sn][kk] = weights k = 32h + 8kk .. +7 of
     // column half sn; 256-weight blocks: dl[sn] = d / 128 of the lane's
@@ -397,14 +432,14 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 
     // acc: the output sums; Q3: tmp holds the current 256-weight block's sums
     // of x * s * c, added to acc times d / 128 at the block's end.
-    f32x16 acc[kSMX][2], tmp[kB256 ? kSMX : 1][2];
+    f32x16 acc[kSMX][2], tmp[(kB256 || kQ3K) ? kSMX : 1][2];
 #pragma unroll
     for (int a = 0; a < kSMX; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    if constexpr (kB256) {
+    if constexpr (kB256 || kQ3K) {
 #pragma unroll
         for (int a = 0; a < kSMX; ++a)
 #pragma unroll
@@ -495,9 +530,9 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                         if (!(sn ? oc1 : oc0)) continue;
                         const int br = sn ? br1 : br0;
                         float v = acc[sm][sn][r];
+                        if constexpr (kNL) v *= 0.0625f;           // the fold's factor 16
                         const int64_t o = (int64_t)(r0 + m) * g.ldo + br;
-                        if (g.y16) g.y16[o] = (uint16_t)f32_to_f16_bits(v);
-                        else g.out32[o] = v;
+                        g.out32[o] = v;
                     }
                 }
             }
@@ -516,16 +551,19 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     {
         for (int i = tid; i < kLutDw; i += 256) {
             uint32_t v;
-            if (kQ3) {
+            if (kQ3 || kQ3K) {
                 const int en = i >> 5;
                 v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
             } else if (kNat) {
                 const int en = i >> 3;
                 v = pack2(f32_to_f16_bits((float)kT4[en & 15]), f32_to_f16_bits((float)kT4[en >> 4]));
             } else if (kNL) {
+                // T4 / 8 (exact): the fragments hold 16 d T4 / 128, undone in
+                // the epilogue, so that d T4 / 128 stays in fp16's normal range
+                // for every normal d (|T4| >= 10) up to 4126
                 const int en = i >> 3;
-                v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.0078125f),
-                          f32_to_f16_bits((float)kT4[en >> 4] * 0.0078125f));
+                v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.125f),
+                          f32_to_f16_bits((float)kT4[en >> 4] * 0.125f));
             } else {
                 const int en = (i >> 5) & 15;              // 16 entries; the rest repeats
                 const int lo = en & 3, hi = en >> 2;
@@ -622,12 +660,166 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
             }
         }
     };
+    // ---- the 6-bit sub-scaled codecs (one N tile per block, a period per
+    // 256-weight block = 4 K steps).  Per step x of a block and column half
+    // sn, the lane's raw bytes come from its row's window in the wave's
+    // period area; Q3K-256 windows start 0 or 2 bytes before the block (the
+    // block's dword alignment), so its words are realigned with a funnel
+    // shift.
+    auto run_sub = [&](auto smc) {
+        constexpr int SM = decltype(smc)::value;
+        RawP P;
+        load_period(nt0, 0, P);
+        __syncthreads();                             // stage 0 and the table written
+        int rs[2];                                   // record offset of the lane's row, per half
+#pragma unroll
+        for (int sn = 0; sn < 2; ++sn) rs[sn] = brow_of(nt0, sn) * rb_w;
+        auto step_sub = [&](int kt, RawA& Ra) {
+            const int x = kt & 3;                    // step within the block (wave-uniform)
+            const int st = kt & 1;
+            put_a(st ^ 1, Ra);
+            if (x == 0) put_period(P);
+            load_a(min(kt + 3, nk - 1), Ra);
+            if (x == 0) load_period(nt0, kt / kPer + 1, P);
+            if constexpr (kQ3K) {
+                // per half: the step's 24 index bytes (6 words), d / 128 and the
+                // step's four 6-bit sub-scales (bits 24 x .. 24 x + 23 of the 96)
+                uint32_t fq[2][4], f24[2];
+                float dl[2];
+#pragma unroll
+                for (int sn = 0; sn < 2; ++sn) {
+                    const uint32_t* rw = reinterpret_cast<const uint32_t*>(&Bq[w][(32 * sn + l32) * kRowB]);
+                    const bool sh = ((rs[sn] + kQ3KBytes * (kt >> 2)) & 2) != 0;
+                    auto al = [&](uint32_t lo, uint32_t hi) { return sh ? __builtin_amdgcn_alignbit(hi, lo, 16) : lo; };
+                    uint32_t dw[7], q[6];
+#pragma unroll
+                    for (int i = 0; i < 7; ++i) dw[i] = rw[6 * x + i];
+#pragma unroll
+                    for (int i = 0; i < 6; ++i) q[i] = al(dw[i], dw[i + 1]);
+                    // the lane's 8 codes of chunk kk: bits 48 kk + 24 h of the 192
+                    fq[sn][0] = hh ? __builtin_amdgcn_alignbit(q[1], q[0], 24) : q[0];
+                    fq[sn][1] = hh ? (q[2] >> 8) : __builtin_amdgcn_alignbit(q[2], q[1], 16);
+                    fq[sn][2] = hh ? __builtin_amdgcn_alignbit(q[4], q[3], 24) : q[3];
+                    fq[sn][3] = hh ? (q[5] >> 8) : __builtin_amdgcn_alignbit(q[5], q[4], 16);
+                    const uint32_t t24 = rw[24], t25 = rw[25], t26 = rw[26], t27 = rw[27];
+                    const uint32_t W0 = al(t24, t25), W1 = al(t25, t26), W2 = al(t26, t27);
+                    const uint32_t W3 = sh ? (t27 >> 16) : t27;
+                    const uint32_t S0 = __builtin_amdgcn_alignbit(W1, W0, 16);
+                    const uint32_t S1 = __builtin_amdgcn_alignbit(W2, W1, 16);
+                    const uint32_t S2 = __builtin_amdgcn_alignbit(W3, W2, 16);
+                    f24[sn] = x == 0 ? S0 : x == 1 ? __builtin_amdgcn_alignbit(S1, S0, 24)
+                              : x == 2 ? __builtin_amdgcn_alignbit(S2, S1, 16) : (S2 >> 8);   // bits 24 x ..
+                    dl[sn] = f16_bits_to_f32(W0 & 0xffffu) * 0.0078125f;
+                }
+                // chunk kk = the 16-weight sub-block 4 x + kk.  B = s * c with
+                // |s c| up to 4064, beyond fp16's exact integers: it enters as
+                // the two exact parts (s mod 16) c and 16 floor(s / 16) c, each
+                // an fp16 integer, summed by two MFMAs into the block's
+                // partial sums; d / 128 is applied to those at the block's end.
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    u32x4 fa[SM];
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm) fa[sm] = As[st][aslot(32 * sm + l32, 2 * kk + hh)];
+#pragma unroll
+                    for (int sn = 0; sn < 2; ++sn) {
+                        const uint32_t f = fq[sn][kk];
+                        // a plain array: clang lowers __builtin_bit_cast of an
+                        // ext_vector element as a read of element 0
+                        uint32_t fb[4];
+                        fb[0] = lds_ld(((f << 7) & 0x1F80u) | cb);
+                        fb[1] = lds_ld(((f << 1) & 0x1F80u) | cb);
+                        fb[2] = lds_ld(((f >> 5) & 0x1F80u) | cb);
+                        fb[3] = lds_ld(((f >> 11) & 0x1F80u) | cb);
+                        const int sv = sext6(f24[sn] >> (6 * kk));
+                        const _Float16 slo = (_Float16)(float)(sv & 15), shi = (_Float16)(float)(16 * (sv >> 4));
+                        const h2g slo2 = {slo, slo}, shi2 = {shi, shi};
+                        u32x4 b1, b2;
+#pragma unroll
+                        for (int pq = 0; pq < 4; ++pq) {
+                            b1[pq] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, fb[pq]) * slo2);
+                            b2[pq] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, fb[pq]) * shi2);
+                        }
+#pragma unroll
+                        for (int sm = 0; sm < SM; ++sm) {
+                            tmp[sm][sn] = mfma32_f16(fa[sm], b1, tmp[sm][sn]);
+                            tmp[sm][sn] = mfma32_f16(fa[sm], b2, tmp[sm][sn]);
+                        }
+                    }
+                }
+                if (x == 3) {                                // block done: acc += partial * d / 128
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                        for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                acc[sm][sn][r] += tmp[sm][sn][r] * dl[sn];
+                                tmp[sm][sn][r] = 0.f;
+                            }
+                }
+            } else {
+                // NL4S-256: sub-block 2 x + c is chunks 2c, 2c + 1 (one index
+                // word each); d and the 48 sub-scale bits in words 32-33
+                uint64_t sv[2];
+                float dl[2];
+#pragma unroll
+                for (int sn = 0; sn < 2; ++sn) {
+                    const uint32_t* rw = reinterpret_cast<const uint32_t*>(&Bq[w][(32 * sn + l32) * kRowB]);
+                    const uint32_t t32 = rw[32], t33 = rw[33];
+                    sv[sn] = ((uint64_t)t33 << 16) | (t32 >> 16);
+                    dl[sn] = f16_bits_to_f32(t32 & 0xffffu) * 0.0078125f;
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    u32x4 fa[SM][2];
+#pragma unroll
+                    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) fa[sm][k2] = As[st][aslot(32 * sm + l32, 2 * (2 * c + k2) + hh)];
+#pragma unroll
+                    for (int sn = 0; sn < 2; ++sn) {
+                        const uint32_t* rw = reinterpret_cast<const uint32_t*>(&Bq[w][(32 * sn + l32) * kRowB]);
+                        u32x4 fb[2];
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) {
+                            const uint32_t nb = rw[8 * x + 2 * (2 * c + k2) + hh];
+                            fb[k2][0] = lds_ld(((nb << 5) & 0x1FE0u) | cb);
+                            fb[k2][1] = lds_ld(((nb >> 3) & 0x1FE0u) | cb);
+                            fb[k2][2] = lds_ld(((nb >> 11) & 0x1FE0u) | cb);
+                            fb[k2][3] = lds_ld(((nb >> 19) & 0x1FE0u) | cb);
+                        }
+                        const float sc = dl[sn] * (float)sext6((uint32_t)(sv[sn] >> (12 * x + 6 * c)));
+#pragma unroll
+                        for (int sm = 0; sm < SM; ++sm) {
+                            f32x16 t = mfma32_f16(fa[sm][0], fb[0], f32x16{});
+                            t = mfma32_f16(fa[sm][1], fb[1], t);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[sm][sn][r] += t[r] * sc;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        };
+        for (int kt = 0; kt < nk; kt += 2) {
+            step_sub(kt, A1);
+            step_sub(kt + 1, A0);
+        }
+        epilogue(nt0, smc);
+    };
+
     // The loop is instantiated per count of live 32-row groups (ragged
     // expert tails skip the MFMAs of groups past their rows).
     const int nsm = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
     static_assert(kSMX == 2, "64-row tiles");
-    if (nsm == 2) run(Cnt<2>{});
-    else run(Cnt<1>{});
+    if constexpr (kSub) {
+        if (nsm == 2) run_sub(Cnt<2>{});
+        else run_sub(Cnt<1>{});
+    } else {
+        if (nsm == 2) run(Cnt<2>{});
+        else run(Cnt<1>{});
+    }
 
 }
 
@@ -652,17 +844,18 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
     const unsigned grid = gemm_grid((swi_tiles(I) + a.npb - 1) / a.npb, max_tiles);
     if (fmt == kFmtQ3S256) k_gemm<UG_Q3><<<grid, 256, 0, st>>>(a);
     else if (fmt == kFmtQ2S256) k_gemm<UG_Q2S><<<grid, 256, 0, st>>>(a);
+    else if (fmt == kFmtQ3K256) k_gemm<UG_Q3K><<<grid, 256, 0, st>>>(a);
+    else if (fmt == kFmtNL4S256) k_gemm<UG_NL4S><<<grid, 256, 0, st>>>(a);
     else k_gemm<UG_NL4><<<grid, 256, 0, st>>>(a);
 }
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
-                      hipStream_t st) {
+                      int I, int64_t dn_off, int fmt, float* y_perm, hipStream_t st) {
     GemmArgs a{};
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
-    a.dn_off = dn_off; a.out32 = y_perm; a.y16 = y_perm16; a.ldo = H;
+    a.dn_off = dn_off; a.out32 = y_perm; a.ldo = H;
     a.npb = (I / BK) % 2 == 0 ? 4 : 1;               // tiles chain only with an even step count
     const unsigned grid = gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles);
     if (fmt == kFmtNL4) k_gemm<DN_NL4><<<grid, 256, 0, st>>>(a);

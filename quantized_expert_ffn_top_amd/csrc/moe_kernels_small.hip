@@ -78,6 +78,51 @@ __global__ void k_dequant_q2(const uint8_t* __restrict__ blocks, int64_t n_blk,
     }
 }
 
+// One thread per 16-weight sub-block of a Q3K-256 block (110 bytes, 2-byte
+// aligned: read bytewise): index bytes 6j .. 6j + 5, d at 96, the 6-bit
+// sub-scale j at bits 6j of the 96-bit field at 98.
+__global__ void k_dequant_q3k(const uint8_t* __restrict__ blocks, int64_t n_sub,
+                              float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_sub) return;
+    const uint8_t* b = blocks + (i >> 4) * kQ3KBytes;
+    const int j = (int)(i & 15);
+    uint64_t idx = 0;
+#pragma unroll
+    for (int t = 0; t < 6; ++t) idx |= (uint64_t)b[6 * j + t] << (8 * t);
+    const float d = f16_bits_to_f32((uint32_t)b[96] | ((uint32_t)b[97] << 8));
+    const int bit = 6 * j, by = 98 + (bit >> 3);
+    // (the second byte only when the field crosses into it: the last field
+    // ends with the block)
+    const uint32_t w = (uint32_t)b[by] | ((bit & 7) > 2 ? (uint32_t)b[by + 1] << 8 : 0u);
+    const int s = sext6(w >> (bit & 7));
+    float* o = out + i * 16;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[t] = q3_value(d, s, (int)((idx >> (3 * t)) & 7u));
+}
+
+// One thread per 32-weight sub-block of an NL4S-256 block (136 bytes, 8-byte
+// aligned): index bytes 16j .. 16j + 15, d at 128, the 6-bit sub-scale j at
+// bits 6j of the 48-bit field at 130.
+__global__ void k_dequant_nl4s(const uint8_t* __restrict__ blocks, int64_t n_sub,
+                               float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_sub) return;
+    const uint8_t* b = blocks + (i >> 3) * kNL4SBytes;
+    const int j = (int)(i & 7);
+    const float d = f16_bits_to_f32((uint32_t)b[128] | ((uint32_t)b[129] << 8));
+    const int bit = 6 * j, by = 130 + (bit >> 3);
+    const uint32_t w = (uint32_t)b[by] | ((bit & 7) > 2 ? (uint32_t)b[by + 1] << 8 : 0u);
+    const float ds = d * (float)sext6(w >> (bit & 7));
+    float* o = out + i * 32;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const uint32_t byte = b[16 * j + t];
+        o[2 * t] = ds * (float)kT4[byte & 15u] * 0.0078125f;
+        o[2 * t + 1] = ds * (float)kT4[byte >> 4] * 0.0078125f;
+    }
+}
+
 // ---------------------------------------------------------------- staging
 
 // x bf16 -> fp16 (the matrix-core operand type of the quantized experts).
@@ -319,60 +364,63 @@ __global__ void __launch_bounds__(1024) k_build_tiles(const int32_t* __restrict_
 
 // ---------------------------------------------------------------- combine
 
-// y[t][h] = sum_j w[t][j] * y_perm[inv[t*k+j]][h] (+ shared[t][h]); 4 h per thread.
 // y[t][h..h+3] = sum_j w[t][j] * y_perm[inv[t k + j]][h..h+3] (j in order)
-// + shared[t][h..h+3]; y_perm fp32 or fp16.
-template <typename YT>
-__device__ __forceinline__ float4 load4(const YT* p);
-template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
-}
-template <> __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    return make_float4(f16_bits_to_f32(v.x & 0xffffu), f16_bits_to_f32(v.x >> 16),
-                       f16_bits_to_f32(v.y & 0xffffu), f16_bits_to_f32(v.y >> 16));
-}
-template <typename YT>
-__global__ void k_combine(const YT* __restrict__ y_perm, const int32_t* __restrict__ inv,
-                          const float* __restrict__ w, int T, int k, int H,
-                          const float* __restrict__ shared, float* __restrict__ y) {
+// + shared[t][h..h+3].  A thread takes NV float4 columns of one token (column
+// c0 + 256 v); the token's rows are read eight at a time, every column of the
+// eight in flight before any is summed.
+template <int NV>
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
+                                                 const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, int k, int H,
+                                                 const float* __restrict__ shared,
+                                                 float* __restrict__ y) {
     const int t = blockIdx.y;
-    const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (h >= H) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int j = 0;
-    for (; j + 4 <= k; j += 4) {                      // four rows in flight
-        float4 v[4];
-        float wt[4];
+    const int nc = H >> 2;
+    const int c0 = blockIdx.x * (256 * NV) + threadIdx.x;
+    const int32_t* iv = inv + (int64_t)t * k;
+    const float* wt = w + (int64_t)t * k;
+    float4 acc[NV];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            wt[u] = w[t * k + j + u];
-            v[u] = load4(y_perm + (int64_t)inv[t * k + j + u] * H + h);
+    for (int v = 0; v < NV; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        const int nj = min(8, k - j0);
+        float4 r[8][NV];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u < nj) {
+                const float4* row = reinterpret_cast<const float4*>(y_perm + (int64_t)iv[j0 + u] * H);
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    if (c0 + 256 * v < nc) r[u][v] = row[c0 + 256 * v];
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc.x += wt[u] * v[u].x;
-            acc.y += wt[u] * v[u].y;
-            acc.z += wt[u] * v[u].z;
-            acc.w += wt[u] * v[u].w;
+        for (int u = 0; u < 8; ++u) {
+            if (u < nj) {
+                const float ww = wt[j0 + u];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    acc[v].x += ww * r[u][v].x;
+                    acc[v].y += ww * r[u][v].y;
+                    acc[v].z += ww * r[u][v].z;
+                    acc[v].w += ww * r[u][v].w;
+                }
+            }
         }
     }
-    for (; j < k; ++j) {
-        const float wt = w[t * k + j];
-        const float4 v = load4(y_perm + (int64_t)inv[t * k + j] * H + h);
-        acc.x += wt * v.x;
-        acc.y += wt * v.y;
-        acc.z += wt * v.z;
-        acc.w += wt * v.w;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int c = c0 + 256 * v;
+        if (c >= nc) continue;
+        if (shared) {
+            const float4 sv = reinterpret_cast<const float4*>(shared + (int64_t)t * H)[c];
+            acc[v].x += sv.x;
+            acc[v].y += sv.y;
+            acc[v].z += sv.z;
+            acc[v].w += sv.w;
+        }
+        reinterpret_cast<float4*>(y + (int64_t)t * H)[c] = acc[v];
     }
-    if (shared) {
-        const float4 s = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + h);
-        acc.x += s.x;
-        acc.y += s.y;
-        acc.z += s.z;
-        acc.w += s.w;
-    }
-    *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = acc;
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -471,6 +519,8 @@ void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, 
     if (fmt == kFmtQ3S256) k_dequant_q3s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
     else if (fmt == kFmtNL4) k_dequant_nl4<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
     else if (fmt == kFmtQ2S256) k_dequant_q2s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
+    else if (fmt == kFmtQ3K256) k_dequant_q3k<<<cdiv(2 * n32, 256), 256, 0, st>>>(b, 2 * n32, out);
+    else if (fmt == kFmtNL4S256) k_dequant_nl4s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
     else k_dequant_q2<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
 }
 
@@ -504,14 +554,14 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
 
 void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
                     const float* shared, float* y, hipStream_t st) {
-    dim3 grid(cdiv(H / 4, 256), T);
-    k_combine<float><<<grid, 256, 0, st>>>(y_perm, inv, w, T, k, H, shared, y);
-}
-
-void launch_combine16(const uint16_t* y_perm16, const int32_t* inv, const float* w, int T, int k,
-                      int H, const float* shared, float* y, hipStream_t st) {
-    dim3 grid(cdiv(H / 4, 256), T);
-    k_combine<uint16_t><<<grid, 256, 0, st>>>(y_perm16, inv, w, T, k, H, shared, y);
+    // small batches: one float4 column per thread (more blocks in flight);
+    // large ones: up to three per thread (more loads in flight per thread)
+    const int nc = H / 4;
+    const int nv = T < 1024 ? 1 : min(3, cdiv(nc, 256));
+    dim3 grid(cdiv(nc, 256 * nv), T);
+    if (nv == 1) k_combine<1><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
+    else if (nv == 2) k_combine<2><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
+    else k_combine<3><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
 }
 
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,

@@ -43,6 +43,10 @@ particular range are overwritten bit-wise --
   66..69 as for Q3S-256; bytes 70..79 = 0.
   Q2-32 block: d (bytes 0..1) = 0x2400 | 10 random bits, in [2^-6, 2^-5);
   index bytes uniform random.
+  Q3K-256 block (110 bytes) and NL4S-256 block (136 bytes): index bytes
+  uniform random; d (bytes 96..97, resp. 128..129) in [2^-9, 2^-8); the
+  6-bit sub-scale fields (bytes 98..109, resp. 130..135) in 16..31 ("rtn"
+  mode) or any value (other modes).
   (Each d range is the one a round-to-nearest encoding of N(0, 0.02) weights
   gives for that codec.)  "wide" mode instead draws each block's d binade
   from four (WIDE_D_EXPONENTS: subnormal or zero, [2^-10, 2^-9), the
@@ -66,11 +70,14 @@ Q3S_BLOCK_BYTES = 104     # field widths of the codecs (byte layout only)
 NL4_BLOCK_BYTES = 18
 Q2S_BLOCK_BYTES = 80
 Q2_BLOCK_BYTES = 10
+Q3K_BLOCK_BYTES = 110
+NL4S_BLOCK_BYTES = 136
 # format number -> (weights per block, bytes per block); the numbers are the
 # library's moe_format values
-FMT_Q3S256, FMT_NL4_32, FMT_Q2S256, FMT_Q2_32 = 2, 3, 4, 5
+FMT_Q3S256, FMT_NL4_32, FMT_Q2S256, FMT_Q2_32, FMT_Q3K256, FMT_NL4S256 = 2, 3, 4, 5, 6, 7
 BLOCKS = {FMT_Q3S256: (256, Q3S_BLOCK_BYTES), FMT_NL4_32: (32, NL4_BLOCK_BYTES),
-          FMT_Q2S256: (256, Q2S_BLOCK_BYTES), FMT_Q2_32: (32, Q2_BLOCK_BYTES)}
+          FMT_Q2S256: (256, Q2S_BLOCK_BYTES), FMT_Q2_32: (32, Q2_BLOCK_BYTES),
+          FMT_Q3K256: (256, Q3K_BLOCK_BYTES), FMT_NL4S256: (256, NL4S_BLOCK_BYTES)}
 
 # Router-bias strength.  b_e = -ZIPF_ALPHA * s * ln(rank_e).  Chosen once by
 # bisection on the 8192-token prefill workload (seed 3, s = 1.0) so that the
@@ -106,6 +113,11 @@ class Shape:
 
 TINY = Shape(hidden=256, inter=128, n_experts=16, top_k=2, shared_inter=0)
 REAL = Shape(hidden=3072, inter=512, n_experts=512, top_k=10, shared_inter=512)
+# The draft head's MoE layer (model card "Qwen3.8-Flash-Next - Avalon GGUF",
+# "MTP sidecar"): the main layers' shape, up|gate in the 3.44-bpw codec
+# (Q3K-256 here), down in NL4-32.
+MTP_HEAD = Shape(hidden=3072, inter=512, n_experts=512, top_k=10, shared_inter=512,
+                 upgate_fmt=FMT_Q3K256, down_fmt=FMT_NL4_32)
 
 
 @dataclass(frozen=True)
@@ -191,13 +203,15 @@ MODES = ("rtn", "full", "wide", "small")
 # N(0, 0.02) weights gives, and a large binade (the largest that keeps the
 # SwiGLU outputs and the down rows of N(0, 1) tokens far below 65504).
 WIDE_D_EXPONENTS = {FMT_Q3S256: (0, 5, 8, 12), FMT_NL4_32: (0, 5, 10, 13),
-                    FMT_Q2S256: (0, 5, 7, 12), FMT_Q2_32: (0, 5, 9, 12)}
+                    FMT_Q2S256: (0, 5, 7, 12), FMT_Q2_32: (0, 5, 9, 12),
+                    FMT_Q3K256: (0, 3, 6, 9), FMT_NL4S256: (0, 3, 6, 9)}
 # exponent field of d in "small" mode, every codec: d in [2^-12, 2^-11), where
 # d * |table entry| / 128 of the smaller entries falls below binary16's
 # smallest normal
 SMALL_D_EXPONENT = 3
 # exponent field of d in "rtn" and "full" mode
-RTN_D_EXPONENT = {FMT_Q3S256: 8, FMT_NL4_32: 10, FMT_Q2S256: 7, FMT_Q2_32: 9}
+RTN_D_EXPONENT = {FMT_Q3S256: 8, FMT_NL4_32: 10, FMT_Q2S256: 7, FMT_Q2_32: 9,
+                  FMT_Q3K256: 6, FMT_NL4S256: 6}
 
 
 def _set_d(hi, fmt, mode):
@@ -223,11 +237,36 @@ def _set_subscales(sb, mode):
         sb.copy_((sb & 0x33) | 0x44)
 
 
+def _set_subscales6(sb, n, mode):
+    """sb: uint8 [blocks, ceil(6n/8)] view of n six-bit sub-scale fields
+    (field j at bits 6j .. 6j+5, little-endian): in "rtn" mode each field is
+    forced into 16..31 (the range round-to-nearest gives: bit 4 set, bit 5
+    clear); any value (-32..31) otherwise."""
+    if mode != "rtn":
+        return
+    nb = sb.shape[1]
+    shifts = torch.arange(8, dtype=torch.uint8, device=sb.device)
+    bits = ((sb[:, :, None] >> shifts) & 1).reshape(sb.shape[0], 8 * nb)
+    for j in range(n):
+        bits[:, 6 * j + 4] = 1
+        bits[:, 6 * j + 5] = 0
+    w = (bits.reshape(sb.shape[0], nb, 8).to(torch.int32) << shifts.to(torch.int32)).sum(dim=2)
+    sb.copy_(w.to(torch.uint8))
+
+
 def _fix_fields(fmt, raw, mode):
     """Set the d, sub-scale and reserved fields of every block of one codec."""
     if mode not in MODES:
         raise ValueError("mode must be one of %s" % (MODES,))
     blk = raw.view(-1, BLOCKS[fmt][1])
+    if fmt == FMT_Q3K256:
+        _set_d(blk[:, 97], fmt, mode)
+        _set_subscales6(blk[:, 98:110], 16, mode)
+        return
+    if fmt == FMT_NL4S256:
+        _set_d(blk[:, 129], fmt, mode)
+        _set_subscales6(blk[:, 130:136], 8, mode)
+        return
     if fmt == FMT_Q3S256:
         _set_d(blk[:, 97], fmt, mode)
         _set_subscales(blk[:, 98:102], mode)

@@ -83,7 +83,8 @@ def _w(experts=P, stride=45056, router=P, shared=(None, None)):
     (dict(hidden=100), 2), (dict(hidden=256 * 33 + 0, inter=96), 2), (dict(inter=32), 2),
     (dict(n_experts=0), 2), (dict(top_k=17, n_experts=16), 2), (dict(shared_inter=100), 2),
     (dict(upgate_fmt=1), 3), (dict(down_fmt=2), 3), (dict(upgate_fmt=5), 3),
-    (dict(down_fmt=4), 3), (dict(upgate_fmt=6), 3), (dict(down_fmt=0), 3),
+    (dict(down_fmt=4), 3), (dict(upgate_fmt=8), 3), (dict(down_fmt=0), 3),
+    (dict(down_fmt=6), 3), (dict(down_fmt=7), 3),
 ])
 def test_layer_forward_rejects_bad_shapes(case, status):
     base = dict(hidden=256, inter=128, n_experts=16, top_k=2, shared_inter=0, upgate_fmt=2,

@@ -81,14 +81,58 @@ def test_dequant_q2_hand_blocks_bitexact():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("ug,dn", [(synth.FMT_Q2S256, synth.FMT_Q2_32), (synth.FMT_NL4_32, synth.FMT_NL4_32)])
-def test_dequant_real_mixed_experts_bitexact(ug, dn):
+def _dequant_padded(fmt, raw, n):
+    """moe_dequantize on raw block bytes copied into a 16-byte-multiple buffer."""
+    flat = np.ascontiguousarray(raw, dtype=np.uint8).reshape(-1)
+    src = torch.zeros(((flat.size + 15) // 16) * 16, dtype=torch.uint8, device=dev())
+    src[:flat.size] = _u8(flat)
+    out = torch.empty(n, dtype=torch.float32, device=dev())
+    Q.moe_dequantize(fmt, src, n, out)
+    return out.cpu().numpy()
+
+
+def test_dequant_q3k_hand_blocks_bitexact():
+    """Every 6-bit sub-scale (-32..31) at every one of the 16 positions, with
+    d from subnormal to the largest finite and negative."""
+    blocks = []
+    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
+        for base in (-32, -16, 0, 16):
+            s = [base + j for j in range(16)]
+            blocks.append(OF.pack_q3k_block(d_bits, s, [i % 8 for i in range(256)]))
+            blocks.append(OF.pack_q3k_block(d_bits, s[::-1], [7 - (i * 5) % 8 for i in range(256)]))
+    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, OF.Q3K_BLOCK_BYTES)
+    got = _dequant_padded(Q.MOE_FMT_Q3K256, raw, raw.shape[0] * 256)
+    ref = OF.dequant_q3k(raw).reshape(-1).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_nl4s_hand_blocks_bitexact():
+    """Every 6-bit sub-scale at every one of the 8 positions, every table entry."""
+    blocks = []
+    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
+        for base in range(-32, 32, 8):
+            s = [base + j for j in range(8)]
+            blocks.append(OF.pack_nl4s_block(d_bits, s, [i % 16 for i in range(256)]))
+            blocks.append(OF.pack_nl4s_block(d_bits, s[::-1], [15 - (i * 7) % 16 for i in range(256)]))
+    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, OF.NL4S_BLOCK_BYTES)
+    got = _dequant_padded(Q.MOE_FMT_NL4S256, raw, raw.shape[0] * 256)
+    ref = OF.dequant_nl4s(raw).reshape(-1).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("ug,dn,mode", [(synth.FMT_Q2S256, synth.FMT_Q2_32, "full"),
+                                        (synth.FMT_NL4_32, synth.FMT_NL4_32, "full"),
+                                        (synth.FMT_Q3K256, synth.FMT_NL4_32, "rtn"),
+                                        (synth.FMT_Q3K256, synth.FMT_Q2_32, "wide"),
+                                        (synth.FMT_NL4S256, synth.FMT_NL4_32, "small"),
+                                        (synth.FMT_NL4S256, synth.FMT_Q2_32, "wide")])
+def test_dequant_real_mixed_experts_bitexact(ug, dn, mode):
     """Records of the mixed-format layers at real shape: every block of 8
     experts, GPU-generated, against the oracle on the CPU-regenerated bytes."""
     sh = synth.Shape(3072, 512, 512, 10, 512, ug, dn)
     for e in range(0, 512, 64):
-        rec_gpu = synth.expert_record(sh, 5, 1, e, device=dev(), mode="full")
-        rec_cpu = synth.expert_record(sh, 5, 1, e, device="cpu", mode="full").numpy()
+        rec_gpu = synth.expert_record(sh, 5, 1, e, device=dev(), mode=mode)
+        rec_cpu = synth.expert_record(sh, 5, 1, e, device="cpu", mode=mode).numpy()
         assert np.array_equal(rec_gpu.cpu().numpy(), rec_cpu)
         nug = sh.upgate_bytes
         for fmt, lo, hi, n in ((ug, 0, nug, 2 * sh.inter * sh.hidden),
