@@ -32,7 +32,9 @@ through the 48 layers; the roofline object is for the routed up|gate GEMMs
 1 + K tokens (K drafts, --spec K, default 2) through 48 decode-shaped
 Q3S-256 / NL4-32 layers, each independently seeded with a fresh Zipf(1.0)
 bias, RMSNorm + residual between layers, all 53 GB of experts resident.  A
-step is one 48-layer pass.
+step is one 48-layer pass, captured once in a HIP graph and replayed (each
+replay checked bit for bit against the eager pass, whose time is reported
+beside it).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--stack-prefill | --stack-decode [--spec K]]
 """
@@ -95,6 +97,8 @@ def parse():
     p.add_argument("--layers", type=int, default=16, help="decode layers rotated through")
     p.add_argument("--prefill-steps", type=int, default=10)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only the 8192-token prefill layer (profiler runs); prints its timings")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--stack-prefill", action="store_true",
                    help="the 48-layer mixed-format 9536-token prefill chunk instead")
@@ -214,7 +218,7 @@ def main():
         return
 
     results = {"decode": {}, "prefill": None}
-    for T in (1, 3, 5, 8):
+    for T in (() if args.prefill_only else (1, 3, 5, 8)):
         x = synth.tokens_bf16(T, sh.hidden, 2, 0).to(dev)
         us = distinct_experts(T, x)
         ms = time_steps(T, x, args.steps, args.warmup, args.layers)
@@ -261,6 +265,9 @@ def main():
         print("# prefill T=%d: %.3f ms, %.1f TFLOP/s, kernels %s" % (
             Tp, ms, flops / (ms * 1e-3) / 1e12, kern), file=sys.stderr)
 
+    if args.prefill_only:
+        print(json.dumps({"prefill": results["prefill"]}))
+        return
     # roofline of the dominant kernel of the headline workload (decode T=8)
     dec8 = results["decode"][8]
     kd8, U8 = dec8.pop("_kd"), dec8.pop("_U")
@@ -446,15 +453,39 @@ def stack_decode(args, Q, synth, torch, np, dev):
     for _ in range(args.warmup):
         one_pass()
     torch.cuda.synchronize()
+    h_eager = h.clone()
     steps = max(1, args.steps)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_eager = timed(one_pass)
+    # the whole step (48 layers: 5 launches each, plus the norms) captured once
+    # in a HIP graph and replayed; every replay is checked against the eager
+    # pass (the kernels are deterministic)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
         one_pass()
-    e1.record(stream)
+    stream.wait_stream(side)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    with torch.cuda.graph(graph):
+        one_pass()
+    for _ in range(3):
+        h.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(h, h_eager):
+            sys.exit("graph replay differs from the eager step")
+    ms = timed(graph.replay)
     assert bool(torch.isfinite(h).all())
     U = float(np.mean(us))
     step_bytes = sum(layer_bytes(T, u) for u in us)
@@ -474,10 +505,11 @@ def stack_decode(args, Q, synth, torch, np, dev):
                      "kernel": "whole step (all kernels of the 48 layers), algorithmic bytes"},
         "cpu_baseline": None,
         "results": {"distinct_experts_mean": U, "step_bytes": int(step_bytes),
-                    "us_per_layer": round(ms * 1e3 / nl, 2)},
+                    "us_per_layer": round(ms * 1e3 / nl, 2), "graph_replay": True,
+                    "ms_per_step_eager": round(ms_eager, 4)},
     }
-    print("# stack decode: %.3f ms per 48-layer step, U = %.1f, %.0f GB/s" % (
-        ms, U, step_bytes / (ms * 1e-3) / 1e9), file=sys.stderr)
+    print("# stack decode: %.3f ms per 48-layer step (graph replay; eager %.3f ms), U = %.1f, "
+          "%.0f GB/s" % (ms, ms_eager, U, step_bytes / (ms * 1e-3) / 1e9), file=sys.stderr)
     print(json.dumps(line))
 
 

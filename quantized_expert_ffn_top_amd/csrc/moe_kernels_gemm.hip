@@ -142,10 +142,16 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     __shared__ u32x4 As[kStages][TBM * 8];
     // Decode tables, replicated so that random indices spread over the banks:
     // Q3 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
-    // NL4 byte -> (T4[lo], T4[hi]) / 128, 8 copies (entry * 8 + lane % 8);
+    // NL4 byte -> (T4[lo], T4[hi]) (/ 8 for the down fold), 32 or 16 copies
+    // (entry * copies + lane % copies);
     // Q2S nibble -> (C2[lo], C2[hi]) and Q2 nibble -> (lo - 2, hi - 2), 32
     // copies (entry * 32 + lane % 32).
-    __shared__ __attribute__((aligned(8192))) uint32_t lut[kLutDw];
+    // NL4 tables: 32 copies (16 with the larger NL4S-256 period area, so
+    // that two blocks still fit a CU's LDS)
+    constexpr int kNLCopies = kNLS ? 16 : 32;
+    constexpr int kNLSh = kNLS ? 6 : 7;                        // log2(copies * 4)
+    constexpr int kTabDw = kNLTab ? 256 * kNLCopies : kLutDw;
+    __shared__ __attribute__((aligned(kTabDw * 4))) uint32_t lut[kTabDw];
     constexpr int kPer = (kB256 || kSub) ? 4 : 2;   // quantized B: K steps per period
     // bytes of a weight row per period in LDS (Q3K-256: the 110-byte block
     // inside the 112-byte dword-aligned window that holds it)
@@ -340,9 +346,16 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     };
 
 
-    // LDS byte address of a table entry = cb | entry << 7 (32 copies) or << 5
-    // (NL4, 8 copies).
-    const uint32_t cb = lds_addr(lut) | (kNLTab ? (uint32_t)(lane & 7) * 4u : (uint32_t)l32 * 4u);
+    // LDS byte address of a table entry = cb | entry << 7 (32 copies) or
+    // << kNLSh (NL4).
+    const uint32_t cb = lds_addr(lut) | (kNLTab ? (uint32_t)(lane & (kNLCopies - 1)) * 4u : (uint32_t)l32 * 4u);
+    // NL4: table address of index byte B of the word nb
+    auto nl_addr = [&](uint32_t nb, auto bc) {
+        constexpr int B = decltype(bc)::value;
+        constexpr uint32_t mask = 0xFFu << kNLSh;
+        const uint32_t v = B == 0 ? (nb << kNLSh) : (nb >> (8 * B - kNLSh));
+        return (v & mask) | cb;
+    };
 
     // Fragments of one K step: f[sn][kk] = weights k = 32h + 8kk .. +7 of
     // column half sn; 256-weight blocks: dl[sn] = d / 128 of the lane's
@@ -373,8 +386,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 } else {
                     nb = hh ? Rb[2 * c + 2] : Rb[2 * c + 1];
                 }
-                const uint32_t aa[4] = {((nb << 5) & 0x1FE0u) | cb, ((nb >> 3) & 0x1FE0u) | cb,
-                                        ((nb >> 11) & 0x1FE0u) | cb, ((nb >> 19) & 0x1FE0u) | cb};
+                const uint32_t aa[4] = {nl_addr(nb, Cnt<0>{}), nl_addr(nb, Cnt<1>{}), nl_addr(nb, Cnt<2>{}),
+                                        nl_addr(nb, Cnt<3>{})};
 #pragma unroll
                 for (int p = 0; p < 4; ++p) F.f[sn][kk][p] = lds_ld(aa[p]);   // (T4[lo], T4[hi]), exact
             } else if constexpr (kQ3) {
@@ -396,8 +409,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
                 const h2g d2 = {d, d};
                 const uint32_t nb = __builtin_amdgcn_perm(R[sn][kk + 1], R[sn][kk], hh ? 0x07060504u : 0x05040302u);
-                const uint32_t aa[4] = {((nb << 5) & 0x1FE0u) | cb, ((nb >> 3) & 0x1FE0u) | cb,
-                                        ((nb >> 11) & 0x1FE0u) | cb, ((nb >> 19) & 0x1FE0u) | cb};
+                const uint32_t aa[4] = {nl_addr(nb, Cnt<0>{}), nl_addr(nb, Cnt<1>{}), nl_addr(nb, Cnt<2>{}),
+                                        nl_addr(nb, Cnt<3>{})};
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
                     F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * d2);
@@ -549,28 +562,29 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // bytes.
     const int nk = g.K / BK;
     {
-        for (int i = tid; i < kLutDw; i += 256) {
+        // 16-byte chunks: four copies of one entry each
+        for (int i = tid; i < kTabDw / 4; i += 256) {
             uint32_t v;
             if (kQ3 || kQ3K) {
-                const int en = i >> 5;
+                const int en = i >> 3;
                 v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
             } else if (kNat) {
-                const int en = i >> 3;
+                const int en = i >> (kNLSh - 4);
                 v = pack2(f32_to_f16_bits((float)kT4[en & 15]), f32_to_f16_bits((float)kT4[en >> 4]));
             } else if (kNL) {
                 // T4 / 8 (exact): the fragments hold 16 d T4 / 128, undone in
                 // the epilogue, so that d T4 / 128 stays in fp16's normal range
                 // for every normal d (|T4| >= 10) up to 4126
-                const int en = i >> 3;
+                const int en = i >> (kNLSh - 4);
                 v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.125f),
                           f32_to_f16_bits((float)kT4[en >> 4] * 0.125f));
             } else {
-                const int en = (i >> 5) & 15;              // 16 entries; the rest repeats
+                const int en = (i >> 3) & 15;              // 16 entries; the rest repeats
                 const int lo = en & 3, hi = en >> 2;
                 if (kBF == BF_Q2S) v = pack2(f32_to_f16_bits((float)kC2[lo]), f32_to_f16_bits((float)kC2[hi]));
                 else v = pack2(f32_to_f16_bits((float)(lo - 2)), f32_to_f16_bits((float)(hi - 2)));
             }
-            lut[i] = v;
+            reinterpret_cast<u32x4*>(lut)[i] = u32x4{v, v, v, v};
         }
     }
     RawA A0, A1;
@@ -784,10 +798,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 #pragma unroll
                         for (int k2 = 0; k2 < 2; ++k2) {
                             const uint32_t nb = rw[8 * x + 2 * (2 * c + k2) + hh];
-                            fb[k2][0] = lds_ld(((nb << 5) & 0x1FE0u) | cb);
-                            fb[k2][1] = lds_ld(((nb >> 3) & 0x1FE0u) | cb);
-                            fb[k2][2] = lds_ld(((nb >> 11) & 0x1FE0u) | cb);
-                            fb[k2][3] = lds_ld(((nb >> 19) & 0x1FE0u) | cb);
+                            fb[k2][0] = lds_ld(nl_addr(nb, Cnt<0>{}));
+                            fb[k2][1] = lds_ld(nl_addr(nb, Cnt<1>{}));
+                            fb[k2][2] = lds_ld(nl_addr(nb, Cnt<2>{}));
+                            fb[k2][3] = lds_ld(nl_addr(nb, Cnt<3>{}));
                         }
                         const float sc = dl[sn] * (float)sext6((uint32_t)(sv[sn] >> (12 * x + 6 * c)));
 #pragma unroll

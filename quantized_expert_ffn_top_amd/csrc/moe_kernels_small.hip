@@ -365,9 +365,55 @@ __global__ void __launch_bounds__(1024) k_build_tiles(const int32_t* __restrict_
 // ---------------------------------------------------------------- combine
 
 // y[t][h..h+3] = sum_j w[t][j] * y_perm[inv[t k + j]][h..h+3] (j in order)
-// + shared[t][h..h+3].  A thread takes NV float4 columns of one token (column
-// c0 + 256 v); the token's rows are read eight at a time, every column of the
-// eight in flight before any is summed.
+// + shared[t][h..h+3].  Small batches: one float4 column per thread, four
+// rows in flight.
+__global__ void __launch_bounds__(256) k_combine_small(const float* __restrict__ y_perm,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w, int k, int H,
+                                                       const float* __restrict__ shared,
+                                                       float* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (h >= H) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+        float4 v[4];
+        float wt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            wt[u] = w[t * k + j + u];
+            v[u] = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + j + u] * H + h);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc.x += wt[u] * v[u].x;
+            acc.y += wt[u] * v[u].y;
+            acc.z += wt[u] * v[u].z;
+            acc.w += wt[u] * v[u].w;
+        }
+    }
+    for (; j < k; ++j) {
+        const float wt = w[t * k + j];
+        const float4 v = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + j] * H + h);
+        acc.x += wt * v.x;
+        acc.y += wt * v.y;
+        acc.z += wt * v.z;
+        acc.w += wt * v.w;
+    }
+    if (shared) {
+        const float4 s = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + h);
+        acc.x += s.x;
+        acc.y += s.y;
+        acc.z += s.z;
+        acc.w += s.w;
+    }
+    *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = acc;
+}
+
+// The same sum for large batches: a thread takes NV float4 columns of one
+// token (column c0 + 256 v); the token's rows are read eight at a time, every
+// column of the eight in flight before any is summed.
 template <int NV>
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
                                                  const int32_t* __restrict__ inv,
@@ -557,7 +603,11 @@ void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int
     // small batches: one float4 column per thread (more blocks in flight);
     // large ones: up to three per thread (more loads in flight per thread)
     const int nc = H / 4;
-    const int nv = T < 1024 ? 1 : min(3, cdiv(nc, 256));
+    if (T < 1024) {
+        k_combine_small<<<dim3(cdiv(nc, 256), T), 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
+        return;
+    }
+    const int nv = min(3, cdiv(nc, 256));
     dim3 grid(cdiv(nc, 256 * nv), T);
     if (nv == 1) k_combine<1><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
     else if (nv == 2) k_combine<2><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
