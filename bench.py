@@ -6,8 +6,9 @@ codec), top-10 with softmax over the selected logits, one always-on bf16
 shared expert (I_s=512), I=512; router W_r bf16 [512][3072] plus a Zipf(1.0)
 popularity bias; tokens bf16 N(0,1).  A step is one whole layer forward
 (router, top-k, permutation, up|gate + SwiGLU, down, combine) over a batch of
-T tokens, T = 8 for the headline value; T = 1 and 3 are reported beside it,
-and the 8192-token prefill chunk too.  Decode steps rotate through 16
+T tokens, T = 8 for the headline value; T = 1, 3 and 5 are reported beside
+it, and the 8192-token prefill chunk too (Zipf and uniform routing, the same
+experts).  Decode steps rotate through 16
 independently seeded layers (17.7 GB of packed experts) so the 256 MB
 Infinity Cache cannot serve repeated experts; inputs are resident in HBM
 before timing starts.
@@ -18,7 +19,9 @@ recorded by the library around that kernel on the caller's stream; its
 algorithmic bytes are those of the experts the batch actually routes to.
 
 cpu_baseline: the CPU oracle (fp64 NumPy, dequantising from the packed bytes)
-on one T = 8 decode layer of the same workload.
+on T = 8 decode layers of the same workload, all host cores; results.cpu_oracle
+adds the same sample on one thread and an expert sample of the 8192-token
+prefill layer.
 
 --stack-prefill runs the mixed-format workload instead and prints its own
 JSON line: one 9536-token chunk through 48 layers whose routed experts use the
@@ -100,6 +103,8 @@ def parse():
     p.add_argument("--prefill-only", action="store_true",
                    help="only the 8192-token prefill layer (profiler runs); prints its timings")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--host-gen", action="store_true",
+                   help="build the synthetic layers on the host and copy them (profiler runs)")
     p.add_argument("--stack-prefill", action="store_true",
                    help="the 48-layer mixed-format 9536-token prefill chunk instead")
     p.add_argument("--stack-decode", action="store_true",
@@ -112,6 +117,10 @@ def parse():
     p.add_argument("--copy-probe", action="store_true",
                    help="run only four 1 GiB device-to-device copies (the byte calibration "
                         "of the rocprofv3 traffic counters)")
+    p.add_argument("--traffic-json", nargs=4,
+                   metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="write profiles/traffic.json from the counter-collection CSVs of the "
+                        "FETCH_SIZE and WRITE_SIZE passes over --traffic-probe and --copy-probe")
     p.add_argument("--summarize", nargs="+", metavar="CSV",
                    help="print per-(kernel, grid) tables of rocprofv3 kernel-trace or "
                         "counter-collection CSV files and exit")
@@ -123,6 +132,9 @@ def main():
     if args.summarize:
         for path in args.summarize:
             summarize_csv(path)
+        return
+    if args.traffic_json:
+        write_traffic_json(*args.traffic_json)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -156,7 +168,17 @@ def main():
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
 
     t0 = time.time()
-    layers = [synth.real_layer(sh, 2, l, zipf_s=1.0, device=dev) for l in range(args.layers)]
+    if args.host_gen:
+        # built on the host and copied: the only GPU kernels of the process are
+        # then the library's and the runtime's copies (profiler runs)
+        def host_layer(l):
+            L = synth.real_layer(sh, 2, l, zipf_s=1.0, device="cpu")
+            for f in ("experts", "router_w", "router_b", "shared_ug", "shared_down"):
+                setattr(L, f, getattr(L, f).to(dev))
+            return L
+        layers = [host_layer(l) for l in range(args.layers)]
+    else:
+        layers = [synth.real_layer(sh, 2, l, zipf_s=1.0, device=dev) for l in range(args.layers)]
     wts = [Q.weights(L.experts, sh.expert_bytes, L.router_w, L.router_b, L.shared_ug,
                      L.shared_down) for L in layers]
     torch.cuda.synchronize()
@@ -217,7 +239,7 @@ def main():
         print("# traffic probe: %d decode layers at T=8" % (2 * args.layers), file=sys.stderr)
         return
 
-    results = {"decode": {}, "prefill": None}
+    results = {"decode": {}, "prefill": None, "prefill_uniform": None}
     for T in (() if args.prefill_only else (1, 3, 5, 8)):
         x = synth.tokens_bf16(T, sh.hidden, 2, 0).to(dev)
         us = distinct_experts(T, x)
@@ -243,30 +265,47 @@ def main():
         print("# decode T=%d: %.4f ms/step, U=%.1f, %.0f GB/s layer, kernels %s" % (
             T, ms, U, lb / (ms * 1e-3) / 1e9, kern), file=sys.stderr)
 
+    pre_sample = None
     if not args.no_prefill:
         Tp = 8192
         x = synth.tokens_bf16(Tp, sh.hidden, 3, 0).to(dev)
-        ms = time_steps(Tp, x, args.prefill_steps, 2, 1)
-        kd = time_kernels(Tp, x, 4, 1, 12)
-        names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate",
-                 "down", "combine"]
-        flops = FLOP_PER_TOKEN * Tp
-        ug_flops = 2.0 * Tp * K * 2 * I * H
-        dn_flops = 2.0 * Tp * K * I * H
-        kern = {nm: {"us": round(t * 1e3, 1)} for nm, t in zip(names, kd)}
-        kern["upgate"]["TFLOPs"] = round(ug_flops / (kd[5] * 1e-3) / 1e12, 1)
-        kern["down"]["TFLOPs"] = round(dn_flops / (kd[6] * 1e-3) / 1e12, 1)
-        results["prefill"] = {
-            "tokens": Tp, "tokens_per_s": round(Tp / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
-            "algorithmic_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
-            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-            "kernels": kern,
-        }
-        print("# prefill T=%d: %.3f ms, %.1f TFLOP/s, kernels %s" % (
-            Tp, ms, flops / (ms * 1e-3) / 1e12, kern), file=sys.stderr)
+        L0 = layers[0]
+        # the same experts and router with the Zipf bias (wts[0]) and with none
+        # (uniform routing)
+        w_uni = Q.weights(L0.experts, sh.expert_bytes, L0.router_w, torch.zeros_like(L0.router_b),
+                          L0.shared_ug, L0.shared_down)
+        for key, wl in (("prefill", wts), ("prefill_uniform", [w_uni])):
+            saved = wts[0]
+            wts[0] = wl[0]
+            ms = time_steps(Tp, x, args.prefill_steps, 2, 1)
+            kd = time_kernels(Tp, x, 4, 1, 12)
+            wts[0] = saved
+            names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate",
+                     "down", "combine"]
+            flops = FLOP_PER_TOKEN * Tp
+            ug_flops = 2.0 * Tp * K * 2 * I * H
+            dn_flops = 2.0 * Tp * K * I * H
+            kern = {nm: {"us": round(t * 1e3, 1)} for nm, t in zip(names, kd)}
+            kern["upgate"]["TFLOPs"] = round(ug_flops / (kd[5] * 1e-3) / 1e12, 1)
+            kern["down"]["TFLOPs"] = round(dn_flops / (kd[6] * 1e-3) / 1e12, 1)
+            results[key] = {
+                "tokens": Tp, "routing": "Zipf(1.0)" if key == "prefill" else "uniform",
+                "tokens_per_s": round(Tp / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                "algorithmic_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                "kernels": kern,
+            }
+            print("# %s T=%d: %.3f ms, %.1f TFLOP/s, kernels %s" % (
+                key, Tp, ms, flops / (ms * 1e-3) / 1e12, kern), file=sys.stderr)
+        if not args.no_cpu and not args.prefill_only:
+            ids = torch.empty((Tp, sh.top_k), dtype=torch.int32, device=dev)
+            y = torch.empty((Tp, sh.hidden), dtype=torch.float32, device=dev)
+            Q.moe_layer_forward(d, wts[0], x, y, ws, topk_ids_out=ids)
+            torch.cuda.synchronize()
+            pre_sample = (L0, x, ids)
 
     if args.prefill_only:
-        print(json.dumps({"prefill": results["prefill"]}))
+        print(json.dumps({"prefill": results["prefill"], "prefill_uniform": results["prefill_uniform"]}))
         return
     # roofline of the dominant kernel of the headline workload (decode T=8)
     dec8 = results["decode"][8]
@@ -282,6 +321,11 @@ def main():
             "bytes_per_launch": int(ub), "us_per_launch": round(kd8[1] * 1e3, 2)}
 
     cpu = None if args.no_cpu else cpu_baseline(layers, sh)
+    if not args.no_cpu:
+        results["cpu_oracle"] = {"decode_T8_all_cores": cpu,
+                                 "decode_T8_one_thread": cpu_baseline(layers, sh, min_s=6.0, threads=1)}
+        if pre_sample is not None:
+            results["cpu_oracle"]["prefill_8192_expert_sample"] = cpu_baseline_prefill(*pre_sample, sh)
 
     ms8 = dec8["ms_per_step"]
     line = {
@@ -574,6 +618,61 @@ def summarize_csv(path):
     print()
 
 
+def counter_means(path, counter, count=False):
+    """Mean per dispatch of `counter` (summed over its rows within a dispatch),
+    per kernel name, from a rocprofv3 counter-collection CSV (count: the
+    number of dispatches instead)."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("moe::", "")
+    out = collections.defaultdict(list)
+    for key, v in per.items():
+        out[names[key]].append(v)
+    return {k: (len(v) if count else sum(v) / len(v)) for k, v in out.items()}
+
+
+TRAFFIC_SOURCES = ["moe_common.hpp", "moe_kernels.hpp", "moe_kernels_decode.hip"]
+
+
+def write_traffic_json(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    """HBM bytes per launch of the three decode kernels from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a 1 GiB device copy (1,048,576 KiB read and written)."""
+    fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
+    ndisp = {k: n for k, n in counter_means(fetch_csv, "FETCH_SIZE", count=True).items()}
+    ndisp = {kern: next((n for k, n in ndisp.items() if k.startswith(kern)), 0)
+             for kern in ("k_dec_stage1", "k_upgate_dec", "k_down_dec")}
+    cf = [v for k, v in counter_means(cfetch_csv, "FETCH_SIZE").items() if "copyBuffer" in k]
+    cw = [v for k, v in counter_means(cwrite_csv, "WRITE_SIZE").items() if "copyBuffer" in k]
+    ff, wf = 1048576.0 / max(cf), 1048576.0 / max(cw)
+    sha = source_digest(TRAFFIC_SOURCES)
+    out = {}
+    for kern in ("k_dec_stage1", "k_upgate_dec", "k_down_dec"):
+        fk = [v for k, v in fetch.items() if k.startswith(kern)]
+        wk = [v for k, v in write.items() if k.startswith(kern)]
+        if not fk or not wk:
+            continue
+        out[kern] = {
+            "sources": TRAFFIC_SOURCES, "sources_sha256": sha,
+            "hbm_bytes_per_launch": int(round((fk[0] * ff + wk[0] * wf) * 1024)),
+            "fetch_kib_per_dispatch": round(fk[0], 2), "write_kib_per_dispatch": round(wk[0], 2),
+            "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+            "workload": "decode layer, T=8 tokens, %d launches over %d rotating layers "
+                        "(bench.py --traffic-probe --host-gen --layers %d)" % (
+                            ndisp[kern], ndisp[kern] // 2, ndisp[kern] // 2)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print("wrote %s: %s" % (path, {k: v["hbm_bytes_per_launch"] for k, v in out.items()}))
+
+
 def source_digest(files):
     """sha256 over the named kernel sources, in order (the kernel's identity)."""
     h = hashlib.sha256()
@@ -596,9 +695,10 @@ def traffic_for(kernel, algo_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layers, sh, min_s=10.0):
+def cpu_baseline(layers, sh, min_s=10.0, threads=None):
     """The oracle as it stands, on decode layers of the workload (T = 8 tokens
-    each, layer after layer until at least `min_s` seconds of CPU work)."""
+    each, layer after layer until at least `min_s` seconds of CPU work), with
+    the BLAS on `threads` threads (default: every core the process may use)."""
     import numpy as np
     import torch
 
@@ -609,7 +709,7 @@ def cpu_baseline(layers, sh, min_s=10.0):
         from threadpoolctl import threadpool_limits
     except ImportError:                                     # pragma: no cover
         threadpool_limits = None
-    cores = len(os.sched_getaffinity(0))
+    cores = threads or len(os.sched_getaffinity(0))
     T = 8
     x = synth.tokens_bf16(T, sh.hidden, 2, 0)
 
@@ -645,6 +745,49 @@ def cpu_baseline(layers, sh, min_s=10.0):
             "sample": "%d decode layers of the workload, T=8 tokens each (router, top-k, ~60 "
                       "routed experts dequantised from their packed bytes, shared expert), "
                       "fp64 NumPy, %.1f s" % (done, dt)}
+
+
+def cpu_baseline_prefill(layer, x, ids, sh, min_s=10.0):
+    """The oracle on an expert sample of the 8192-token prefill layer: experts
+    taken in id order, each dequantised from its packed bytes and run (SwiGLU
+    FFN, fp64) on all of its routed rows, until at least `min_s` seconds; the
+    router, top-k and shared expert are not in the sample.  tokens/s = the
+    rows processed / k / time."""
+    import numpy as np
+    import torch
+
+    from oracle import formats as OF
+    from oracle import moe as OM
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                     # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    xs = OM.bf16_bits_to_float(x.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+    ids = ids.cpu().numpy()
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    t0 = time.time()
+    rows = experts = 0
+    try:
+        for e in range(sh.n_experts):
+            toks = np.nonzero((ids == e).any(axis=1))[0]
+            if len(toks) == 0:
+                continue
+            wu, wg, wd = OF.expert_matrices(layer.experts[e].cpu().numpy(), sh.hidden, sh.inter)
+            OM.ffn(xs[toks], wu, wg, wd)
+            rows += len(toks)
+            experts += 1
+            if time.time() - t0 >= min_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.time() - t0
+    return {"value": round(rows / sh.top_k / dt, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "routed experts of the 8192-token prefill layer in id order, each "
+                      "dequantised and run on all its rows: %d experts, %d rows (of %d), "
+                      "fp64 NumPy, %.1f s" % (experts, rows, ids.size, dt)}
 
 
 if __name__ == "__main__":

@@ -21,8 +21,9 @@
  *   - Pointers are DEVICE pointers unless a comment says "host".  The caller
  *     allocates and frees every buffer, the workspace included; the library
  *     never allocates or frees device memory and keeps no state except a cache
- *     of device properties.  Calls are re-entrant; concurrent calls need
- *     distinct workspaces and outputs.
+ *     of device properties and, for moe_layer_forward_noalloc only, one array
+ *     per GPU that the library's own code holds.  Calls are re-entrant;
+ *     concurrent calls need distinct workspaces and outputs.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on it; no call synchronises the host.
  *   - All argument checks (null pointers, shapes, formats, alignment,
@@ -33,10 +34,19 @@
  *     asynchronous and surface at the caller's next synchronisation.
  *   - Element types: bf16 and fp16 are passed as uint16_t bit patterns.
  *   - Preconditions not checked on the device: expert ids given to
- *     moe_permute lie in [0, E); logits are not NaN; weight scales d are
- *     finite; activations x satisfy |x| <= 65504 (the matrix-core path takes
- *     x as fp16; bf16 values in that range convert exactly down to 2^-17 and
- *     lose at most 2^-25 absolute below it).
+ *     moe_permute lie in [0, E) and are distinct within each token's row;
+ *     logits are not NaN; weight scales d are finite; the activations x and
+ *     the SwiGLU outputs a (below) satisfy |v| <= 65504.
+ *   - Numerics.  Accumulation is fp32 everywhere.  The matrix cores take x
+ *     and a as fp16: a bf16 value v converts exactly when 2^-17 <= |v| <=
+ *     65504 and with an absolute error <= 2^-25 below that (|v| > 65504
+ *     would become inf).  Routed weights enter exactly (the quantized
+ *     integers, with the scales applied in fp32 to partial sums), except the
+ *     NL4_32 down weights of the grouped-GEMM path (T > 16 or the mixed
+ *     formats), which enter as fp16_rne(16 d T4[q] / 128) / 16: relative
+ *     error <= 2^-11 for every normal d up to 4126, absolute <= 2^-29 for a
+ *     subnormal d.  The unweighted routed rows y_perm are fp32 on both paths.
+ *     The shared expert and the router are bf16 x bf16 products.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -164,7 +174,11 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
 moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                      int32_t* topk_ids, float* topk_w, void* stream);
 
-/* Counting-sort permutation (A3).  topk_ids int32 [T][k] (values in [0,E)) ->
+/* Counting-sort permutation (A3).  Each token's slots go to k experts ("Avalon"
+ * README, opening paragraphs: 10 of 512 per token) and every selected expert
+ * is computed ("Betelgeuse" post: none is dropped); grouping a batch's slots
+ * by expert lets each expert's weights be read once per batch.
+ * topk_ids int32 [T][k] (values in [0,E), distinct within a row) ->
  * offsets int32 [E+1] (expert e owns permuted rows offsets[e]..offsets[e+1]-1,
  * offsets[E] = T*k), perm int32 [T*k] (permuted row p holds flat slot
  * f = t*k + j; stable: ascending f within an expert) and inv_perm int32 [T*k]
@@ -173,8 +187,12 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs (A4-A7).  For every permuted row p of expert e (token
- * t = perm[p] / k): y_perm[p] = W_down[e] bf16_rne(silu(W_gate[e] x[t]) *
+/* Expert FFNs (A4-A7).  Model card, "Files / Main model": each routed expert
+ * is an up, a gate and a down matrix (packed up | gate | down) in the
+ * quantized types above; the shared expert sits in the dense bf16 part.  The
+ * up/gate pair is read as a SwiGLU unit, and a is rounded to bf16, the
+ * activation type of the dense part.  For every permuted row p of expert e
+ * (token t = perm[p] / k): y_perm[p] = W_down[e] bf16_rne(silu(W_gate[e] x[t]) *
  * W_up[e] x[t]), unweighted, fp32 [T*k][H].  If shared_y is not NULL and
  * desc->shared_inter > 0 the shared expert's output for every token is
  * written to shared_y fp32 [T][H].  x bf16 [T][H]; offsets/perm as produced by
@@ -184,13 +202,17 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
                           const int32_t* perm, float* y_perm, float* shared_y,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine (A8): y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k+j]]
- * (+ shared_y[t] if not NULL), summed in j order, fp32 [T][H]. */
+/* Weighted combine (A8): the layer output is the router-weighted sum of the
+ * token's k routed experts plus the shared expert ("Avalon" README, opening
+ * paragraphs; model card, "Files / Main model").
+ * y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k+j]] (+ shared_y[t] if
+ * not NULL), summed in j order, fp32 [T][H]. */
 moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float* topk_w,
                        int32_t T, int32_t k, int32_t H, const float* shared_y,
                        float* y, void* stream);
 
-/* The whole layer (A1-A8): y fp32 [T][H] from x bf16 [T][H].  If
+/* The whole layer (A1-A8), as the formula at the top of this file (its
+ * sources there): y fp32 [T][H] from x bf16 [T][H].  If
  * logits_or_null is given (fp32 [T][E]) the router is skipped.  Optional
  * outputs: topk_ids_out int32 [T][k], topk_w_out fp32 [T][k].  Tokens T <= 16
  * take the bandwidth path (every weight byte streamed once), larger T the
