@@ -247,7 +247,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
  * the library's code on that GPU and held until the process ends.  The call
  * itself allocates nothing.  Returns MOE_ERR_WORKSPACE (launching nothing)
  * when moe_workspace_size(desc, T) exceeds that size -- at the model's shape
- * (H = 3072, I = 512, 512 experts, top-10, I_s = 512) every batch up to 256
+ * (H = 3072, I = 512, 512 experts, top-10, I_s = 512) every batch up to 428
  * tokens fits.  All calls on one GPU share its array: calls that overlap in
  * time on one GPU (other streams, other host threads) race and must be
  * serialised by the caller; calls on one stream are. */
