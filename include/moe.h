@@ -45,7 +45,11 @@
  *     NL4_32 down weights of the grouped-GEMM path (T > 16 or the mixed
  *     formats), which enter as fp16_rne(16 d T4[q] / 128) / 16: relative
  *     error <= 2^-11 for every normal d up to 4126, absolute <= 2^-29 for a
- *     subnormal d.  The unweighted routed rows y_perm are fp32 on both paths.
+ *     subnormal d.  The unweighted routed rows y_perm are fp32 on the bandwidth
+ *     path; the grouped-GEMM path of moe_layer_forward holds them in fp16
+ *     (relative error <= 2^-11) unless a range check in the down GEMM finds a
+ *     value beyond 65504 or a tile of values all below 2^-10 (not all zero),
+ *     and then recomputes them in fp32; moe_expert_ffn returns them in fp32.
  *     The shared expert and the router are bf16 x bf16 products.
  */
 #ifndef MOE_H
@@ -230,9 +234,10 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
  * (kernels + 1).  Kernel order -- T <= 16: stage 1 (router logits, shared
  * up|gate partials, fp16 copy of x), routed up|gate (routing, top-k and
  * permutation, at its start), down projections (routed + shared), combine;
- * T > 16: [router GEMM (if no logits)], top-k, fp16 staging, permutation (3
- * kernels, one mark), [shared expert GEMMs (2 kernels, one mark)], routed
- * up|gate GEMM, routed down GEMM, combine. */
+ * T > 16: [router and shared up|gate GEMM (if no logits or a shared
+ * expert)], top-k, fp16 staging, permutation (3 kernels, one mark), [shared
+ * down GEMM], routed up|gate GEMM, routed down GEMM (fp16 rows), its fp32
+ * repeat (does nothing unless the range check asked for it), combine. */
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,
                                    const uint16_t* x, int32_t T, const float* logits_or_null,
                                    float* y, int32_t* topk_ids_out, float* topk_w_out, void* ws,

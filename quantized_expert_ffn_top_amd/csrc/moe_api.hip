@@ -103,7 +103,7 @@ Ws layout(int H, int I, int E, int k, int Is, int T, bool std_fmt) {
     s.inv = take(n * 4);
     const int gemm_tiles = (int)((n + kGemmBM - 1) / kGemmBM) + (n < (size_t)E ? (int)n : E);
     s.tiles = take((size_t)(s.max_tiles > gemm_tiles ? s.max_tiles : gemm_tiles) * 12);
-    s.ntiles = take(4);
+    s.ntiles = take(8);                     // tile count, then the down GEMM's fp16 range flag
     s.a16 = take(n * I * 2);
     s.a_sh = take((size_t)T * (Is > 0 ? Is : 1) * 2);
     s.y_perm = take(n * H * 4);
@@ -315,7 +315,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, gemm_tiles, perm, k, x16, H, I, a16,
                        desc->upgate_fmt, st);
     launch_gemm_down(ex, wts->expert_stride, tiles, nt, gemm_tiles, a16, H, I, upgate_bytes(desc),
-                     desc->down_fmt, y_perm, st);
+                     desc->down_fmt, y_perm, nullptr, nullptr, nullptr, st);
     return launched("moe_expert_ffn");
 }
 
@@ -330,7 +330,7 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
         return fail(MOE_ERR_ALIGN, "y_perm, shared_y and y must be 16-byte aligned");
     moe_status s = check_device();
     if (s != MOE_OK) return s;
-    launch_combine(y_perm, inv_perm, topk_w, T, k, H, shared_y, y, (hipStream_t)stream);
+    launch_combine(y_perm, nullptr, inv_perm, topk_w, T, k, H, shared_y, y, (hipStream_t)stream);
     return launched("moe_combine");
 }
 
@@ -439,12 +439,23 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         launch_gemm_upgate(ex, wts->expert_stride, tiles, nt, L.max_tiles, perm, k, x16, H, I, a16,
                            desc->upgate_fmt, st);
         mk->mark();
-        // the unweighted rows go through memory in fp32 (any magnitude)
+        // the unweighted rows go through memory as fp16 (half the bytes) unless
+        // the down GEMM's range check finds values fp16 would not hold well;
+        // then the second launch writes them in fp32 and the combine reads
+        // those (it does nothing otherwise)
+        int* range_flag = nt + 1;
         launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I,
-                         upgate_bytes(desc), desc->down_fmt, yp, st);
+                         upgate_bytes(desc), desc->down_fmt, yp, reinterpret_cast<uint16_t*>(yp),
+                         range_flag, nullptr, st);
         mk->mark();
+        launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I,
+                         upgate_bytes(desc), desc->down_fmt, yp, nullptr, nullptr, range_flag, st);
+        mk->mark();
+        launch_combine(yp, range_flag, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+        mk->mark();
+        return launched("moe_layer_forward");
     }
-    launch_combine(yp, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+    launch_combine(yp, nullptr, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
     mk->mark();
     return launched("moe_layer_forward");
 }

@@ -28,8 +28,8 @@ void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32
                           int32_t* ntiles, hipStream_t st);
 void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, int32_t* ntiles,
                         hipStream_t st);
-void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
-                    const float* shared, float* y, hipStream_t st);
+void launch_combine(const float* y_perm, const int* fp16_unless, const int32_t* inv, const float* w,
+                    int T, int k, int H, const float* shared, float* y, hipStream_t st);
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st);
 
@@ -71,10 +71,14 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
                         const uint16_t* x16, int H, int I, uint16_t* a16_perm, int fmt,
                         hipStream_t st);
 // dn_off: byte offset of the down matrix in an expert record; fmt: its format
-// (NL4-32 or Q2-32).  The unweighted rows are stored fp32 to y_perm.
+// (NL4-32 or Q2-32).  The unweighted rows are stored fp32 to y_perm, or, with
+// y_perm16, as fp16 there with the range check that adds to *range_flag
+// (beyond 65504, or a wave's tile of tiny nonzero values).  only_if non-null:
+// the launch does nothing unless *only_if != 0.
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, int64_t dn_off, int fmt, float* y_perm, hipStream_t st);
+                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
+                      int* range_flag, const int* only_if, hipStream_t st);
 
 // ---- dense bf16 products of the grouped-GEMM path (moe_kernels_dense.hip)
 // One launch: router logits [T][E] (+ bias) if w_r is not null, and the

@@ -6,7 +6,7 @@
 //   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
 //           mixed-format layers)
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
-//           weights, epilogue fp32 store (permuted rows)
+//           weights, epilogue fp32 (or range-checked fp16) store (permuted rows)
 //   DN_Q2   the same with Q2-32 weights
 //
 // Tile 64 token rows x 256 weight rows, K steps of 64; four waves, wave w
@@ -83,6 +83,12 @@ struct GemmArgs {
     int64_t dn_off;          // routed down: byte offset of the down matrix in a record
     uint16_t* out16;         // a16_perm / a_sh
     float* out32;            // y_perm
+    // routed down, fp16 form: y_perm as fp16 to y16 (range-checked: a wave
+    // whose stored values exceed 65504, or are all below 2^-10 without being
+    // all zero, adds 1 to *range_flag), else fp32 to out32
+    uint16_t* y16;
+    int* range_flag;
+    const int* only_if;      // non-null: the launch does nothing unless *only_if != 0
     int ldo;                 // output row length
     int npb;                 // routed: N tiles per block (consecutive, same M tile)
 };
@@ -135,6 +141,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr bool kNLTab = kNL || kNLS;                       // the NL4 table (8 copies)
     constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_Q2S || MODE == UG_NL4 || kSub;
     static_assert(kBF != BF_NONE, "a routed mode");
+    if (g.only_if && *g.only_if == 0) return;
     constexpr int TBM = BM;
     constexpr int kAL = TBM * 8 / 256;              // A 16-byte loads per lane per K step
     constexpr int kSMX = TBM / 32;                  // 32-row groups per tile
@@ -525,6 +532,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         // across the N-tile loop
         int r0 = row0;
         __asm__ volatile("" : "+s"(r0));
+        float amax = 0.f;                            // fp16 form: largest |value| stored by the lane
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm) {
 #pragma unroll
@@ -545,9 +553,25 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                         float v = acc[sm][sn][r];
                         if constexpr (kNL) v *= 0.0625f;           // the fold's factor 16
                         const int64_t o = (int64_t)(r0 + m) * g.ldo + br;
-                        g.out32[o] = v;
+                        if (g.y16) {
+                            amax = fmaxf(amax, fabsf(v));
+                            g.y16[o] = (uint16_t)f32_to_f16_bits(v);
+                        } else {
+                            g.out32[o] = v;
+                        }
                     }
                 }
+            }
+        }
+        if constexpr (!kSwi) {
+            if (g.y16) {
+                // the wave's largest value: beyond fp16's range, or a tile of
+                // tiny nonzero values (where fp16 keeps few bits), sends the
+                // layer's routed rows to the fp32 form
+                float wm = amax;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+                if (lane == 0 && (wm > 65504.f || (wm > 0.f && wm < 0x1p-10f))) atomicAdd(g.range_flag, 1);
             }
         }
     };
@@ -865,11 +889,13 @@ void launch_gemm_upgate(const uint8_t* experts, int64_t estride, const int32_t* 
 
 void launch_gemm_down(const uint8_t* experts, int64_t estride, const int32_t* tiles,
                       const int32_t* ntiles, int max_tiles, const uint16_t* a16_perm, int H,
-                      int I, int64_t dn_off, int fmt, float* y_perm, hipStream_t st) {
+                      int I, int64_t dn_off, int fmt, float* y_perm, uint16_t* y_perm16,
+                      int* range_flag, const int* only_if, hipStream_t st) {
     GemmArgs a{};
     a.experts = experts; a.estride = estride; a.tiles = tiles; a.ntiles = ntiles;
     a.max_tiles = max_tiles; a.A = a16_perm; a.lda = I; a.N = H; a.K = I; a.H = H; a.I = I;
-    a.dn_off = dn_off; a.out32 = y_perm; a.ldo = H;
+    a.dn_off = dn_off; a.out32 = y_perm; a.y16 = y_perm16; a.range_flag = range_flag;
+    a.only_if = only_if; a.ldo = H;
     a.npb = (I / BK) % 2 == 0 ? 4 : 1;               // tiles chain only with an even step count
     const unsigned grid = gemm_grid((col_tiles(H) + a.npb - 1) / a.npb, max_tiles);
     if (fmt == kFmtNL4) k_gemm<DN_NL4><<<grid, 256, 0, st>>>(a);

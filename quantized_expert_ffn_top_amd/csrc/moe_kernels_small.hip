@@ -6,6 +6,8 @@
 // opening paragraphs: 10 of 512 experts), ordered by (value desc, index asc),
 // with softmax weights over the selected logits; nothing is pruned or
 // dropped ("Betelgeuse" post: every routed expert is computed).
+#include <type_traits>
+
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -316,7 +318,8 @@ __global__ void __launch_bounds__(1024) k_perm_scan(int32_t* __restrict__ hist, 
     }
     if (e == 0) {
         offsets[E] = tot;
-        *ntiles = ntot;
+        ntiles[0] = ntot;
+        ntiles[1] = 0;       // the down GEMM's fp16 range flag (the layer's workspace)
     }
 }
 
@@ -364,109 +367,72 @@ __global__ void __launch_bounds__(1024) k_build_tiles(const int32_t* __restrict_
 
 // ---------------------------------------------------------------- combine
 
+// Four consecutive values of row `row` (float4 column c) of the unweighted
+// routed rows: fp32, or fp16 (the grouped-GEMM path's range-checked form).
+template <bool H16>
+__device__ __forceinline__ float4 yrow4(const float* __restrict__ y_perm, int64_t row, int H, int c) {
+    if constexpr (H16) {
+        const uint2 v = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y_perm) + row * H)[c];
+        return make_float4(f16_bits_to_f32(v.x & 0xffffu), f16_bits_to_f32(v.x >> 16),
+                           f16_bits_to_f32(v.y & 0xffffu), f16_bits_to_f32(v.y >> 16));
+    } else {
+        return reinterpret_cast<const float4*>(y_perm + row * H)[c];
+    }
+}
+
 // y[t][h..h+3] = sum_j w[t][j] * y_perm[inv[t k + j]][h..h+3] (j in order)
-// + shared[t][h..h+3].  Small batches: one float4 column per thread, four
-// rows in flight.
-__global__ void __launch_bounds__(256) k_combine_small(const float* __restrict__ y_perm,
+// + shared[t][h..h+3].  The rows are fp16 when fp16_unless is given and
+// *fp16_unless == 0 (the down GEMM's range check passed), else fp32.  One
+// float4 column per thread, four rows in flight.
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
+                                                       const int* __restrict__ fp16_unless,
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w, int k, int H,
                                                        const float* __restrict__ shared,
                                                        float* __restrict__ y) {
     const int t = blockIdx.y;
-    const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int c = blockIdx.x * blockDim.x + threadIdx.x, h = 4 * c;
     if (h >= H) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int j = 0;
-    for (; j + 4 <= k; j += 4) {
-        float4 v[4];
-        float wt[4];
+    const bool h16 = fp16_unless && *fp16_unless == 0;
+    auto sum = [&](auto h16c) {
+        constexpr bool F16 = decltype(h16c)::value;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int j = 0;
+        for (; j + 4 <= k; j += 4) {
+            float4 v[4];
+            float wt[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            wt[u] = w[t * k + j + u];
-            v[u] = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + j + u] * H + h);
-        }
+            for (int u = 0; u < 4; ++u) {
+                wt[u] = w[t * k + j + u];
+                v[u] = yrow4<F16>(y_perm, inv[t * k + j + u], H, c);
+            }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc.x += wt[u] * v[u].x;
-            acc.y += wt[u] * v[u].y;
-            acc.z += wt[u] * v[u].z;
-            acc.w += wt[u] * v[u].w;
+            for (int u = 0; u < 4; ++u) {
+                acc.x += wt[u] * v[u].x;
+                acc.y += wt[u] * v[u].y;
+                acc.z += wt[u] * v[u].z;
+                acc.w += wt[u] * v[u].w;
+            }
         }
-    }
-    for (; j < k; ++j) {
-        const float wt = w[t * k + j];
-        const float4 v = *reinterpret_cast<const float4*>(y_perm + (int64_t)inv[t * k + j] * H + h);
-        acc.x += wt * v.x;
-        acc.y += wt * v.y;
-        acc.z += wt * v.z;
-        acc.w += wt * v.w;
-    }
+        for (; j < k; ++j) {
+            const float wt = w[t * k + j];
+            const float4 v = yrow4<F16>(y_perm, inv[t * k + j], H, c);
+            acc.x += wt * v.x;
+            acc.y += wt * v.y;
+            acc.z += wt * v.z;
+            acc.w += wt * v.w;
+        }
+        return acc;
+    };
+    float4 acc = h16 ? sum(std::true_type{}) : sum(std::false_type{});
     if (shared) {
-        const float4 s = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + h);
-        acc.x += s.x;
-        acc.y += s.y;
-        acc.z += s.z;
-        acc.w += s.w;
+        const float4 sv = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + h);
+        acc.x += sv.x;
+        acc.y += sv.y;
+        acc.z += sv.z;
+        acc.w += sv.w;
     }
     *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = acc;
-}
-
-// The same sum for large batches: a thread takes NV float4 columns of one
-// token (column c0 + 256 v); the token's rows are read eight at a time, every
-// column of the eight in flight before any is summed.
-template <int NV>
-__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
-                                                 const int32_t* __restrict__ inv,
-                                                 const float* __restrict__ w, int k, int H,
-                                                 const float* __restrict__ shared,
-                                                 float* __restrict__ y) {
-    const int t = blockIdx.y;
-    const int nc = H >> 2;
-    const int c0 = blockIdx.x * (256 * NV) + threadIdx.x;
-    const int32_t* iv = inv + (int64_t)t * k;
-    const float* wt = w + (int64_t)t * k;
-    float4 acc[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        const int nj = min(8, k - j0);
-        float4 r[8][NV];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (u < nj) {
-                const float4* row = reinterpret_cast<const float4*>(y_perm + (int64_t)iv[j0 + u] * H);
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                    if (c0 + 256 * v < nc) r[u][v] = row[c0 + 256 * v];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (u < nj) {
-                const float ww = wt[j0 + u];
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    acc[v].x += ww * r[u][v].x;
-                    acc[v].y += ww * r[u][v].y;
-                    acc[v].z += ww * r[u][v].z;
-                    acc[v].w += ww * r[u][v].w;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = c0 + 256 * v;
-        if (c >= nc) continue;
-        if (shared) {
-            const float4 sv = reinterpret_cast<const float4*>(shared + (int64_t)t * H)[c];
-            acc[v].x += sv.x;
-            acc[v].y += sv.y;
-            acc[v].z += sv.z;
-            acc[v].w += sv.w;
-        }
-        reinterpret_cast<float4*>(y + (int64_t)t * H)[c] = acc[v];
-    }
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -598,20 +564,9 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
     k_build_tiles<<<1, 1024, 0, st>>>(offsets, E, BM, tiles, ntiles);
 }
 
-void launch_combine(const float* y_perm, const int32_t* inv, const float* w, int T, int k, int H,
-                    const float* shared, float* y, hipStream_t st) {
-    // small batches: one float4 column per thread (more blocks in flight);
-    // large ones: up to three per thread (more loads in flight per thread)
-    const int nc = H / 4;
-    if (T < 1024) {
-        k_combine_small<<<dim3(cdiv(nc, 256), T), 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
-        return;
-    }
-    const int nv = min(3, cdiv(nc, 256));
-    dim3 grid(cdiv(nc, 256 * nv), T);
-    if (nv == 1) k_combine<1><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
-    else if (nv == 2) k_combine<2><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
-    else k_combine<3><<<grid, 256, 0, st>>>(y_perm, inv, w, k, H, shared, y);
+void launch_combine(const float* y_perm, const int* fp16_unless, const int32_t* inv, const float* w,
+                    int T, int k, int H, const float* shared, float* y, hipStream_t st) {
+    k_combine<<<dim3(cdiv(H / 4, 256), T), 256, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, y);
 }
 
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,

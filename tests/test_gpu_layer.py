@@ -313,6 +313,42 @@ def test_real_prefill_uniform_sampled():
     _real_case(2048, seed=3, zipf_s=0.0, sample=sample)
 
 
+# The grouped-GEMM path holds the routed rows in fp16 unless its range check
+# sends them to fp32: down weights scaled up (every NL4 d set to 2048) and
+# tokens 4 N(0, 1) push half the rows' values past 65504 (a stays near 140),
+# where fp16 would give inf; the "small" field-range cases above take the
+# same fp32 form from the other side (tiles of tiny values).
+@pytest.mark.parametrize("T", [40, 300])
+def test_gemm_rows_beyond_fp16_take_the_fp32_form(T):
+    sh = synth.Shape(512, 128, 24, 3, 64, F.FMT_Q3S256, F.FMT_NL4_32)
+    seed = 41
+    lay = synth.real_layer(sh, seed, 0, zipf_s=1.0, device=dev())
+
+    def big_down(rec):
+        dn = rec[sh.upgate_bytes:].view(-1, 18)
+        dn[:, 0] = 0x00
+        dn[:, 1] = 0x68                              # d = 2048.0
+        return rec
+
+    for e in range(sh.n_experts):
+        big_down(lay.experts[e])
+    x = (synth.tokens_bf16(T, sh.hidden, seed).float() * 4).to(torch.bfloat16).to(dev())
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter, sh.upgate_fmt,
+               sh.down_fmt)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    y, ids, w = _run_layer(d, wts, x)
+    assert np.all(np.isfinite(y))
+    assert np.abs(y).max() > 65504.0 * 2          # the routed rows left fp16's range
+    xs = bf16_np(x)
+    L = OM.router_logits(xs, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+    assert ids_valid_topk(ids, L, sh.top_k)
+    cache = ExpertCache(sh, lambda e: big_down(synth.expert_record(sh, seed, 0, e)).numpy())
+    ref = OM.layer_forward(xs, sh.top_k, cache, sh.n_experts, logits=L, shared=real_shared_np(lay),
+                           force_ids=ids)
+    assert_close(y, ref["y"], "rows beyond fp16 T=%d" % T)
+
+
 def test_layer_deterministic():
     sh, recs, x, logits = tiny_inputs(seed=4, T=300)
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, 0)
