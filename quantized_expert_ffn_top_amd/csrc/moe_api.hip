@@ -295,7 +295,8 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     const int gemm_tiles = (n + kGemmBM - 1) / kGemmBM + (n < E ? n : E);
     if ((size_t)gemm_tiles * 12 > L.ntiles - L.tiles)
         return fail(MOE_ERR_WORKSPACE, "workspace too small for the tile list");
-    s = check_device();
+    int n_cu = 0;
+    s = check_device(&n_cu);
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     const uint8_t* ex = (const uint8_t*)wts->experts;
@@ -306,6 +307,21 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
     uint16_t* x16 = at<uint16_t>(ws, L.x16);
     uint16_t* a16 = at<uint16_t>(ws, L.a16);
     uint16_t* ash = at<uint16_t>(ws, L.a_sh);
+    if (dec_path(T, H, E, std_formats(desc))) {
+        // the bandwidth kernels, with the routing given: one tile per active
+        // expert, the shared up|gate partials and the fp16 copy of x in
+        // stage 1, the routed and shared down rows in the down kernel
+        float* shp = at<float>(ws, L.shp);
+        launch_build_tiles(offsets, E, n, tiles, nt, st);
+        launch_dec_stage1(x, T, H, E, nullptr, nullptr, nullptr, sug, Is, shp, x16, kDecLogitParts, st);
+        const RouteOut ro{nullptr, nullptr, nullptr, nullptr, nullptr, const_cast<int32_t*>(perm),
+                          nullptr, tiles, nt};
+        launch_upgate_dec(ex, wts->expert_stride, nullptr, 1, nullptr, E, k, L.max_tiles, x16, T, H, I, a16,
+                          do_sh ? shp : nullptr, Is, ash, ro, n_cu, st);
+        launch_down_dec(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, T, H, I, k, sdn, ash, Is,
+                        y_perm, do_sh ? shared_y : nullptr, n_cu, st);
+        return launched("moe_expert_ffn");
+    }
     launch_to_f16(x, x16, (int64_t)T * H, st);
     launch_build_tiles(offsets, E, kGemmBM, tiles, nt, st);
     if (do_sh) {

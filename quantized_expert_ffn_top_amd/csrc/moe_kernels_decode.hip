@@ -370,9 +370,19 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
         const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
         reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
     }
-    // routing (every block; block 0 publishes it), in the partial-sum space
-    route_block<NT>(logits, np, lbias, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids, ro.w,
-                    ro.ids_out, ro.w_out, ro.offsets, ro.perm, ro.inv, ro.tiles, ro.ntiles);
+    if (logits) {
+        // routing (every block; block 0 publishes it), in the partial-sum space
+        route_block<NT>(logits, np, lbias, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids,
+                        ro.w, ro.ids_out, ro.w_out, ro.offsets, ro.perm, ro.inv, ro.tiles, ro.ntiles);
+    } else {
+        // routing given (the expert FFN export): its tile list (one tile per
+        // active expert, in expert order) and permutation
+        const int ntl = *ro.ntiles;
+        for (int i = tid; i < 3 * ntl; i += NT) s_tiles[i] = ro.tiles[i];
+        for (int i = tid; i < T * k; i += NT) s_perm[i] = ro.perm[i];
+        if (tid == 0) s_nt = ntl;
+        __syncthreads();
+    }
     const int nsl = I / 16;
     const int n_items = __builtin_amdgcn_readfirstlane(s_nt) * nsl;
     const int G = gridDim.x;
@@ -608,6 +618,8 @@ constexpr int kDnWaves = 8;
 constexpr int kDnChunkDw = 72;                    // 16 NL4 blocks of a row (288 bytes)
 constexpr int kDnStageDw = kDnChunkDw + 2;        // stage row stride (= 10 mod 32: the 16 rows x 2 lane groups of a half-wave hit distinct banks)
 constexpr int kDnLoads = 16 * kDnChunkDw / 64;    // dword loads per lane per staged chunk (18)
+constexpr int kDnChunk16 = 16 * kDnChunkDw / 4;   // 16-byte pieces of a whole chunk (288)
+constexpr int kDnLoads16 = (kDnChunk16 + 63) / 64;   // 16-byte loads per lane (5; the last by lanes 0-31)
 constexpr int kDnShSteps = 16;                    // shared down: 16x16x32 steps per load batch (Is <= 512 at once)
 
 // Persistent: blocks of kDnWaves waves; after the table is built every wave works
@@ -616,7 +628,7 @@ constexpr int kDnShSteps = 16;                    // shared down: 16x16x32 steps
 // of one expert split its H/16 slices of 16 output rows.  A wave keeps the
 // A operand of its expert (the routed rows' fp16 activations, <= 16 slots)
 // in registers.  Routed slice: the 16 rows x 16 blocks of a K chunk (4608
-// contiguous bytes) are loaded with coalesced dword loads two units ahead,
+// contiguous bytes) are loaded with coalesced 16-byte loads two units ahead,
 // written to the wave's LDS stage and decoded from there: one 16x16x32 step
 // per NL4 block (lane group g takes 8 weights = 4 index bytes; B = table
 // integers T4[q], exact fp16) and the block scale d/128 multiplies the fp32
@@ -630,7 +642,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const uint16_t* __restrict__ sh_down, const uint16_t* __restrict__ a_sh, int Is,
     float* __restrict__ y_perm, float* __restrict__ y_sh) {
     __shared__ __attribute__((aligned(32768))) uint32_t lut[kNl4LutDw];   // byte bits OR onto the address
-    __shared__ uint32_t stg[kDnWaves][16 * kDnStageDw];
+    __shared__ __attribute__((aligned(16))) uint32_t stg[kDnWaves][16 * kDnStageDw];
     __shared__ int s_claim[kDnWaves];                       // slices taken, per group of waves
     __shared__ int s_spare[kDnWaves][64];                   // the other lanes' claims land here
     const int tid = threadIdx.x, lane = __lane_id();
@@ -766,12 +778,14 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const uint32_t cbase = lds_addr(lut) + (uint32_t)(lane & 31) * 4u;
     uint32_t* st = stg[w];
 
-    // lane's dwords of a staged chunk: (global byte offset | stage dword << 16)
-    uint32_t off[kDnLoads];
+    // whole chunks (16 NL4 blocks per row): the lane's 16-byte pieces,
+    // (global byte offset | stage dword << 16); piece j is bytes 16 (j % 18)
+    // of row j / 18
+    uint32_t off[kDnLoads16];
 #pragma unroll
-    for (int i = 0; i < kDnLoads; ++i) {
-        const int j = lane + 64 * i, row = j / kDnChunkDw, col = j - row * kDnChunkDw;
-        off[i] = (uint32_t)(row * rb + 4 * col) | ((uint32_t)(row * kDnStageDw + col) << 16);
+    for (int i = 0; i < kDnLoads16; ++i) {
+        const int j = min(lane + 64 * i, kDnChunk16 - 1), row = j / 18, col = j - row * 18;
+        off[i] = (uint32_t)(row * rb + 16 * col) | ((uint32_t)(row * kDnStageDw + 4 * col) << 16);
     }
     // A operand of the expert: chunk c, block b -> av[b]
     u32x4 av[16];
@@ -783,7 +797,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     if (ONEK) load_a(0);
 
     struct Buf {
-        uint32_t v[kDnLoads];
+        uint32_t v[FULL16 ? 4 * kDnLoads16 : kDnLoads];
     };
     Buf P0, P1;
     // the expert's down rows as a buffer: 32-bit lane offsets, the unit's start
@@ -792,28 +806,43 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
         const_cast<uint8_t*>(W), 0, H * rb, 0x00020000);
     auto issue = [&](int sl, int c, Buf& B) {               // chunk c of slice sl
         const int soff = sl < nsl ? 16 * sl * rb + 288 * c : 0x7ff00000;
-        const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
-        const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
+        if constexpr (FULL16) {
+            // 16-byte loads (lanes 32-63 load their fifth piece again: the
+            // chunk has 4.5 pieces per lane; the copy is not stored)
 #pragma unroll
-        for (int i = 0; i < kDnLoads; ++i) {
-            uint32_t go;
-            if (FULL16) {
-                go = off[i] & 0xffffu;
-            } else {
-                const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
-                go = j < 16 * dpr ? (uint32_t)(row * rb + 4 * col) : 0u;
+            for (int i = 0; i < kDnLoads16; ++i) {
+                const u32x4 t = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, off[i] & 0xffffu, soff, 0));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) B.v[4 * i + q] = t[q];
             }
-            B.v[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, go, soff, 0);
+        } else {
+            const int cbk = min(16, nb - 16 * c);
+            const int dpr = cbk * kNL4Bytes / 4;
+#pragma unroll
+            for (int i = 0; i < kDnLoads; ++i) {
+                const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
+                const uint32_t go = j < 16 * dpr ? (uint32_t)(row * rb + 4 * col) : 0u;
+                B.v[i] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, go, soff, 0);
+            }
         }
     };
     auto put = [&](int c, const Buf& B) {
-        const int cbk = FULL16 ? 16 : min(16, nb - 16 * c);
-        const int dpr = FULL16 ? kDnChunkDw : cbk * kNL4Bytes / 4;
+        if constexpr (FULL16) {
+            // the stage's row stride (74 dwords) keeps pieces 8-byte aligned
 #pragma unroll
-        for (int i = 0; i < kDnLoads; ++i) {
-            if (FULL16) {
-                st[off[i] >> 16] = B.v[i];
-            } else {
+            for (int i = 0; i < kDnLoads16; ++i) {
+                if (i + 1 < kDnLoads16 || lane + 64 * i < kDnChunk16) {
+                    uint2* d2 = reinterpret_cast<uint2*>(st + (off[i] >> 16));
+                    d2[0] = make_uint2(B.v[4 * i], B.v[4 * i + 1]);
+                    d2[1] = make_uint2(B.v[4 * i + 2], B.v[4 * i + 3]);
+                }
+            }
+        } else {
+            const int cbk = min(16, nb - 16 * c);
+            const int dpr = cbk * kNL4Bytes / 4;
+#pragma unroll
+            for (int i = 0; i < kDnLoads; ++i) {
                 const int j = lane + 64 * i, row = j / dpr, col = j - row * dpr;
                 if (j < 16 * dpr) st[row * kDnStageDw + col] = B.v[i];
             }
