@@ -18,6 +18,10 @@ up|gate kernel of the bandwidth path), its duration measured with HIP events
 recorded by the library around that kernel on the caller's stream; its
 algorithmic bytes are those of the experts the batch actually routes to.
 
+results.stack_decode_T3 and results.stack_prefill_9536: the two 48-layer
+workloads below, run inside the default line with 5 timed steps each
+(--no-stacks skips them).
+
 cpu_baseline: the CPU oracle (fp64 NumPy, dequantising from the packed bytes)
 on T = 8 decode layers of the same workload, all host cores; results.cpu_oracle
 adds the same sample on one thread and an expert sample of the 8192-token
@@ -103,6 +107,8 @@ def parse():
     p.add_argument("--prefill-only", action="store_true",
                    help="only the 8192-token prefill layer (profiler runs); prints its timings")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-stacks", action="store_true",
+                   help="skip the two 48-layer workloads of the default run")
     p.add_argument("--host-gen", action="store_true",
                    help="build the synthetic layers on the host and copy them (profiler runs)")
     p.add_argument("--stack-prefill", action="store_true",
@@ -339,10 +345,28 @@ def main():
                    "tokens": 8, "layers_rotated": args.layers},
         "roofline": roof, "cpu_baseline": cpu, "results": results,
     }
+    if not args.no_stacks:
+        # the two 48-layer workloads, with fewer steps, inside this line: the
+        # speculative-verify step (T = 3, graph replay) and the mixed-format
+        # 9536-token prefill chunk; the decode layers are freed first
+        import argparse as _ap
+        del layers, wts
+        pre_sample = None
+        torch.cuda.empty_cache()
+        sargs = _ap.Namespace(**vars(args))
+        sargs.steps, sargs.warmup, sargs.spec = 5, 1, 2
+        for key, fn in (("stack_decode_T3", stack_decode), ("stack_prefill_9536", stack_prefill)):
+            sl = fn(sargs, Q, synth, torch, np, dev, emit=False)
+            results[key] = {"metric": sl["metric"], "value": sl["value"], "unit": sl["unit"],
+                            "ms_per_step": sl["ms_per_step"], "steps": sl["steps"],
+                            "workload": sl["config"]["workload"], "roofline": sl["roofline"],
+                            "results": sl["results"]}
+            del sl
+            torch.cuda.empty_cache()
     print(json.dumps(line))
 
 
-def stack_prefill(args, Q, synth, torch, np, dev):
+def stack_prefill(args, Q, synth, torch, np, dev, emit=True):
     """48 mixed-format layers, one 9536-token chunk (see the module header)."""
     wl = synth.WORKLOADS["stack_prefill"]
     T, seed, nl = wl.tokens[0], wl.seed, wl.layers
@@ -449,10 +473,12 @@ def stack_prefill(args, Q, synth, torch, np, dev):
                     "per_format": per_fmt},
     }
     print("# stack prefill: %.2f ms per 48-layer pass, per format %s" % (ms, per_fmt), file=sys.stderr)
-    print(json.dumps(line))
+    if emit:
+        print(json.dumps(line))
+    return line
 
 
-def stack_decode(args, Q, synth, torch, np, dev):
+def stack_decode(args, Q, synth, torch, np, dev, emit=True):
     """48 decode-shaped layers, 1 + spec tokens per step (see the module header)."""
     wl = synth.WORKLOADS["stack"]
     seed, nl = wl.seed, wl.layers
@@ -554,7 +580,9 @@ def stack_decode(args, Q, synth, torch, np, dev):
     }
     print("# stack decode: %.3f ms per 48-layer step (graph replay; eager %.3f ms), U = %.1f, "
           "%.0f GB/s" % (ms, ms_eager, U, step_bytes / (ms * 1e-3) / 1e9), file=sys.stderr)
-    print(json.dumps(line))
+    if emit:
+        print(json.dumps(line))
+    return line
 
 
 def summarize_csv(path):
