@@ -624,14 +624,14 @@ def summarize_csv(path):
             print("| %s | %d | %s | %d | %.6g |" % (k, g, c, len(v), sum(v) / len(v)))
     else:
         # every kernel of a layer forward is tagged with the batch of the layer:
-        # the token count T of the combine kernel that ends it (its grid's
-        # second dimension)
+        # the token count T of the combine kernel that ends it (its grid holds
+        # ceil(H / 1024) blocks of 256 per token)
         rows.sort(key=lambda r: int(r["Start_Timestamp"]))
         tag = [None] * len(rows)
         nxt = None
         for i in range(len(rows) - 1, -1, -1):
             if "k_combine" in rows[i]["Kernel_Name"]:
-                nxt = int(float(rows[i].get("Grid_Size_Y", 0))) or None
+                nxt = grid(rows[i]) // (256 * ((H + 1023) // 1024))
             tag[i] = nxt
         agg = collections.defaultdict(list)
         for r, t in zip(rows, tag):

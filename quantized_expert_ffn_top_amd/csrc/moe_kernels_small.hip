@@ -390,8 +390,11 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_per
                                                        const float* __restrict__ w, int k, int H,
                                                        const float* __restrict__ shared,
                                                        float* __restrict__ y) {
-    const int t = blockIdx.y;
-    const int c = blockIdx.x * blockDim.x + threadIdx.x, h = 4 * c;
+    // block b: token b / ncb, float4 columns 256 (b % ncb) .. +255 (a
+    // one-dimensional grid: any T up to the library's limit)
+    const int ncb = (H / 4 + 255) / 256;
+    const int t = blockIdx.x / ncb;
+    const int c = (blockIdx.x - t * ncb) * blockDim.x + threadIdx.x, h = 4 * c;
     if (h >= H) return;
     const bool h16 = fp16_unless && *fp16_unless == 0;
     auto sum = [&](auto h16c) {
@@ -566,7 +569,7 @@ void launch_build_tiles(const int32_t* offsets, int E, int BM, int32_t* tiles, i
 
 void launch_combine(const float* y_perm, const int* fp16_unless, const int32_t* inv, const float* w,
                     int T, int k, int H, const float* shared, float* y, hipStream_t st) {
-    k_combine<<<dim3(cdiv(H / 4, 256), T), 256, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, y);
+    k_combine<<<(unsigned)(cdiv(H / 4, 256) * T), 256, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, y);
 }
 
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,

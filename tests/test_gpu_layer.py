@@ -349,6 +349,37 @@ def test_gemm_rows_beyond_fp16_take_the_fp32_form(T):
     assert_close(y, ref["y"], "rows beyond fp16 T=%d" % T)
 
 
+def test_real_layer_max_tokens():
+    """The largest batch the library takes (2^18 tokens, 2.6M routed slots) at
+    the real shape: every token's ids are k distinct experts, its weights sum
+    to 1 and its output is finite; sampled tokens (the first, the last, and
+    some in between) against the oracle, routing included."""
+    import sys
+    T, sh, seed = 1 << 18, synth.REAL, 51
+    print("[max tokens] generating", file=sys.__stderr__, flush=True)
+    lay = synth.real_layer(sh, seed, 0, zipf_s=1.0, device=dev())
+    x = synth.tokens_bf16(T, sh.hidden, seed).to(dev())
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    print("[max tokens] layer", file=sys.__stderr__, flush=True)
+    y, ids, w = _run_layer(d, wts, x)
+    print("[max tokens] checks", file=sys.__stderr__, flush=True)
+    assert np.all(np.isfinite(y))
+    assert ids.min() >= 0 and ids.max() < sh.n_experts
+    assert (np.diff(np.sort(ids, axis=1), axis=1) > 0).all()
+    assert np.abs(w.sum(axis=1) - 1.0).max() <= 1e-5
+    sample = np.array([0, 1, 4097, T // 2, T - 65, T - 2, T - 1])
+    xs = bf16_np(x[torch.from_numpy(sample).to(dev())])
+    L = OM.router_logits(xs, bf16_np(lay.router_w), lay.router_b.cpu().numpy().astype(np.float64))
+    assert ids_valid_topk(ids[sample], L, sh.top_k)
+    cache = ExpertCache(sh, lambda e: synth.expert_record(sh, seed, 0, e).numpy())
+    ref = OM.layer_forward(xs, sh.top_k, cache, sh.n_experts, logits=L, shared=real_shared_np(lay),
+                           force_ids=ids[sample])
+    assert np.abs(w[sample] - ref["w"]).max() <= 1e-5
+    assert_close(y[sample], ref["y"], "max tokens T=%d" % T)
+
+
 def test_layer_deterministic():
     sh, recs, x, logits = tiny_inputs(seed=4, T=300)
     d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, 0)
