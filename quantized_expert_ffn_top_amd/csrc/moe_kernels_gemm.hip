@@ -1,10 +1,11 @@
 // Grouped-GEMM path of the layer (prefill-sized batches).  One kernel
-// template, five uses (the routed experts; the router and the shared expert
+// template, seven uses (the routed experts; the router and the shared expert
 // are dense bf16 products, in moe_kernels_dense.hip):
 //   UG_Q3   routed up|gate: A = token rows gathered through the permutation
 //           (fp16), B = Q3S-256 weights, epilogue SwiGLU
-//   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights (the
-//           mixed-format layers)
+//   UG_Q2S  the same with Q2S-256 weights, UG_NL4 with NL4-32 weights, UG_Q3K
+//           with Q3K-256 and UG_NL4S with NL4S-256 weights (the mixed-format
+//           layers and the draft head)
 //   DN_NL4  routed down: A = the expert's rows of a (fp16), B = NL4-32
 //           weights, epilogue fp32 (or range-checked fp16) store (permuted rows)
 //   DN_Q2   the same with Q2-32 weights
@@ -51,7 +52,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int N> struct Cnt { static constexpr int value = N; };
 
-// (the numbers are the kernels' names in traces: k_gemm<0>, <1>, <5>, <6>, <7>)
+// (the numbers are the kernels' names in traces: k_gemm<0>, <1>, <5> .. <9>)
 enum GemmMode { UG_Q3 = 0, DN_NL4 = 1, UG_Q2S = 5, UG_NL4 = 6, DN_Q2 = 7, UG_Q3K = 8, UG_NL4S = 9 };
 // quantized B formats of the routed modes
 enum BFmt { BF_NONE, BF_Q3, BF_Q2S, BF_NL4, BF_Q2, BF_Q3K, BF_NL4S };
