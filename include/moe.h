@@ -200,7 +200,9 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
  * W_up[e] x[t]), unweighted, fp32 [T*k][H].  If shared_y is not NULL and
  * desc->shared_inter > 0 the shared expert's output for every token is
  * written to shared_y fp32 [T][H].  x bf16 [T][H]; offsets/perm as produced by
- * moe_permute (the library also rebuilds its internal tile list from them). */
+ * moe_permute (the library also rebuilds its internal tile list from them).
+ * T <= 16 with Q3S_256 up|gate and NL4_32 down runs the bandwidth kernels
+ * (routing taken from offsets/perm), anything else the grouped GEMMs. */
 moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* wts,
                           const uint16_t* x, int32_t T, const int32_t* offsets,
                           const int32_t* perm, float* y_perm, float* shared_y,
