@@ -322,38 +322,44 @@ __host__ __device__ constexpr int ug_stage_stride(int H) { return (H / 256) * 10
 constexpr int kUgStaticLds = kQ3LutDw * 4 + 4 * (4 * kMaxSlots + 1) + 16;
 // one stage: 32 rows and a 16-byte scratch slot for the loads past the rows
 __host__ __device__ constexpr int ug_stage_bytes(int H) { return 32 * ug_stage_stride(H) + 16; }
-// 12 waves (3 per SIMD) when the H/128 K groups split evenly over them, else 8
+// waves that load, stage and finish the items, besides the decoding waves
+constexpr int kUgLoadWaves = 4;
+// decoding waves (two per SIMD, with one loader wave)
 __host__ __device__ constexpr int ug_waves(int H) {
-    return ((H / 128) % 12 == 0 && (H / 128) / 12 <= 2) ? 12 : 8;
+    (void)H;
+    return 8;
 }
 
-// Persistent: one block of WAVES waves per CU; each block owns a contiguous range
-// of items (active expert a, 16-column slice): the 16 up rows and the 16
-// matching gate rows (32 x H/256 packed blocks).  An item's rows are loaded
-// with coalesced CH-byte loads two items ahead into registers, written to an
-// LDS stage when their turn comes (row stride = row bytes + 8, so that the
-// per-lane reads of 16 rows hit distinct banks), and decoded from there.
-// The waves split K in groups of 128 (4 sub-blocks; wave w takes groups
-// w + WAVES*i); lane group g of a
+// Persistent: one block per CU of WAVES decoding waves and kUgLoadWaves
+// loading waves; each block owns a contiguous range of items (active expert
+// a, 16-column slice): the 16 up rows and the 16 matching gate rows (32 x
+// H/256 packed blocks).  The loading waves fetch an item's rows with
+// coalesced CH-byte loads into registers while the item before it is in the
+// other LDS stage, write them to their stage when their turn comes (row stride = row bytes + 8, so that the
+// per-lane reads of 16 rows hit distinct banks) and run the item's epilogue;
+// the decoding waves only decode.  They split K in groups of 128 (4
+// sub-blocks; wave w takes groups w + WAVES*i); lane group g of a
 // 16x16x32 step takes one whole 32-weight sub-block (12 index bytes), so the
 // B operand of a step spans 4 sub-blocks of one 256-weight block:
 // B = s*c (exact fp16 integers) and the block scale d/128 multiplies the
 // fp32 partial of the group.  The A operand holds every token of the batch
 // (row m = token m, rows >= T zero): each item multiplies all tokens and
-// keeps the routed ones.  Epilogue: partials of the waves summed in wave
-// order through LDS, a = bf16_rne(silu(g) * u), stored as fp16 (exact).
+// keeps the routed ones.  Epilogue (loading waves): partials of the
+// decoding waves summed in wave order through LDS, a = bf16_rne(silu(g) * u),
+// stored as fp16 (exact).
 // After the routed items every block finishes its share of the shared
 // expert: a_sh[t][o] = bf16(silu(sum_c g) * sum_c u) over the stage-1 chunks.
 template <int GPW, bool FULL, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
+__global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
     const uint8_t* __restrict__ experts, int64_t estride, const float* __restrict__ logits, int np,
     const float* __restrict__ lbias, int E, int k, const uint16_t* __restrict__ x16, int T, int H,
     int I, uint16_t* __restrict__ a16_perm,
     const float* __restrict__ shp, int nkc, int Is, uint16_t* __restrict__ a_sh, RouteOut ro) {
-    constexpr int NT = 64 * WAVES;                          // threads
+    constexpr int NT = 64 * (WAVES + kUgLoadWaves);         // threads
+    constexpr int NL = 64 * kUgLoadWaves;                   // loader threads
     constexpr int CH = FULL ? 16 : 8;                       // bytes per staging load
-    // chunks per thread: 32 rows of <= 52 * WAVES * GPW bytes
-    constexpr int NCH = (32 * 52 * WAVES * GPW / CH + NT - 1) / NT;
+    // chunks per loader thread: 32 rows of <= 52 * WAVES * GPW bytes
+    constexpr int NCH = (32 * 52 * WAVES * GPW / CH + NL - 1) / NL;
     __shared__ __attribute__((aligned(8192))) uint32_t lut[kQ3LutDw];  // pair bits OR onto the address
     __shared__ int s_tiles[3 * kMaxSlots], s_perm[kMaxSlots], s_nt;
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
@@ -392,61 +398,80 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int RS = rb + 8;
     const int NG = FULL ? WAVES * GPW : H / 128;
 
-
-    // A operand: every token of the batch
-    u32x4 av[GPW][4];
-    {
+    // One register array serves both roles (a wave runs only one): the A
+    // operand of a decoder (every token of the batch, its K groups), the
+    // item in flight of a loader.
+    constexpr int RA = GPW * 16, RB = NCH * CH / 4;
+    uint32_t R[RA > RB ? RA : RB];
+    // Roles: waves [0, WAVES) decode; the kUgLoadWaves waves after them load
+    // the items, stage them and finish them, so that the decoders never wait
+    // for a load, a stage write or an epilogue.
+    const bool loader = w >= WAVES;
+    const int lt = tid - 64 * WAVES;                        // loader thread (loaders only)
+    if (!loader) {
         const bool vt = r < T;
         const uint16_t* xr = x16 + (int64_t)(vt ? r : 0) * H + 32 * g;
 #pragma unroll
         for (int gi = 0; gi < GPW; ++gi) {
             const int q = w + WAVES * gi;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[gi][i] = ((FULL || q < NG) && vt) ? ld16(xr + q * 128 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 v = ((FULL || q < NG) && vt) ? ld16(xr + q * 128 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) R[16 * gi + 4 * i + c] = v[c];
+            }
         }
     }
+    auto av = [&](int gi, int i) {
+        return u32x4{R[16 * gi + 4 * i], R[16 * gi + 4 * i + 1], R[16 * gi + 4 * i + 2], R[16 * gi + 4 * i + 3]};
+    };
 
-    // staging map of this thread (the same for every item): chunk j covers
-    // CH bytes of row `row` (0..15 up, 16..31 gate) at column `col`
+    // staging map of a loader thread (the same for every item): chunk j covers
+    // CH bytes of row `row` (0..15 up, 16..31 gate) at column `col`, packed
+    // as row << 16 | col (row 32: past the rows, a scratch slot)
     const int cpr = rb / CH;                                // chunks per row
-    int gofs[NCH], lofs[NCH];
+    int rc[NCH];
+    // the larger variants decode rc where it is used (kept decoded out of
+    // the loop, the offsets would not fit the registers)
+    constexpr bool kPinRc = GPW >= 4 || (GPW == 3 && !FULL);
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-        const int c = tid + NT * j;
+        const int c = lt + NL * j;
         const int row = c / cpr, col = (c - row * cpr) * CH;
-        const bool ok = row < 32;
-        gofs[j] = ok ? (row < 16 ? row : I - 16 + row) * rb + col : 0;
-        lofs[j] = ok ? row * RS + col : 32 * RS;           // past the rows: a scratch slot
+        rc[j] = (c >= 0 && row < 32) ? (row << 16 | col) : 32 << 16;
     }
 
-    struct Buf {                                            // one item in flight
-        uint32_t v[NCH][CH / 4];
-    };
-    Buf P0, P1;
-    auto issue = [&](int i, Buf& B) {
+    auto issue = [&](int i) {                               // item i -> R
         const int ic = min(i, max(0, min(i1, n_items) - 1)), at = ic / nsl, sl = ic - at * nsl;
         const int e = __builtin_amdgcn_readfirstlane(s_tiles[3 * at]);
         const uint8_t* base = experts + (int64_t)e * estride + (int64_t)(16 * sl) * rb;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
+            int v = rc[c];
+            if constexpr (kPinRc) __asm__ volatile("" : "+v"(v));
+            const int row = v >> 16, col = v & 0xffff;
+            const int go = row < 32 ? (row < 16 ? row : I - 16 + row) * rb + col : 0;
             if constexpr (CH == 16) {
-                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + gofs[c]));
-                B.v[c][0] = t[0]; B.v[c][1] = t[1]; B.v[c][2] = t[2]; B.v[c][3] = t[3];
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + go));
+                R[4 * c] = t[0]; R[4 * c + 1] = t[1]; R[4 * c + 2] = t[2]; R[4 * c + 3] = t[3];
             } else {
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + gofs[c]));
-                B.v[c][0] = t[0]; B.v[c][1] = t[1];
+                const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + go));
+                R[2 * c] = t[0]; R[2 * c + 1] = t[1];
             }
         }
     };
-    auto put = [&](int sb, const Buf& B) {                  // registers -> stage sb (8-byte stores)
+    auto put = [&](int sb) {                                // R -> stage sb (8-byte stores)
         uint8_t* st = stage + sb * ug_stage_bytes(H);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
+            int v = rc[c];
+            if constexpr (kPinRc) __asm__ volatile("" : "+v"(v));
+            const int lo = (v >> 16) * RS + (v & 0xffff);
 #pragma unroll
             for (int h = 0; h < CH / 8; ++h)
-                *reinterpret_cast<uint2*>(st + lofs[c] + 8 * h) = make_uint2(B.v[c][2 * h], B.v[c][2 * h + 1]);
+                *reinterpret_cast<uint2*>(st + lo + 8 * h) =
+                    make_uint2(R[(CH / 4) * c + 2 * h], R[(CH / 4) * c + 2 * h + 1]);
         }
     };
 
@@ -458,10 +483,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
     const int r_idx = r * RS + (w >> 1) * kQ3Bytes + 12 * (4 * (w & 1) + g);
     const int r_tail = r * RS + (w >> 1) * kQ3Bytes + 96;
 
-    auto decode = [&](int it, int sb) {                     // sb: stage of item it
-        const int at = it / nsl, sl = it - at * nsl;
-        const int row0 = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 1]);
-        const int rows = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 2]);
+    auto decode = [&](int it, int sb) {                     // decoders; sb: stage of item it
         const uint32_t st = lds_addr(stage + sb * ug_stage_bytes(H));
         f32x4 acc_u = {0.f, 0.f, 0.f, 0.f}, acc_g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -479,27 +501,31 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
                 const _Float16 sg = (_Float16)(float)q3_tail_s(tlg, js);
                 const h2 su2 = {su, su}, sg2 = {sg, sg};
                 f32x4 pu = {0.f, 0.f, 0.f, 0.f}, pg = {0.f, 0.f, 0.f, 0.f};
-                // all 32 table reads of the group in flight before any is used
-                uint32_t lu[16], lg[16];
+                // the group's 32 table reads in two halves of 16, each half in
+                // flight before any of it is used
 #define MOE_PAIR(I_, P_)                                                        \
-    lu[4 * I_ + P_] = lds_ld(q3_pair_addr<24 * I_ + 6 * P_>(iu, cbase));        \
-    lg[4 * I_ + P_] = lds_ld(q3_pair_addr<24 * I_ + 6 * P_>(ig, cbase));
+    lu[4 * ((I_) & 1) + P_] = lds_ld(q3_pair_addr<24 * (I_) + 6 * P_>(iu, cbase)); \
+    lg[4 * ((I_) & 1) + P_] = lds_ld(q3_pair_addr<24 * (I_) + 6 * P_>(ig, cbase));
 #define MOE_STEP(I_) MOE_PAIR(I_, 0) MOE_PAIR(I_, 1) MOE_PAIR(I_, 2) MOE_PAIR(I_, 3)
-                MOE_STEP(0) MOE_STEP(1) MOE_STEP(2) MOE_STEP(3)
+#define MOE_HALF(H_)                                                            \
+    {                                                                           \
+        uint32_t lu[8], lg[8];                                                  \
+        MOE_STEP(2 * H_) MOE_STEP(2 * H_ + 1)                                   \
+        __builtin_amdgcn_sched_barrier(0);                                      \
+        u32x4 bu[2], bg[2];                                                     \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                         \
+            bu[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lu[i]) * su2); \
+            bg[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lg[i]) * sg2); \
+        }                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                         \
+            pu = mfma16_f16(av(gi, 2 * H_ + i), bu[i], pu);                     \
+            pg = mfma16_f16(av(gi, 2 * H_ + i), bg[i], pg);                     \
+        }                                                                       \
+    }
+                MOE_HALF(0) MOE_HALF(1)
+#undef MOE_HALF
 #undef MOE_STEP
 #undef MOE_PAIR
-                __builtin_amdgcn_sched_barrier(0);
-                u32x4 bu[4], bg[4];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    bu[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lu[i]) * su2);
-                    bg[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lg[i]) * sg2);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pu = mfma16_f16(av[gi][i], bu[i], pu);
-                    pg = mfma16_f16(av[gi][i], bg[i], pg);
-                }
                 const float du = q3_tail_d(tlu) * 0.0078125f;
                 const float dg = q3_tail_d(tlg) * 0.0078125f;
 #pragma unroll
@@ -512,69 +538,70 @@ __global__ void __launch_bounds__(64 * WAVES, 1) k_upgate_dec(
         const int buf = it & 1;
         red[buf][w][0][lane] = acc_u;
         red[buf][w][1][lane] = acc_g;
-        __syncthreads();
-        // finish: waves 0-3, thread (slot j, column n); D row m = token tj sits at
-        // lane (m/4)*16 + n, element m%4.  Every thread issues the store (equal
-        // memory-op counts on all paths); those without an output store out of
-        // range, which the buffer unit drops.
-        const int j = tid >> 4, n = tid & 15;
-        uint16_t av16 = 0;
-        if (w < 4) {
-            const int slot = s_perm[row0 + (j < rows ? j : 0)];
-            const int tj = (int)(((uint32_t)slot * kmag) >> 16);
-            const float* ru =
-                reinterpret_cast<const float*>(&red[buf][0][0][(tj >> 2) * 16 + n]) + (tj & 3);
-            float u = 0.f, gg = 0.f;
+    };
+
+    // loaders: thread (slot j, column n) of item it; D row m = token tj sits
+    // at lane (m/4)*16 + n, element m%4 of each decoder's partials, summed in
+    // decoder order.  Every loader thread issues the store (equal memory-op
+    // counts on all paths); those without an output store out of range, which
+    // the buffer unit drops.
+    auto finish = [&](int it) {
+        const int at = it / nsl, sl = it - at * nsl;
+        const int row0 = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 1]);
+        const int rows = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 2]);
+        const int buf = it & 1;
+        const int j = lt >> 4, n = lt & 15;
+        const int slot = s_perm[row0 + (j < rows ? j : 0)];
+        const int tj = (int)(((uint32_t)slot * kmag) >> 16);
+        const float* ru = reinterpret_cast<const float*>(&red[buf][0][0][(tj >> 2) * 16 + n]) + (tj & 3);
+        float u = 0.f, gg = 0.f;
 #pragma unroll
-            for (int v = 0; v < WAVES; ++v) {
-                u += ru[v * 2 * 64 * 4];
-                gg += ru[v * 2 * 64 * 4 + 64 * 4];
-            }
-            av16 = (uint16_t)f32_to_f16_bits(bf16_to_f32(f32_to_bf16(silu_mul_fast(gg, u))));
+        for (int v = 0; v < WAVES; ++v) {
+            u += ru[v * 2 * 64 * 4];
+            gg += ru[v * 2 * 64 * 4 + 64 * 4];
         }
-        const bool ok = w < 4 && j < rows;
-        const uint32_t off = ok ? (uint32_t)(((row0 + j) * I + 16 * sl + n) * 2) : 0x80000000u;
+        const uint16_t av16 = (uint16_t)f32_to_f16_bits(bf16_to_f32(f32_to_bf16(silu_mul_fast(gg, u))));
+        const uint32_t off = j < rows ? (uint32_t)(((row0 + j) * I + 16 * sl + n) * 2) : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b16(av16, a_out, off, 0, 0);
     };
 
-    // pipeline, one barrier per item: step i writes item i + 1 from its
-    // registers to stage (i + 1 - i0) % 2, loads item i + 3 into those
-    // registers, decodes item i from stage (i - i0) % 2 and writes its partial
-    // sums; after the
-    // barrier waves 0-3 finish item i while the others go on.  Items i + 2
-    // and i + 3 are in flight during the decode of item i; the last steps
-    // load nothing past the block's items (a block without items loads item
-    // min(i0, n_items - 1) in the prologue).
-    issue(i0, P0);
-    issue(i0 + 1, P1);
-    put(0, P0);
-    issue(i0 + 2, P0);
+    // Pipeline, one barrier per item.  Step it: the decoders decode item it
+    // from stage (it - i0) % 2 into red[it % 2]; the loaders write item it + 1
+    // from their registers to stage (it + 1 - i0) % 2, load item it + 2 into
+    // those registers and finish item it - 1 from red[(it - 1) % 2].  Item
+    // it + 2 is in flight during the decode of item it; loads stop at the
+    // block's last item (a block without items loads item min(i0, n_items - 1)
+    // in the prologue).
+    if (loader) {
+        issue(i0);
+        put(0);
+        issue(i0 + 1);
+    }
     __syncthreads();                                        // stage 0 written
-    auto step = [&](int it, Buf& B) {                       // B holds item it + 1
-        put((it + 1 - i0) & 1, B);
+    auto lstep = [&](int it, bool more) {                   // R holds item it + 1
+        put((it + 1 - i0) & 1);
         __builtin_amdgcn_sched_barrier(0);
-        issue(it + 3, B);
+        if (more) issue(it + 2);
         __builtin_amdgcn_sched_barrier(0);
-        decode(it, (it - i0) & 1);
-    };
-    auto step_last = [&](int it, Buf& B) {                  // no item it + 3 to load
-        put((it + 1 - i0) & 1, B);
-        __builtin_amdgcn_sched_barrier(0);
-        decode(it, (it - i0) & 1);
+        if (it > i0) finish(it - 1);
     };
     int it = i0;
-    for (; it + 4 < i1; it += 2) {
-        step(it, P1);
-        step(it + 1, P0);
+    for (; it + 2 < i1; ++it) {
+        if (loader) lstep(it, true);
+        else decode(it, (it - i0) & 1);
+        __syncthreads();
     }
-    // the last (up to four) items: loads only for items that exist
-#define MOE_LAST(J, B)                                                          \
-    if (it + J < i1) {                                                          \
-        if (it + J + 3 < i1) step(it + J, B);                                   \
-        else step_last(it + J, B);                                              \
+    // the last (up to two) items: loads only for items that exist
+    for (; it < i1; ++it) {
+        if (loader) {
+            if (it + 1 < i1) lstep(it, false);
+            else if (it > i0) finish(it - 1);
+        } else {
+            decode(it, (it - i0) & 1);
+        }
+        __syncthreads();
     }
-    MOE_LAST(0, P1) MOE_LAST(1, P0) MOE_LAST(2, P1) MOE_LAST(3, P0)
-#undef MOE_LAST
+    if (loader && i1 > i0) finish(i1 - 1);
 
     if (shp) {                                              // shared expert: sum partials, SwiGLU
         for (int i = blockIdx.x * NT + tid; i < T * Is; i += G * NT) {
@@ -975,7 +1002,7 @@ static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, 
                          int I, uint16_t* a16_perm, const float* shp, int nkc, int Is,
                          uint16_t* a_sh, const RouteOut& ro) {
     const size_t dyn = std::max((size_t)ug_red_bytes(WAVES) + 2 * (size_t)ug_stage_bytes(H),
-                                (size_t)route_scratch_bytes(T, E, WAVES));
+                                (size_t)route_scratch_bytes(T, E, WAVES + kUgLoadWaves));
     static bool attr = false;                      // opt in to more than 64 KB of LDS once
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)&k_upgate_dec<GPW, FULL, WAVES>,
@@ -983,7 +1010,7 @@ static void upgate_dec_t(unsigned grid, hipStream_t st, const uint8_t* experts, 
                             160 * 1024 - kUgStaticLds);
         attr = true;
     }
-    k_upgate_dec<GPW, FULL, WAVES><<<grid, 64 * WAVES, dyn, st>>>(
+    k_upgate_dec<GPW, FULL, WAVES><<<grid, 64 * (WAVES + kUgLoadWaves), dyn, st>>>(
         experts, estride, logits, np, lbias, E, k, x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro);
 }
 
@@ -994,7 +1021,8 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* log
     const int max_items = max_tiles * (I / 16);
     const unsigned grid = (unsigned)std::max(1, std::min(n_cu, max_items));
     const int nkc = H / kShKChunk;
-    // 12 waves (3 per SIMD) when the K groups split evenly over them, else 8
+    // 8 decoding waves; K groups per wave: GPW (the last waves' share short
+    // when H / 128 is not a multiple of 8)
     const int NG = H / 128;
     const int waves = ug_waves(H);
     const int gpw = (NG + waves - 1) / waves;
@@ -1002,11 +1030,6 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* log
     shp = (Is > 0) ? shp : nullptr;
 #define MOE_UGT(G, F, W) upgate_dec_t<G, F, W>(grid, st, experts, estride, logits, np, lbias, E, k, \
                                                x16, T, H, I, a16_perm, shp, nkc, Is, a_sh, ro)
-    if (waves == 12) {
-        if (gpw == 1) MOE_UGT(1, true, 12);
-        else MOE_UGT(2, true, 12);
-        return;
-    }
     switch (gpw) {
 #define MOE_UG(G)                          \
     case G:                                \
@@ -1022,7 +1045,7 @@ void launch_upgate_dec(const uint8_t* experts, int64_t estride, const float* log
 
 bool upgate_dec_supported(int H, int T, int E) {
     const int dyn = std::max(ug_red_bytes(ug_waves(H)) + 2 * ug_stage_bytes(H),
-                             route_scratch_bytes(T, E, ug_waves(H)));
+                             route_scratch_bytes(T, E, ug_waves(H) + kUgLoadWaves));
     return H / 128 <= 8 * 4 && kUgStaticLds + dyn <= 160 * 1024;
 }
 

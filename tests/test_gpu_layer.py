@@ -236,6 +236,31 @@ def test_limit_shape_layer(T, sh):
     _real_case(T, seed=8, sh=sh)
 
 
+# Hidden sizes of the bandwidth path's other up|gate kernel variants: the
+# eight decoding waves take H/128 K groups of 128, so H = 2304 gives 3 groups
+# per wave with the last waves' share short, H = 3584 four with a short share,
+# H = 4096 four each (the largest hidden size whose two staged items fit LDS).
+@pytest.mark.parametrize("H", [2304, 3584, 4096])
+@pytest.mark.parametrize("T", [1, 7, 16])
+def test_bandwidth_path_hidden_sizes(T, H):
+    sh = synth.Shape(hidden=H, inter=64, n_experts=16, top_k=2, shared_inter=64)
+    _real_case(T, seed=13, sh=sh)
+    # the bandwidth path ran: stage 1, up|gate, down, combine (4 kernels, 5 marks)
+    lay = synth.real_layer(sh, 13, 0, device=dev())
+    d = Q.desc(sh.hidden, sh.inter, sh.n_experts, sh.top_k, sh.shared_inter)
+    wts = Q.weights(lay.experts, sh.expert_bytes, lay.router_w, lay.router_b, lay.shared_ug,
+                    lay.shared_down)
+    x = synth.tokens_bf16(T, sh.hidden, 13).to(dev())
+    y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev())
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
+    for ev in evs:
+        ev.record()
+    torch.cuda.synchronize()
+    n = Q.moe_layer_forward_timed(d, wts, x, y, Q.workspace(d, T, dev()), [ev.cuda_event for ev in evs])
+    torch.cuda.synchronize()
+    assert n == 5
+
+
 @pytest.mark.parametrize("T", [17, 64])
 def test_real_small_gemm_layer(T):
     _real_case(T, seed=7)
