@@ -425,7 +425,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         // partial planes, summed with the bias by the routing
         launch_upgate_dec(ex, wts->expert_stride, logits_or_null ? logits_or_null : lg,
                           logits_or_null ? 1 : kDecLogitParts,
-                          logits_or_null ? nullptr : wts->router_b, E, k,
+                          (logits_or_null || kDecLogitParts == 1) ? nullptr : wts->router_b, E, k,
                           L.max_tiles, x16, T, H, I, a16, has_sh ? shp : nullptr, Is, ash, ro,
                           n_cu, st);
         mk->mark();

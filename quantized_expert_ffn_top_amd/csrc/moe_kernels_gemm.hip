@@ -141,6 +141,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr bool kNat = MODE == UG_NL4 || kSub;              // natural K order
     constexpr bool kNLTab = kNL || kNLS;                       // the NL4 table (8 copies)
     constexpr bool kSwi = MODE == UG_Q3 || MODE == UG_Q2S || MODE == UG_NL4 || kSub;
+    // the down modes compute the transposed tile (weights as the MFMA's first
+    // operand): a lane then holds 4 consecutive output columns per register
+    // group, stored with one vector store
+    constexpr bool kTr = !kSwi;
     static_assert(kBF != BF_NONE, "a routed mode");
     if (g.only_if && *g.only_if == 0) return;
     constexpr int TBM = BM;
@@ -481,6 +485,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 #pragma unroll
             for (int sn = 0; sn < 2; ++sn) {
                 if constexpr (kB256) tmp[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], tmp[sm][sn]);
+                else if constexpr (kTr) acc[sm][sn] = mfma32_f16(fb[sn][kk], fa[sm], acc[sm][sn]);
                 else acc[sm][sn] = mfma32_f16(fa[sm], fb[sn][kk], acc[sm][sn]);
             }
     };
@@ -534,8 +539,43 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         int r0 = row0;
         __asm__ volatile("" : "+s"(r0));
         float amax = 0.f;                            // fp16 form: largest |value| stored by the lane
+        if constexpr (kTr) {
+            // transposed: lane l, register r of group (sm, sn) holds token row
+            // 32 sm + l % 32 and output column 64 w + 32 sn + 8 (r / 4) +
+            // 4 (l / 32) + r % 4 of the tile (N is a multiple of 32, so a
+            // half is in range or not as a whole)
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) {
+            for (int sm = 0; sm < SM; ++sm) {
+                const int m = 32 * sm + l32;
+                if (m >= rows) continue;
+#pragma unroll
+                for (int sn = 0; sn < 2; ++sn) {
+                    const int c0 = nt * BN + 64 * w + 32 * sn;
+                    if (c0 >= g.N) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            v[i] = acc[sm][sn][4 * j + i];
+                            if constexpr (kNL) v[i] *= 0.0625f;    // the fold's factor 16
+                        }
+                        const int64_t o = (int64_t)(r0 + m) * g.ldo + c0 + 8 * j + 4 * hh;
+                        if (g.y16) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[i]));
+                            *reinterpret_cast<uint2*>(g.y16 + o) =
+                                make_uint2(pack2(f32_to_f16_bits(v[0]), f32_to_f16_bits(v[1])),
+                                           pack2(f32_to_f16_bits(v[2]), f32_to_f16_bits(v[3])));
+                        } else {
+                            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v[0], v[1], v[2], v[3]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int sm = 0; sm < (kTr ? 0 : SM); ++sm) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = 32 * sm + 8 * (r >> 2) + 4 * hh + (r & 3);
