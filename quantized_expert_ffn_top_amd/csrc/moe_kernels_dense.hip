@@ -53,6 +53,7 @@ __device__ __forceinline__ float silu_mul_exact(float g, float u) { return g / (
 
 }  // namespace
 
+template <bool VEC>   // VEC: N0 a multiple of 4, C0 and bias 16-byte aligned
 __global__ void __launch_bounds__(256, 2) k_dense(DenseArgs g) {
     __shared__ u32x4 As[2][DBM * kDChunks];           // 2 x 8 KB
     __shared__ u32x4 Bs[2][DBN * kDChunks];           // 2 x 16 KB
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(256, 2) k_dense(DenseArgs g) {
 #pragma unroll
             for (int sm = 0; sm < 2; ++sm)
 #pragma unroll
-                for (int sn = 0; sn < 4; ++sn) acc[sm][sn] = mfma32_bf16(fa[sm], fb[sn], acc[sm][sn]);
+                for (int sn = 0; sn < 4; ++sn) acc[sm][sn] = mfma32_bf16(fb[sn], fa[sm], acc[sm][sn]);
         }
         if (kt + 1 < nk) {
             put(st ^ 1, R);                            // stage st ^ 1 was last read in step kt - 1
@@ -150,31 +151,52 @@ __global__ void __launch_bounds__(256, 2) k_dense(DenseArgs g) {
         __syncthreads();
     }
 
-    // ---- epilogue.  Lane l, register r of accumulator (sm, sn): row
-    // 32 sm + 8 (r / 4) + 4 (l / 32) + r % 4 of the wave's rows, column l % 32
-    // of its sn-th group of 32.
+    // ---- epilogue.  The tiles are computed transposed (B fragment first):
+    // lane l, register r of accumulator (sm, sn) holds row 32 sm + l % 32 of
+    // the wave's A rows and column 8 (r / 4) + 4 (l / 32) + r % 4 of its sn-th
+    // group of 32, so each register group r / 4 is four consecutive columns,
+    // stored at once (one by one when the row length N0 is not a multiple of
+    // 4; Is is a multiple of 64).
 #pragma unroll
     for (int sm = 0; sm < 2; ++sm) {
+        const int m = m0 + 64 * wm + 32 * sm + l32;
+        if (m >= g.M) continue;
+        if (!swi) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = m0 + 64 * wm + 32 * sm + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (m >= g.M) continue;
-            if (!swi) {
+            for (int sn = 0; sn < 4; ++sn) {
 #pragma unroll
-                for (int sn = 0; sn < 4; ++sn) {
-                    const int n = nt * DBN + 128 * wn + 32 * sn + l32;
-                    if (n < g.N0) {
-                        const float b = g.bias ? g.bias[n] : 0.f;
-                        g.C0[(int64_t)m * g.N0 + n] = acc[sm][sn][r] + b;
+                for (int j = 0; j < 4; ++j) {
+                    const int n = nt * DBN + 128 * wn + 32 * sn + 8 * j + 4 * hh;
+                    float* out = g.C0 + (int64_t)m * g.N0 + n;
+                    if constexpr (VEC) {
+                        if (n >= g.N0) continue;
+                        float4 v = make_float4(acc[sm][sn][4 * j], acc[sm][sn][4 * j + 1],
+                                               acc[sm][sn][4 * j + 2], acc[sm][sn][4 * j + 3]);
+                        if (g.bias) {
+                            const float4 b = *reinterpret_cast<const float4*>(g.bias + n);
+                            v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+                        }
+                        *reinterpret_cast<float4*>(out) = v;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (n + i < g.N0) out[i] = acc[sm][sn][4 * j + i] + (g.bias ? g.bias[n + i] : 0.f);
                     }
                 }
-            } else {
+            }
+        } else {
 #pragma unroll
-                for (int sn = 0; sn < 2; ++sn) {
-                    const int o = (nt - g.nt0) * (DBN / 2) + 64 * wn + 32 * sn + l32;
-                    if (o < g.Is)
-                        g.A1[(int64_t)m * g.Is + o] =
-                            (uint16_t)f32_to_bf16(silu_mul_exact(acc[sm][sn + 2][r], acc[sm][sn][r]));
+            for (int sn = 0; sn < 2; ++sn) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int o = (nt - g.nt0) * (DBN / 2) + 64 * wn + 32 * sn + 8 * j + 4 * hh;
+                    if (o >= g.Is) continue;
+                    uint32_t h[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        h[i] = f32_to_bf16(silu_mul_exact(acc[sm][sn + 2][4 * j + i], acc[sm][sn][4 * j + i]));
+                    *reinterpret_cast<uint2*>(g.A1 + (int64_t)m * g.Is + o) =
+                        make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
                 }
             }
         }
@@ -190,7 +212,9 @@ void launch_dense(const DenseArgs& in, hipStream_t st) {
     const int mtiles = (a.M + DBM - 1) / DBM;
     a.mpx = (mtiles + 7) / 8;
     const unsigned grid = (unsigned)(8 * a.mpx * (a.nt0 + a.nt1));
-    k_dense<<<grid, 256, 0, st>>>(a);
+    const bool vec = (a.N0 & 3) == 0 && ((uintptr_t)a.C0 & 15) == 0 && ((uintptr_t)a.bias & 15) == 0;
+    if (vec) k_dense<true><<<grid, 256, 0, st>>>(a);
+    else k_dense<false><<<grid, 256, 0, st>>>(a);
 }
 
 }  // namespace
