@@ -31,14 +31,16 @@ prefill layer.
 JSON line: one 9536-token chunk through 48 layers whose routed experts use the
 model card's per-layer formats (up|gate Q3S-256 / Q2S-256 / NL4-32, down
 NL4-32 / Q2-32; seeded order), Zipf(0.8) routing, RMSNorm + residual between
-layers, all 48 layers resident in HBM (about 51 GB).  A step is one pass
+layers (fused into each layer's last kernel by moe_layer_forward_residual), all
+48 layers resident in HBM (about 51 GB).  A step is one pass
 through the 48 layers; the roofline object is for the routed up|gate GEMMs
 (MFMA-bound), their time summed over the layers of a pass.
 
 --stack-decode runs the speculative-verify step instead (its own JSON line):
 1 + K tokens (K drafts, --spec K, default 2) through 48 decode-shaped
 Q3S-256 / NL4-32 layers, each independently seeded with a fresh Zipf(1.0)
-bias, RMSNorm + residual between layers, all 53 GB of experts resident.  A
+bias, RMSNorm + residual between layers (fused as above), all 53 GB of
+experts resident.  A
 step is one 48-layer pass, captured once in a HIP graph and replayed (each
 replay checked bit for bit against the eager pass, whose time is reported
 beside it).
@@ -392,21 +394,28 @@ def stack_prefill(args, Q, synth, torch, np, dev, emit=True):
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    normed2 = torch.empty_like(normed)
+
     def one_pass(timed_events=None):
-        # h += MoE_l(norm_l(h)); the residual add of layer l and the norm of
-        # layer l + 1 are one call
+        # h += MoE_l(norm_l(h)): the layer call adds its output to h and writes
+        # the next layer's normalised input (two buffers in turn); the pass
+        # with per-kernel events runs the unfused pair of calls instead
         h.copy_(x0)
         marks = []
         Q.moe_rmsnorm_residual(h, None, gammas[0], 1e-6, normed)
+        nin, nout = normed, normed2
         for l in range(nl):
+            last = l + 1 == nl
             if timed_events is None:
-                Q.moe_layer_forward(descs[l], wts[l], normed, y, ws)
+                Q.moe_layer_forward_residual(descs[l], wts[l], nin, h, ws,
+                                             gamma=None if last else gammas[l + 1], eps=1e-6,
+                                             normed=None if last else nout)
+                nin, nout = nout, nin
             else:
                 marks.append(Q.moe_layer_forward_timed(descs[l], wts[l], normed, y, ws,
                                                        [ev.cuda_event for ev in timed_events[l]]))
-            last = l + 1 == nl
-            Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
-                                   None if last else normed)
+                Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
+                                       None if last else normed)
         return marks
 
     for _ in range(max(1, args.warmup // 8)):
@@ -504,19 +513,23 @@ def stack_decode(args, Q, synth, torch, np, dev, emit=True):
     ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    normed2 = torch.empty_like(normed)
+
     def one_pass(count=False):
+        # h += MoE_l(norm_l(h)): the layer call adds its output to h and writes
+        # the next layer's normalised input (two buffers in turn)
         h.copy_(x0)
         us = []
         Q.moe_rmsnorm_residual(h, None, gammas[0], 1e-6, normed)
+        nin, nout = normed, normed2
         for l in range(nl):
-            if count:
-                Q.moe_layer_forward(d, wts[l], normed, y, ws, topk_ids_out=ids)
-                us.append(int(torch.unique(ids).numel()))
-            else:
-                Q.moe_layer_forward(d, wts[l], normed, y, ws)
             last = l + 1 == nl
-            Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
-                                   None if last else normed)
+            Q.moe_layer_forward_residual(d, wts[l], nin, h, ws, gamma=None if last else gammas[l + 1],
+                                         eps=1e-6, normed=None if last else nout,
+                                         topk_ids_out=ids if count else None)
+            if count:
+                us.append(int(torch.unique(ids).numel()))
+            nin, nout = nout, nin
         return us
 
     us = one_pass(count=True)
@@ -537,7 +550,8 @@ def stack_decode(args, Q, synth, torch, np, dev, emit=True):
         return e0.elapsed_time(e1) / steps
 
     ms_eager = timed(one_pass)
-    # the whole step (48 layers: 5 launches each, plus the norms) captured once
+    # the whole step (48 layers of 4 launches each, the last one carrying the
+    # residual add and the next norm, plus the first norm) captured once
     # in a HIP graph and replayed; every replay is checked against the eager
     # pass (the kernels are deterministic)
     graph = torch.cuda.CUDAGraph()

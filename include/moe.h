@@ -160,7 +160,7 @@ typedef struct {
  * any T <= T_max.  Host-only, pure; returns 0 for an invalid desc/T_max. */
 size_t moe_workspace_size(const moe_layer_desc* desc, int32_t T_max);
 
-/* Router logits (A1): logits[t][e] = sum_h x[t][h] * W_r[e][h] + b[e], fp32
+/* Router logits: logits[t][e] = sum_h x[t][h] * W_r[e][h] + b[e], fp32
  * accumulation.  x bf16 [T][H], w_r bf16 [E][H], b fp32 [E] or NULL, logits
  * fp32 [T][E].  Same kernels moe_layer_forward runs.  ws / ws_bytes are
  * not used (may be NULL / 0).
@@ -170,7 +170,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
                              const uint16_t* w_r, const float* b, float* logits,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Top-k routing (A2).  logits fp32 [T][E] -> topk_ids int32 [T][k] (by
+/* Top-k routing.  logits fp32 [T][E] -> topk_ids int32 [T][k] (by
  * descending logit, ties to the lower index) and topk_w fp32 [T][k] = softmax
  * of the selected logits.  No capacity limit, nothing dropped ("Betelgeuse":
  * every one of the routed experts is computed).  1 <= k <= min(E, 32),
@@ -178,7 +178,7 @@ moe_status moe_router_logits(const uint16_t* x, int32_t T, int32_t H, int32_t E,
 moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                      int32_t* topk_ids, float* topk_w, void* stream);
 
-/* Counting-sort permutation (A3).  Each token's slots go to k experts ("Avalon"
+/* Counting-sort permutation.  Each token's slots go to k experts ("Avalon"
  * README, opening paragraphs: 10 of 512 per token) and every selected expert
  * is computed ("Betelgeuse" post: none is dropped); grouping a batch's slots
  * by expert lets each expert's weights be read once per batch.
@@ -191,7 +191,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs (A4-A7).  Model card, "Files / Main model": each routed expert
+/* Expert FFNs.  Model card, "Files / Main model": each routed expert
  * is an up, a gate and a down matrix (packed up | gate | down) in the
  * quantized types above; the shared expert sits in the dense bf16 part.  The
  * up/gate pair is read as a SwiGLU unit, and a is rounded to bf16, the
@@ -208,7 +208,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* desc, const moe_layer_weights* w
                           const int32_t* perm, float* y_perm, float* shared_y,
                           void* ws, size_t ws_bytes, void* stream);
 
-/* Weighted combine (A8): the layer output is the router-weighted sum of the
+/* Weighted combine: the layer output is the router-weighted sum of the
  * token's k routed experts plus the shared expert ("Avalon" README, opening
  * paragraphs; model card, "Files / Main model").
  * y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k+j]] (+ shared_y[t] if
@@ -217,7 +217,7 @@ moe_status moe_combine(const float* y_perm, const int32_t* inv_perm, const float
                        int32_t T, int32_t k, int32_t H, const float* shared_y,
                        float* y, void* stream);
 
-/* The whole layer (A1-A8), as the formula at the top of this file (its
+/* The whole layer, as the formula at the top of this file (its
  * sources there): y fp32 [T][H] from x bf16 [T][H].  If
  * logits_or_null is given (fp32 [T][E]) the router is skipped.  Optional
  * outputs: topk_ids_out int32 [T][k], topk_w_out fp32 [T][k].  Tokens T <= 16
@@ -228,6 +228,24 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
                              const uint16_t* x, int32_t T, const float* logits_or_null,
                              float* y, int32_t* topk_ids_out, float* topk_w_out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* The layer with the residual add and the next layer's RMSNorm of a pre-norm
+ * stack fused into its combine: h[t] += y[t] for the layer output y of
+ * moe_layer_forward (which is not written), then, if gamma and
+ * normed_bf16_out are not NULL, normed[t] = bf16_rne(gamma * h[t] /
+ * sqrt(mean(h[t]^2) + eps)).  The stack is the model card's 48 layers
+ * ("Qwen3.8-Flash-Next - Avalon GGUF", "Files / Main model"); the pages do
+ * not spell out where the norm sits, and each layer reading the normalised
+ * residual stream and adding its output back is the plain reading.  h fp32 [T][H]
+ * (updated in place, 16-byte aligned), gamma fp32 [H] (16-byte aligned),
+ * normed bf16 [T][H] (8-byte aligned); the other arguments as in
+ * moe_layer_forward.  The results are the same bits as moe_layer_forward
+ * followed by moe_rmsnorm_residual(h, y, gamma, eps, ...). */
+moe_status moe_layer_forward_residual(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                      const uint16_t* x, int32_t T, const float* logits_or_null,
+                                      float* h, const float* gamma, float eps,
+                                      uint16_t* normed_bf16_out, int32_t* topk_ids_out,
+                                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Instrumented moe_layer_forward, for measurement: identical work, and in
  * addition events[0] (hipEvent_t, created by the caller) is recorded on
@@ -272,7 +290,7 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
                           void* stream);
 
-/* Helper for stacked layers (A9, pre-norm residual): if delta is not NULL,
+/* Helper for stacked layers (pre-norm residual): if delta is not NULL,
  * h += delta; then, if gamma and normed_bf16_out are not NULL,
  * normed[t] = bf16_rne(gamma * h[t] / sqrt(mean(h[t]^2) + eps)).  h fp32 [T][H]
  * (updated in place), delta fp32 [T][H], gamma fp32 [H], normed bf16 [T][H]. */

@@ -7,7 +7,8 @@ this package is its Python binding (ctypes) plus the build script.
 from ._lib import (EXPORTS, LIB_PATH, MOE_FMT_BF16, MOE_FMT_NL4_32, MOE_FMT_NL4S256, MOE_FMT_Q2_32,
                    MOE_FMT_Q2S256, MOE_FMT_Q3K256, MOE_FMT_Q3S256, LayerDesc,
                    LayerWeights, MoeError, desc, load, moe_combine, moe_dequantize,
-                   moe_expert_ffn, moe_layer_forward, moe_layer_forward_noalloc, moe_layer_forward_timed,
+                   moe_expert_ffn, moe_layer_forward, moe_layer_forward_noalloc, moe_layer_forward_residual,
+                   moe_layer_forward_timed,
                    moe_permute, moe_rmsnorm_residual,
                    moe_route, moe_router_logits, moe_workspace_size, weights, workspace)
 
@@ -15,6 +16,7 @@ __all__ = ["EXPORTS", "LIB_PATH", "MOE_FMT_BF16", "MOE_FMT_NL4_32", "MOE_FMT_Q2_
            "MOE_FMT_Q2S256", "MOE_FMT_Q3S256", "MOE_FMT_Q3K256", "MOE_FMT_NL4S256",
            "LayerDesc", "LayerWeights", "MoeError", "desc", "load", "moe_combine",
            "moe_dequantize", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_noalloc",
+           "moe_layer_forward_residual",
            "moe_layer_forward_timed",
            "moe_permute",
            "moe_rmsnorm_residual", "moe_route", "moe_router_logits", "moe_workspace_size",

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_timed",
+           "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_residual",
+           "moe_layer_forward_timed",
            "moe_layer_forward_noalloc", "moe_dequantize", "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
 
 
@@ -73,6 +74,8 @@ def load():
         "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P, P]),
         "moe_layer_forward": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P,
                                     I32, P, P, P, P, P, SZ, P]),
+        "moe_layer_forward_residual": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                             P, I32, P, P, P, F, P, P, P, P, SZ, P]),
         "moe_layer_forward_timed": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                           P, I32, P, P, P, P, P, SZ, P, P, I32,
                                           ctypes.POINTER(I32)]),
@@ -179,6 +182,17 @@ def moe_layer_forward(d, w, x, y, ws, logits=None, topk_ids_out=None, topk_w_out
                                     _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(x)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_residual(d, w, x, h, ws, gamma=None, eps=1e-6, normed=None, logits=None,
+                               topk_ids_out=None, topk_w_out=None):
+    """h += layer(x) in place; normed = bf16(gamma * h / rms(h)) when gamma is given."""
+    T = x.shape[0]
+    _check(load().moe_layer_forward_residual(ctypes.byref(d), ctypes.byref(w), _ptr(x), T,
+                                             _ptr(logits), _ptr(h), _ptr(gamma), eps, _ptr(normed),
+                                             _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(x)),
+           "moe_layer_forward_residual")
 
 
 def moe_layer_forward_timed(d, w, x, y, ws, events, logits=None, topk_ids_out=None,

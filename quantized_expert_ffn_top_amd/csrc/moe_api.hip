@@ -367,19 +367,27 @@ struct Marks {
     }
 };
 
+// The residual add and the next RMSNorm fused into the layer's combine.
+struct Fuse {
+    float* h;
+    const float* gamma;
+    float eps;
+    uint16_t* normed;
+};
+
 moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weights* wts,
                               const uint16_t* x, int32_t T, const float* logits_or_null, float* y,
                               int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                              size_t ws_bytes, void* stream, Marks* mk) {
+                              size_t ws_bytes, void* stream, Marks* mk, const Fuse* fz = nullptr) {
     g_last_error.clear();
     moe_status s = check_desc(desc);
     if (s != MOE_OK) return s;
     const bool has_sh = desc->shared_inter > 0;
     s = check_weights(desc, wts, logits_or_null == nullptr, has_sh);
     if (s != MOE_OK) return s;
-    if (!x || !y) return fail(MOE_ERR_NULL, "x and y must be non-NULL");
+    if (!x || (!y && !fz)) return fail(MOE_ERR_NULL, "x and y must be non-NULL");
     if (T < 1 || T > kMaxT) return fail(MOE_ERR_SHAPE, "need 1 <= T <= 2^18");
-    if (!al16(x) || !al16(y) || (logits_or_null && !al4(logits_or_null)) ||
+    if (!al16(x) || (y && !al16(y)) || (logits_or_null && !al4(logits_or_null)) ||
         (topk_ids_out && !al4(topk_ids_out)) || (topk_w_out && !al4(topk_w_out)))
         return fail(MOE_ERR_ALIGN, "x and y must be 16-byte aligned");
     const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k,
@@ -467,11 +475,19 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
         launch_gemm_down(ex, wts->expert_stride, tiles, nt, L.max_tiles, a16, H, I,
                          upgate_bytes(desc), desc->down_fmt, yp, nullptr, nullptr, range_flag, st);
         mk->mark();
-        launch_combine(yp, range_flag, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+        if (fz)
+            launch_combine_norm(yp, range_flag, inv, wv, T, k, H, has_sh ? ysh : nullptr, fz->h,
+                                fz->gamma, fz->eps, fz->normed, st);
+        else
+            launch_combine(yp, range_flag, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
         mk->mark();
         return launched("moe_layer_forward");
     }
-    launch_combine(yp, nullptr, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
+    if (fz)
+        launch_combine_norm(yp, nullptr, inv, wv, T, k, H, has_sh ? ysh : nullptr, fz->h, fz->gamma,
+                            fz->eps, fz->normed, st);
+    else
+        launch_combine(yp, nullptr, inv, wv, T, k, H, has_sh ? ysh : nullptr, y, st);
     mk->mark();
     return launched("moe_layer_forward");
 }
@@ -487,6 +503,24 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
     Marks mk{nullptr, 0, 0, nullptr};
     return layer_forward_impl(desc, wts, x, T, logits_or_null, y, topk_ids_out, topk_w_out, ws,
                               ws_bytes, stream, &mk);
+}
+
+moe_status moe_layer_forward_residual(const moe_layer_desc* desc, const moe_layer_weights* wts,
+                                      const uint16_t* x, int32_t T, const float* logits_or_null,
+                                      float* h, const float* gamma, float eps,
+                                      uint16_t* normed_bf16_out, int32_t* topk_ids_out,
+                                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!h) return fail(MOE_ERR_NULL, "h is NULL");
+    if ((gamma == nullptr) != (normed_bf16_out == nullptr))
+        return fail(MOE_ERR_NULL, "gamma and normed_bf16_out must both be given or both NULL");
+    if (!(eps >= 0.f)) return fail(MOE_ERR_SHAPE, "eps must be >= 0");
+    if (!al16(h) || (gamma && !al16(gamma)) || ((uintptr_t)normed_bf16_out & 7))
+        return fail(MOE_ERR_ALIGN, "h and gamma must be 16-byte, normed_bf16_out 8-byte aligned");
+    const Fuse fz{h, gamma, eps, normed_bf16_out};
+    Marks mk{nullptr, 0, 0, nullptr};
+    return layer_forward_impl(desc, wts, x, T, logits_or_null, nullptr, topk_ids_out, topk_w_out, ws,
+                              ws_bytes, stream, &mk, &fz);
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,

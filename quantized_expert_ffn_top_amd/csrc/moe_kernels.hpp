@@ -32,6 +32,12 @@ void launch_combine(const float* y_perm, const int* fp16_unless, const int32_t* 
                     int T, int k, int H, const float* shared, float* y, hipStream_t st);
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st);
+// The combine with the residual add and the next RMSNorm: h [T][H] += the
+// combined rows; normed = bf16(gamma * h / rms) when gamma is not null.
+// H a multiple of 4 up to 8192; h, gamma 16-byte and normed 8-byte aligned.
+void launch_combine_norm(const float* y_perm, const int* fp16_unless, const int32_t* inv, const float* w,
+                         int T, int k, int H, const float* shared, float* h, const float* gamma,
+                         float eps, uint16_t* normed, hipStream_t st);
 
 // ---- bandwidth path (moe_kernels_decode.hip), T <= kDecMaxT and
 // upgate_dec_supported(H, T, E) (the staged up|gate rows of two items and the

@@ -380,23 +380,12 @@ __device__ __forceinline__ float4 yrow4(const float* __restrict__ y_perm, int64_
     }
 }
 
-// y[t][h..h+3] = sum_j w[t][j] * y_perm[inv[t k + j]][h..h+3] (j in order)
-// + shared[t][h..h+3].  The rows are fp16 when fp16_unless is given and
-// *fp16_unless == 0 (the down GEMM's range check passed), else fp32.  One
-// float4 column per thread, four rows in flight.
-__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
-                                                       const int* __restrict__ fp16_unless,
-                                                       const int32_t* __restrict__ inv,
-                                                       const float* __restrict__ w, int k, int H,
-                                                       const float* __restrict__ shared,
-                                                       float* __restrict__ y) {
-    // block b: token b / ncb, float4 columns 256 (b % ncb) .. +255 (a
-    // one-dimensional grid: any T up to the library's limit)
-    const int ncb = (H / 4 + 255) / 256;
-    const int t = blockIdx.x / ncb;
-    const int c = (blockIdx.x - t * ncb) * blockDim.x + threadIdx.x, h = 4 * c;
-    if (h >= H) return;
-    const bool h16 = fp16_unless && *fp16_unless == 0;
+// Float4 column c of token t's combined output: sum_j w[t][j] *
+// y_perm[inv[t k + j]][4c..4c+3] (j in order) + shared[t][4c..4c+3] (when
+// given).  The rows are fp16 when h16, else fp32.  Four rows in flight.
+__device__ __forceinline__ float4 combine4(const float* __restrict__ y_perm, bool h16,
+                                           const int32_t* __restrict__ inv, const float* __restrict__ w,
+                                           int t, int k, int H, const float* __restrict__ shared, int c) {
     auto sum = [&](auto h16c) {
         constexpr bool F16 = decltype(h16c)::value;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -429,13 +418,32 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_per
     };
     float4 acc = h16 ? sum(std::true_type{}) : sum(std::false_type{});
     if (shared) {
-        const float4 sv = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + h);
+        const float4 sv = *reinterpret_cast<const float4*>(shared + (int64_t)t * H + 4 * c);
         acc.x += sv.x;
         acc.y += sv.y;
         acc.z += sv.z;
         acc.w += sv.w;
     }
-    *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = acc;
+    return acc;
+}
+
+// y[t][h..h+3] = combine4(t, h / 4).  The rows are fp16 when fp16_unless is
+// given and *fp16_unless == 0 (the down GEMM's range check passed), else
+// fp32.  One float4 column per thread.
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y_perm,
+                                                       const int* __restrict__ fp16_unless,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w, int k, int H,
+                                                       const float* __restrict__ shared,
+                                                       float* __restrict__ y) {
+    // block b: token b / ncb, float4 columns 256 (b % ncb) .. +255 (a
+    // one-dimensional grid: any T up to the library's limit)
+    const int ncb = (H / 4 + 255) / 256;
+    const int t = blockIdx.x / ncb;
+    const int c = (blockIdx.x - t * ncb) * blockDim.x + threadIdx.x, h = 4 * c;
+    if (h >= H) return;
+    const bool h16 = fp16_unless && *fp16_unless == 0;
+    *reinterpret_cast<float4*>(y + (int64_t)t * H + h) = combine4(y_perm, h16, inv, w, t, k, H, shared, c);
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -468,28 +476,59 @@ __global__ void k_rmsnorm_residual(float* __restrict__ h, const float* __restric
         nrow[i] = (uint16_t)f32_to_bf16(gamma[i] * (row[i] * r));
 }
 
-// The same for rows of H = 4m <= 1024 NV floats with 16-byte aligned operands:
-// each thread keeps its NV float4 of the row in registers between the sum of
-// squares and the scaling, so the row is read once and written once (with the
-// bf16 output as 8-byte stores).
+// Register form for rows of H = 4m floats (m <= 2048) with 16-byte aligned
+// operands: one block of TPB = min(m rounded up to 64, 1024) threads per row,
+// thread i holding float4 columns i + TPB j (j < NV) in registers between the
+// residual add, the sum of squares and the scaling, so the row is read once
+// and written once (the bf16 output as 8-byte stores).  The sum of squares is
+// reduced in a fixed order: per thread, per wave, then the waves' sums in
+// wave order.
+template <int NV>
+__device__ __forceinline__ void norm_row(const float4 (&v)[NV], int n4, int H, const float* __restrict__ gamma,
+                                         float eps, uint16_t* __restrict__ normed_row, float* s_red) {
+    const int tpb = blockDim.x;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ss = wave_sum_f32(ss);
+    if (__lane_id() == 0) s_red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int q = 0; q < (tpb >> 6); ++q) tot += s_red[q];
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    const float4* g4 = reinterpret_cast<const float4*>(gamma);
+    uint2* nrow = reinterpret_cast<uint2*>(normed_row);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = threadIdx.x + tpb * j;
+        if (i < n4) {
+            const float4 g = g4[i];
+            uint2 o;
+            o.x = f32_to_bf16(g.x * (v[j].x * r)) | (f32_to_bf16(g.y * (v[j].y * r)) << 16);
+            o.y = f32_to_bf16(g.z * (v[j].z * r)) | (f32_to_bf16(g.w * (v[j].w * r)) << 16);
+            nrow[i] = o;
+        }
+    }
+}
+
 template <int NV, bool DELTA>
-__global__ void __launch_bounds__(256) k_rmsnorm_residual_v(float* __restrict__ h, const float* __restrict__ delta,
-                                                            const float* __restrict__ gamma, float eps, int H,
-                                                            uint16_t* __restrict__ normed) {
-    __shared__ float s_red[4];
-    const int n4 = H >> 2;
+__global__ void __launch_bounds__(1024) k_rmsnorm_residual_v(float* __restrict__ h, const float* __restrict__ delta,
+                                                             const float* __restrict__ gamma, float eps, int H,
+                                                             uint16_t* __restrict__ normed) {
+    __shared__ float s_red[16];
+    const int n4 = H >> 2, tpb = blockDim.x;
     float4* row = reinterpret_cast<float4*>(h + (int64_t)blockIdx.x * H);
     float4 v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int i = threadIdx.x + 256 * j;
+        const int i = threadIdx.x + tpb * j;
         v[j] = i < n4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (DELTA) {
         const float4* drow = reinterpret_cast<const float4*>(delta + (int64_t)blockIdx.x * H);
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const int i = threadIdx.x + 256 * j;
+            const int i = threadIdx.x + tpb * j;
             if (i < n4) {
                 const float4 d = drow[i];
                 v[j].x += d.x;
@@ -501,27 +540,46 @@ __global__ void __launch_bounds__(256) k_rmsnorm_residual_v(float* __restrict__ 
         }
     }
     if (!normed) return;
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    ss = wave_sum_f32(ss);
-    if (__lane_id() == 0) s_red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    const float4* g4 = reinterpret_cast<const float4*>(gamma);
-    uint2* nrow = reinterpret_cast<uint2*>(normed + (int64_t)blockIdx.x * H);
+    norm_row<NV>(v, n4, H, gamma, eps, normed + (int64_t)blockIdx.x * H, s_red);
+}
+
+// The layer's combine fused with the residual add and the next layer's
+// RMSNorm, in the register form above: h[t] += combine4(t, .) and, with
+// gamma, normed[t] = bf16(gamma * h[t] / sqrt(mean(h[t]^2) + eps)).  The same
+// column mapping, sums and reduction as k_combine followed by
+// k_rmsnorm_residual_v, so the results are the same bits.
+template <int NV>
+__global__ void __launch_bounds__(1024) k_combine_norm(const float* __restrict__ y_perm,
+                                                       const int* __restrict__ fp16_unless,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w, int k, int H,
+                                                       const float* __restrict__ shared, float* __restrict__ h,
+                                                       const float* __restrict__ gamma, float eps,
+                                                       uint16_t* __restrict__ normed) {
+    __shared__ float s_red[16];
+    const int t = blockIdx.x, n4 = H >> 2, tpb = blockDim.x;
+    const bool h16 = fp16_unless && *fp16_unless == 0;
+    float4* row = reinterpret_cast<float4*>(h + (int64_t)t * H);
+    float4 v[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int i = threadIdx.x + 256 * j;
+        const int i = threadIdx.x + tpb * j;
+        v[j] = i < n4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = threadIdx.x + tpb * j;
         if (i < n4) {
-            const float4 g = g4[i];
-            uint2 o;
-            o.x = f32_to_bf16(g.x * (v[j].x * r)) | (f32_to_bf16(g.y * (v[j].y * r)) << 16);
-            o.y = f32_to_bf16(g.z * (v[j].z * r)) | (f32_to_bf16(g.w * (v[j].w * r)) << 16);
-            nrow[i] = o;
+            const float4 d = combine4(y_perm, h16, inv, w, t, k, H, shared, i);
+            v[j].x += d.x;
+            v[j].y += d.y;
+            v[j].z += d.z;
+            v[j].w += d.w;
+            row[i] = v[j];
         }
     }
+    if (!normed) return;
+    norm_row<NV>(v, n4, H, gamma, eps, normed + (int64_t)t * H, s_red);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -572,19 +630,37 @@ void launch_combine(const float* y_perm, const int* fp16_unless, const int32_t* 
     k_combine<<<(unsigned)(cdiv(H / 4, 256) * T), 256, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, y);
 }
 
+// Block width of the register-form row kernels: m = H / 4 float4 columns,
+// one per thread up to 1024 (rounded up to whole waves), two beyond.
+static inline int row_tpb(int H) {
+    const int n4 = H >> 2;
+    return n4 <= 1024 ? ((n4 + 63) & ~63) : 1024;
+}
+
+void launch_combine_norm(const float* y_perm, const int* fp16_unless, const int32_t* inv, const float* w,
+                         int T, int k, int H, const float* shared, float* h, const float* gamma,
+                         float eps, uint16_t* normed, hipStream_t st) {
+    const int tpb = row_tpb(H);
+    if ((H >> 2) <= 1024)
+        k_combine_norm<1><<<T, tpb, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, h, gamma, eps, normed);
+    else
+        k_combine_norm<2><<<T, tpb, 0, st>>>(y_perm, fp16_unless, inv, w, k, H, shared, h, gamma, eps, normed);
+}
+
 void launch_rmsnorm(float* h, const float* delta, const float* gamma, float eps, int T, int H,
                     uint16_t* normed, hipStream_t st) {
     auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
     const bool vec = (H & 3) == 0 && H <= 8192 && a16(h) && (!delta || a16(delta)) &&
                      (!normed || (a16(gamma) && ((uintptr_t)normed & 7) == 0));
+    const int tpb = row_tpb(H);
     if (!vec) {
         k_rmsnorm_residual<<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
-    } else if (H <= 4096) {
-        if (delta) k_rmsnorm_residual_v<4, true><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
-        else k_rmsnorm_residual_v<4, false><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+    } else if ((H >> 2) <= 1024) {
+        if (delta) k_rmsnorm_residual_v<1, true><<<T, tpb, 0, st>>>(h, delta, gamma, eps, H, normed);
+        else k_rmsnorm_residual_v<1, false><<<T, tpb, 0, st>>>(h, delta, gamma, eps, H, normed);
     } else {
-        if (delta) k_rmsnorm_residual_v<8, true><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
-        else k_rmsnorm_residual_v<8, false><<<T, 256, 0, st>>>(h, delta, gamma, eps, H, normed);
+        if (delta) k_rmsnorm_residual_v<2, true><<<T, tpb, 0, st>>>(h, delta, gamma, eps, H, normed);
+        else k_rmsnorm_residual_v<2, false><<<T, tpb, 0, st>>>(h, delta, gamma, eps, H, normed);
     }
 }
 

@@ -112,6 +112,29 @@ def test_layer_forward_error_paths():
     assert _fwd(d2, _w()) == 1                             # shared_inter > 0, no shared weights
 
 
+def test_layer_forward_residual_error_paths():
+    """The fused residual entry point checks its own arguments first, then the
+    layer's (bad descriptor, weights, workspace) as moe_layer_forward does."""
+    d = Q.desc(256, 128, 16, 2, 0)
+    lib = Q.load()
+    w = _w()
+
+    def call(h=P2, gamma=P, eps=1e-6, normed=P2, d_=d, ws_bytes=1 << 30):
+        return lib.moe_layer_forward_residual(ctypes.byref(d_), ctypes.byref(w), P, 4, None, h, gamma,
+                                              eps, normed, None, None, P, ws_bytes, None)
+    assert call(h=None) == 1                               # no residual stream
+    assert call(normed=None) == 1                          # gamma without an output
+    assert call(gamma=None) == 1                           # an output without gamma
+    assert call(eps=-1.0) == 2
+    assert call(h=P2 + 8) == 4                             # h not 16-byte aligned
+    assert call(gamma=P + 4) == 4
+    assert call(normed=P2 + 2) == 4                        # normed not 8-byte aligned
+    assert call(ws_bytes=16) == 5                          # then the layer's own checks
+    bad = Q.desc(250, 128, 16, 2, 0)
+    assert call(d_=bad) == 2
+    assert Q.load().moe_last_error()
+
+
 def test_stage_error_paths():
     lib = Q.load()
     assert lib.moe_route(None, 4, 16, 2, P, P2, None) == 1

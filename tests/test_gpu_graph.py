@@ -1,5 +1,6 @@
 """The layer inside a captured HIP graph: a three-layer step (RMSNorm +
-residual between layers) captured once with torch.cuda.graph and replayed
+residual between layers, as two calls per layer or fused into the layer's
+call) captured once with torch.cuda.graph and replayed
 several times, with eager work and synchronisations between the replays;
 every replay must equal the eager step bit for bit (the kernels are
 deterministic).  Both regimes: a decode batch (bandwidth kernels) and a
@@ -15,8 +16,9 @@ from tests._helpers import dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused_residual"])
 @pytest.mark.parametrize("T", [3, 40])
-def test_stack_step_graph_replay_matches_eager(T):
+def test_stack_step_graph_replay_matches_eager(T, fused):
     sh, nl, seed = synth.REAL, 3, 17
     layers = [synth.real_layer(sh, seed, l, zipf_s=1.0, device=dev()) for l in range(nl)]
     wts = [Q.weights(L.experts, sh.expert_bytes, L.router_w, L.router_b, L.shared_ug,
@@ -27,16 +29,24 @@ def test_stack_step_graph_replay_matches_eager(T):
     x0 = synth.tokens_bf16(T, sh.hidden, seed).float().to(dev())
     h = torch.empty_like(x0)
     normed = torch.empty((T, sh.hidden), dtype=torch.bfloat16, device=dev())
+    normed2 = torch.empty_like(normed)
     y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev())
 
     def step():
         h.copy_(x0)
         Q.moe_rmsnorm_residual(h, None, gammas[0], 1e-6, normed)
+        nin, nout = normed, normed2
         for l in range(nl):
-            Q.moe_layer_forward(d, wts[l], normed, y, ws)
             last = l + 1 == nl
-            Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
-                                   None if last else normed)
+            if fused:
+                Q.moe_layer_forward_residual(d, wts[l], nin, h, ws,
+                                             gamma=None if last else gammas[l + 1], eps=1e-6,
+                                             normed=None if last else nout)
+                nin, nout = nout, nin
+            else:
+                Q.moe_layer_forward(d, wts[l], normed, y, ws)
+                Q.moe_rmsnorm_residual(h, y, None if last else gammas[l + 1], 1e-6,
+                                       None if last else normed)
 
     step()
     torch.cuda.synchronize()

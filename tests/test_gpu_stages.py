@@ -21,7 +21,7 @@ def _u8(arr):
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8)).to(dev())
 
 
-# ---------------------------------------------------------------- dequant (A4)
+# ---------------------------------------------------------------- dequant
 
 def _hand_q3s_blocks():
     blocks = []
@@ -166,7 +166,7 @@ def test_dequant_real_experts_bitexact(mode):
         assert np.array_equal(out2.cpu().numpy().view(np.uint32), ref2.view(np.uint32)), e
 
 
-# ---------------------------------------------------------------- router (A1)
+# ---------------------------------------------------------------- router
 
 @pytest.mark.parametrize("T,sh", [(1, synth.REAL), (3, synth.REAL), (8, synth.REAL), (16, synth.REAL),
                                   (17, synth.REAL), (300, synth.REAL), (8192, synth.REAL),
@@ -188,7 +188,7 @@ def test_router_logits(T, sh):
     assert np.abs(got - ref).max() <= 2e-5 * np.abs(ref).max()
 
 
-# ---------------------------------------------------------------- top-k (A2)
+# ---------------------------------------------------------------- top-k
 
 def _route(logits_np, k):
     T, E = logits_np.shape
@@ -223,7 +223,7 @@ def test_route_negative_zero_ties_positive_zero():
     assert ids[0].tolist() == [0, 1, 3]
 
 
-# ---------------------------------------------------------------- permute (A3)
+# ---------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("T,E,k", [(1, 512, 10), (3, 512, 10), (8, 512, 10), (16, 16, 2),
                                    (17, 512, 10), (100, 16, 2), (1000, 64, 7), (8192, 512, 10)])
@@ -327,7 +327,7 @@ def test_shared_expert_dense(T, Is):
     assert_close(y_sh.cpu().numpy(), ref_ysh, "dense shared expert T=%d Is=%d" % (T, Is))
 
 
-# ---------------------------------------------------------------- RMSNorm (A9)
+# ---------------------------------------------------------------- RMSNorm
 
 @pytest.mark.parametrize("H", [3072, 6144, 100, 1002])
 def test_rmsnorm_residual(H):
