@@ -288,14 +288,14 @@ def main():
             ms = time_steps(Tp, x, args.prefill_steps, 2, 1)
             kd = time_kernels(Tp, x, 4, 1, 12)
             wts[0] = saved
-            names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate",
+            names = ["router_shared_upgate", "topk_and_f16", "permute", "shared_down", "upgate",
                      "down", "down_fp32_if_needed", "combine"]
             flops = FLOP_PER_TOKEN * Tp
             ug_flops = 2.0 * Tp * K * 2 * I * H
             dn_flops = 2.0 * Tp * K * I * H
             kern = {nm: {"us": round(t * 1e3, 1)} for nm, t in zip(names, kd)}
-            kern["upgate"]["TFLOPs"] = round(ug_flops / (kd[5] * 1e-3) / 1e12, 1)
-            kern["down"]["TFLOPs"] = round(dn_flops / ((kd[6] + kd[7]) * 1e-3) / 1e12, 1)
+            kern["upgate"]["TFLOPs"] = round(ug_flops / (kd[4] * 1e-3) / 1e12, 1)
+            kern["down"]["TFLOPs"] = round(dn_flops / ((kd[5] + kd[6]) * 1e-3) / 1e12, 1)
             results[key] = {
                 "tokens": Tp, "routing": "Zipf(1.0)" if key == "prefill" else "uniform",
                 "tokens_per_s": round(Tp / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
@@ -440,7 +440,7 @@ def stack_prefill(args, Q, synth, torch, np, dev, emit=True):
     torch.cuda.synchronize()
     marks = one_pass(evs)
     torch.cuda.synchronize()
-    names = ["router_shared_upgate", "topk", "to_f16", "permute", "shared_down", "upgate", "down",
+    names = ["router_shared_upgate", "topk_and_f16", "permute", "shared_down", "upgate", "down",
              "down_fp32_if_needed", "combine"]
     fmt_name = {2: "q3s256", 3: "nl4_32", 4: "q2s256", 5: "q2_32", 6: "q3k256", 7: "nl4s256"}
     ug_t, dn_t, ug_by, dn_by, tot = {}, {}, {}, {}, {}
@@ -449,8 +449,8 @@ def stack_prefill(args, Q, synth, torch, np, dev, emit=True):
         for nm, t in zip(names, dur):
             tot[nm] = tot.get(nm, 0.0) + t
         u, dn = descs[l].upgate_fmt, descs[l].down_fmt
-        ug_t.setdefault(fmt_name[u], []).append(dur[5])
-        dn_t.setdefault(fmt_name[dn], []).append(dur[6] + dur[7])
+        ug_t.setdefault(fmt_name[u], []).append(dur[4])
+        dn_t.setdefault(fmt_name[dn], []).append(dur[5] + dur[6])
     ug_flops = 2.0 * T * K * 2 * I * H            # per layer
     dn_flops = 2.0 * T * K * I * H
     per_fmt = {"upgate": {f: {"layers": len(v), "us_mean": round(1e3 * np.mean(v), 1),

@@ -255,7 +255,7 @@ moe_status moe_layer_forward_residual(const moe_layer_desc* desc, const moe_laye
  * up|gate partials, fp16 copy of x), routed up|gate (routing, top-k and
  * permutation, at its start), down projections (routed + shared), combine;
  * T > 16: [router and shared up|gate GEMM (if no logits or a shared
- * expert)], top-k, fp16 staging, permutation (3 kernels, one mark), [shared
+ * expert)], top-k (with the fp16 copy of x), permutation (3 kernels, one mark), [shared
  * down GEMM], routed up|gate GEMM, routed down GEMM (fp16 rows), its fp32
  * repeat (does nothing unless the range check asked for it), combine. */
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* wts,

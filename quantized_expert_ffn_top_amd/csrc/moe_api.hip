@@ -243,7 +243,7 @@ moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32
     if (!al4(logits) || !al4(topk_ids) || !al4(topk_w)) return fail(MOE_ERR_ALIGN, "misaligned");
     moe_status s = check_device();
     if (s != MOE_OK) return s;
-    launch_topk(logits, T, E, k, topk_ids, topk_w, nullptr, nullptr, (hipStream_t)stream);
+    launch_topk(logits, T, E, k, topk_ids, topk_w, nullptr, nullptr, nullptr, nullptr, 0, (hipStream_t)stream);
     return launched("moe_route");
 }
 
@@ -450,9 +450,7 @@ moe_status layer_forward_impl(const moe_layer_desc* desc, const moe_layer_weight
                                        wts->router_b, lg, sug, Is, ash, st);
             mk->mark();
         }
-        launch_topk(L_use, T, E, k, ids, wv, topk_ids_out, topk_w_out, st);
-        mk->mark();
-        launch_to_f16(x, x16, (int64_t)T * H, st);
+        launch_topk(L_use, T, E, k, ids, wv, topk_ids_out, topk_w_out, x, x16, H, st);
         mk->mark();
         launch_permute_large(ids, T, k, E, kGemmBM, hist, offs, perm, inv, tiles, nt, st);
         mk->mark();

@@ -19,8 +19,9 @@ constexpr int kGemmBK = 64;
 // ---- small kernels (moe_kernels_small.hip)
 void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, hipStream_t st);
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st);
+// with x16 (H a multiple of 256, at most 8192): also x16 = fp16(x), one row per token
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                 int32_t* ids2, float* w2, hipStream_t st);
+                 int32_t* ids2, float* w2, const uint16_t* x, uint16_t* x16, int H, hipStream_t st);
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t st);
 void launch_permute_large(const int32_t* ids, int T, int k, int E, int BM, int32_t* hist,

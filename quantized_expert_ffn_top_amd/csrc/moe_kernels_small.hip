@@ -145,24 +145,48 @@ __global__ void k_to_f16(const uint16_t* __restrict__ x, uint16_t* __restrict__ 
 // ---------------------------------------------------------------- routing
 
 // Generic top-k: one wave per token.  Logits from `logits` (fp32 [T][E]).
-__global__ void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                       int32_t* __restrict__ ids, float* __restrict__ w,
-                       int32_t* __restrict__ ids2, float* __restrict__ w2) {
+// With x16 (H a multiple of 256): the wave also writes the fp16 copy of its
+// token's row x[t] (the matrix-core operand of the routed GEMMs), its loads
+// issued before the top-k so that they are in flight meanwhile.
+__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w,
+                                              int32_t* __restrict__ ids2, float* __restrict__ w2,
+                                              const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
+                                              int H) {
     __shared__ uint64_t scr[4][kTopkScratch];
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= T) return;
+    const int lane = __lane_id();
+    // the lane's 4-element pieces of the row: the first kPre loaded before
+    // the top-k, any others (H > 3072) after it
+    constexpr int kPre = 12;
+    uint2 xr[kPre];
+    const int nx = x16 ? H / 256 : 0;
+    const uint2* xs = reinterpret_cast<const uint2*>(x + (int64_t)t * H);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (i < nx) xr[i] = xs[lane + 64 * i];
     const float* row = logits + (int64_t)t * E;
     int id;
     float v;
     wave_topk([&](int e) { return row[e]; }, E, k, scr[threadIdx.x >> 6], id, v);
     float wt = wave_softmax_selected(v, k);
-    const int lane = __lane_id();
     if (lane < k) {
         ids[t * k + lane] = id;
         w[t * k + lane] = wt;
         if (ids2) ids2[t * k + lane] = id;
         if (w2) w2[t * k + lane] = wt;
     }
+    uint2* xd = reinterpret_cast<uint2*>(x16 + (int64_t)t * H);
+    auto cvt = [](uint2 q) {
+        return make_uint2(
+            pack2(f32_to_f16_bits(bf16_to_f32(q.x & 0xffffu)), f32_to_f16_bits(bf16_to_f32(q.x >> 16))),
+            pack2(f32_to_f16_bits(bf16_to_f32(q.y & 0xffffu)), f32_to_f16_bits(bf16_to_f32(q.y >> 16))));
+    };
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        if (i < nx) xd[lane + 64 * i] = cvt(xr[i]);
+    for (int i = kPre; i < nx; ++i) xd[lane + 64 * i] = cvt(xs[lane + 64 * i]);
 }
 
 
@@ -602,8 +626,8 @@ void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st) 
 }
 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                 int32_t* ids2, float* w2, hipStream_t st) {
-    k_topk<<<cdiv(T, 4), 256, 0, st>>>(logits, T, E, k, ids, w, ids2, w2);
+                 int32_t* ids2, float* w2, const uint16_t* x, uint16_t* x16, int H, hipStream_t st) {
+    k_topk<<<cdiv(T, 4), 256, 0, st>>>(logits, T, E, k, ids, w, ids2, w2, x, x16, H);
 }
 
 void launch_permute_small(const int32_t* ids, int T, int E, int k, int32_t* offsets,
