@@ -398,30 +398,15 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
     const int RS = rb + 8;
     const int NG = FULL ? WAVES * GPW : H / 128;
 
-    // One register array serves both roles (a wave runs only one): the A
-    // operand of a decoder (every token of the batch, its K groups), the
-    // item in flight of a loader.
+    // The two roles run separate loops with the same number of barriers, so
+    // their register state never overlaps: a decoder keeps the A operand
+    // (every token of the batch, its K groups), a loader two items in
+    // flight.
     constexpr int RA = GPW * 16, RB = NCH * CH / 4;
-    uint32_t R[RA > RB ? RA : RB];
-    // Roles: waves [0, WAVES) decode; the kUgLoadWaves waves after them load
-    // the items, stage them and finish them, so that the decoders never wait
-    // for a load, a stage write or an epilogue.
+    uint32_t R[RA];                                         // decoders: A
+    uint32_t L0[RB], L1[RB];                                // loaders: item ring
     const bool loader = w >= WAVES;
     const int lt = tid - 64 * WAVES;                        // loader thread (loaders only)
-    if (!loader) {
-        const bool vt = r < T;
-        const uint16_t* xr = x16 + (int64_t)(vt ? r : 0) * H + 32 * g;
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) {
-            const int q = w + WAVES * gi;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 v = ((FULL || q < NG) && vt) ? ld16(xr + q * 128 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) R[16 * gi + 4 * i + c] = v[c];
-            }
-        }
-    }
     auto av = [&](int gi, int i) {
         return u32x4{R[16 * gi + 4 * i], R[16 * gi + 4 * i + 1], R[16 * gi + 4 * i + 2], R[16 * gi + 4 * i + 3]};
     };
@@ -441,7 +426,11 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
         rc[j] = (c >= 0 && row < 32) ? (row << 16 | col) : 32 << 16;
     }
 
-    auto issue = [&](int i) {                               // item i -> R
+    // item i -> S.  Every step issues the same loads (a fixed count, so the
+    // compiler's waits on one slot never cover the other slot's loads): an
+    // item past the block's last one loads one shared 16-byte line.
+    auto issue = [&](int i, uint32_t (&S)[RB]) {
+        const bool live = i < i1;
         const int ic = min(i, max(0, min(i1, n_items) - 1)), at = ic / nsl, sl = ic - at * nsl;
         const int e = __builtin_amdgcn_readfirstlane(s_tiles[3 * at]);
         const uint8_t* base = experts + (int64_t)e * estride + (int64_t)(16 * sl) * rb;
@@ -450,18 +439,18 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
             int v = rc[c];
             if constexpr (kPinRc) __asm__ volatile("" : "+v"(v));
             const int row = v >> 16, col = v & 0xffff;
-            const int go = row < 32 ? (row < 16 ? row : I - 16 + row) * rb + col : 0;
+            const int go = (live && row < 32) ? (row < 16 ? row : I - 16 + row) * rb + col : 0;
             if constexpr (CH == 16) {
                 const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + go));
-                R[4 * c] = t[0]; R[4 * c + 1] = t[1]; R[4 * c + 2] = t[2]; R[4 * c + 3] = t[3];
+                S[4 * c] = t[0]; S[4 * c + 1] = t[1]; S[4 * c + 2] = t[2]; S[4 * c + 3] = t[3];
             } else {
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                 const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + go));
-                R[2 * c] = t[0]; R[2 * c + 1] = t[1];
+                S[2 * c] = t[0]; S[2 * c + 1] = t[1];
             }
         }
     };
-    auto put = [&](int sb) {                                // R -> stage sb (8-byte stores)
+    auto put = [&](int sb, const uint32_t (&S)[RB]) {       // S -> stage sb (8-byte stores)
         uint8_t* st = stage + sb * ug_stage_bytes(H);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -471,7 +460,7 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
 #pragma unroll
             for (int h = 0; h < CH / 8; ++h)
                 *reinterpret_cast<uint2*>(st + lo + 8 * h) =
-                    make_uint2(R[(CH / 4) * c + 2 * h], R[(CH / 4) * c + 2 * h + 1]);
+                    make_uint2(S[(CH / 4) * c + 2 * h], S[(CH / 4) * c + 2 * h + 1]);
         }
     };
 
@@ -545,7 +534,8 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
     // decoder order.  Every loader thread issues the store (equal memory-op
     // counts on all paths); those without an output store out of range, which
     // the buffer unit drops.
-    auto finish = [&](int it) {
+    auto finish = [&](int it0, bool valid) {                // !valid: the store is dropped
+        const int it = valid ? it0 : i0;
         const int at = it / nsl, sl = it - at * nsl;
         const int row0 = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 1]);
         const int rows = __builtin_amdgcn_readfirstlane(s_tiles[3 * at + 2]);
@@ -561,47 +551,64 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
             gg += ru[v * 2 * 64 * 4 + 64 * 4];
         }
         const uint16_t av16 = (uint16_t)f32_to_f16_bits(bf16_to_f32(f32_to_bf16(silu_mul_fast(gg, u))));
-        const uint32_t off = j < rows ? (uint32_t)(((row0 + j) * I + 16 * sl + n) * 2) : 0x80000000u;
+        const uint32_t off = (valid && j < rows) ? (uint32_t)(((row0 + j) * I + 16 * sl + n) * 2) : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b16(av16, a_out, off, 0, 0);
     };
 
-    // Pipeline, one barrier per item.  Step it: the decoders decode item it
-    // from stage (it - i0) % 2 into red[it % 2]; the loaders write item it + 1
-    // from their registers to stage (it + 1 - i0) % 2, load item it + 2 into
-    // those registers and finish item it - 1 from red[(it - 1) % 2].  Item
-    // it + 2 is in flight during the decode of item it; loads stop at the
-    // block's last item (a block without items loads item min(i0, n_items - 1)
-    // in the prologue).
+    // Pipeline, one barrier per item in both roles.  Step it: the decoders
+    // decode item it from stage (it - i0) % 2 into red[it % 2]; the loaders
+    // write item it + 1 from its ring slot to stage (it + 1 - i0) % 2, load
+    // item it + 3 into that slot and finish item it - 1 from red[(it - 1) % 2].
+    // Items it + 2 and it + 3 are in flight during the decode of item it (a
+    // load has two steps to arrive); loads stop at the block's last item (a
+    // block without items loads item min(i0, n_items - 1) in the prologue).
+    // The loader loop takes two steps per trip so that the ring slots are
+    // fixed registers.
     if (loader) {
-        issue(i0);
-        put(0);
-        issue(i0 + 1);
-    }
-    __syncthreads();                                        // stage 0 written
-    auto lstep = [&](int it, bool more) {                   // R holds item it + 1
-        put((it + 1 - i0) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) issue(it + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (it > i0) finish(it - 1);
-    };
-    int it = i0;
-    for (; it + 2 < i1; ++it) {
-        if (loader) lstep(it, true);
-        else decode(it, (it - i0) & 1);
-        __syncthreads();
-    }
-    // the last (up to two) items: loads only for items that exist
-    for (; it < i1; ++it) {
-        if (loader) {
-            if (it + 1 < i1) lstep(it, false);
-            else if (it > i0) finish(it - 1);
-        } else {
-            decode(it, (it - i0) & 1);
+        issue(i0, L0);
+        issue(i0 + 1, L1);
+        put(0, L0);
+        issue(i0 + 2, L0);
+        __syncthreads();                                    // stage 0 written
+        int it = i0;
+        for (; it + 1 < i1; it += 2) {
+            put(1, L1);                                     // item it + 1 (it - i0 even)
+            __builtin_amdgcn_sched_barrier(0);
+            issue(it + 3, L1);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(it - 1, it > i0);
+            __syncthreads();
+            put(0, L0);                                     // step it + 1: item it + 2 (unread if none)
+            __builtin_amdgcn_sched_barrier(0);
+            issue(it + 4, L0);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(it, true);
+            __syncthreads();
         }
-        __syncthreads();
+        if (it < i1) {                                      // the last step when i1 - i0 is odd
+            finish(it - 1, it > i0);
+            __syncthreads();
+        }
+        if (i1 > i0) finish(i1 - 1, true);
+    } else {
+        const bool vt = r < T;
+        const uint16_t* xr = x16 + (int64_t)(vt ? r : 0) * H + 32 * g;
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+            const int q = w + WAVES * gi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 v = ((FULL || q < NG) && vt) ? ld16(xr + q * 128 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) R[16 * gi + 4 * i + c] = v[c];
+            }
+        }
+        __syncthreads();                                    // stage 0 written
+        for (int it = i0; it < i1; ++it) {
+            decode(it, (it - i0) & 1);
+            __syncthreads();
+        }
     }
-    if (loader && i1 > i0) finish(i1 - 1);
 
     if (shp) {                                              // shared expert: sum partials, SwiGLU
         for (int i = blockIdx.x * NT + tid; i < T * Is; i += G * NT) {
