@@ -122,11 +122,17 @@ def desc(hidden, inter, n_experts, top_k, shared_inter=0, upgate_fmt=MOE_FMT_Q3S
 
 def weights(experts, expert_stride, router_w=None, router_b=None, shared_upgate=None,
             shared_down=None):
-    return LayerWeights(experts.data_ptr(), expert_stride,
-                        None if router_w is None else router_w.data_ptr(),
-                        None if router_b is None else router_b.data_ptr(),
-                        None if shared_upgate is None else shared_upgate.data_ptr(),
-                        None if shared_down is None else shared_down.data_ptr())
+    """The device pointers of a layer's weights.  The record keeps the tensors
+    alive: a tensor made inside the call (a zero bias, say) would otherwise be
+    freed at once and its memory handed to the next allocation while the
+    record still points at it."""
+    w = LayerWeights(experts.data_ptr(), expert_stride,
+                     None if router_w is None else router_w.data_ptr(),
+                     None if router_b is None else router_b.data_ptr(),
+                     None if shared_upgate is None else shared_upgate.data_ptr(),
+                     None if shared_down is None else shared_down.data_ptr())
+    w._keep = (experts, router_w, router_b, shared_upgate, shared_down)
+    return w
 
 
 # ---------------------------------------------------------------- entry points

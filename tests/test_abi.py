@@ -190,3 +190,25 @@ def test_workspace_size_for_every_supported_format_pair(ug, dn):
         assert Q.moe_workspace_size(d, T) > 0
     d_bad = Q.desc(3072, 512, 512, 10, 512, dn if dn == 5 else 1, ug if ug == 2 else 4)
     assert Q.moe_workspace_size(d_bad, 8) == 0
+
+
+def test_weights_record_keeps_its_tensors_alive():
+    # a tensor made inside the call (a zero router bias, as the uniform-routing
+    # prefill uses) must outlive the record that points at it
+    import gc
+    import weakref
+
+    import torch
+
+    experts = torch.zeros(64, dtype=torch.uint8)
+    bias = torch.zeros(16, dtype=torch.float32)
+    ref = weakref.ref(bias)
+    w = Q.weights(experts, 64, None, bias)
+    ptr = bias.data_ptr()
+    del bias
+    gc.collect()
+    assert ref() is not None
+    assert w.router_b == ptr
+    del w
+    gc.collect()
+    assert ref() is None
