@@ -24,7 +24,7 @@
 //      loaded coalesced, a period ahead, into a per-wave LDS area; each lane
 //      reads back the bytes of its own MFMA fragment (one 32-weight
 //      sub-block or block of one row per 32-column half) and decodes them
-//      with a replicated LDS table chunk by chunk between the MFMAs.
+//      with an LDS table chunk by chunk between the MFMAs.
 // The MFMA's reduction order within a K step is permuted (lane half h takes
 // k = 32h .. 32h + 31) so that a lane's fragment is one contiguous sub-block;
 // A is read from LDS in the same order.
@@ -98,15 +98,28 @@ struct GemmArgs {
 // that 16 consecutive rows read at one chunk hit 16 distinct bank groups.
 __device__ __forceinline__ int aslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// LDS address of the Q3 pair-table entry for the 6-bit field at bit P of a
-// 96-bit index word: the field lands at address bits 7..12, ORed into cb.
-template <int P> __device__ __forceinline__ uint32_t q3_lut_addr(const uint32_t (&q)[3], uint32_t cb) {
-    constexpr int w = P >> 5, b = P & 31;
-    uint32_t x;
-    if constexpr (b + 6 > 32) x = __builtin_amdgcn_alignbit(q[w + 1], q[w], b - 7);
-    else if constexpr (b >= 7) x = q[w] >> (b - 7);
-    else x = q[w] << (7 - b);
-    return (x & 0x1F80u) | cb;
+// 8-byte LDS read (a must be a multiple of 8): one ds_read_b64.
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ u32x2 lds_ld2(uint32_t a) {
+    return *(const lds_u32x2*)(uintptr_t)a;
+}
+
+// Q3S quad table: entry v (12 bits: four 3-bit codes, the first in the low
+// bits) holds the four codebook values (C3[v & 7], C3[v >> 3 & 7], C3[v >> 6
+// & 7], C3[v >> 9]) as fp16, 8 bytes, in one copy (4096 entries, 32 KB).  One
+// 8-byte read decodes four weights, so the index bits are moved into place
+// once per four weights, not once per two as with a pair table.
+constexpr int kQ3QuadDw = 4096 * 2;
+// Byte address of the entry for the four codes at bits P .. P + 11 of the
+// 96-bit index string q[0..2]: the field lands at address bits 3..14, or-ed
+// onto `base` (a 32 KB-aligned table).
+template <int P> __device__ __forceinline__ uint32_t q3_quad_addr(const uint32_t (&q)[3], uint32_t base) {
+    constexpr int wd = P >> 5, lo = P & 31;
+    uint32_t v;
+    if constexpr (lo + 12 > 32) v = __builtin_amdgcn_alignbit(q[wd + 1], q[wd], lo - 3);
+    else if constexpr (lo >= 3) v = q[wd] >> (lo - 3);
+    else v = q[wd] << (3 - lo);
+    return (v & 0x7ff8u) | base;
 }
 // LDS address of the nibble-table entry for the 4-bit field at bit P of a
 // 64-bit index word (two 2-bit indices): the field lands at address bits
@@ -118,15 +131,6 @@ template <int P> __device__ __forceinline__ uint32_t nib_lut_addr(const uint32_t
     else x = q[w] << (7 - b);
     return (x & 0x780u) | cb;
 }
-// Table addresses of the four pairs of chunk KK (weights 8 KK .. 8 KK + 7).
-template <int KK>
-__device__ __forceinline__ void q3_chunk_addrs(const uint32_t (&q)[3], uint32_t cb, uint32_t (&aa)[4]) {
-    aa[0] = q3_lut_addr<24 * KK + 0>(q, cb);
-    aa[1] = q3_lut_addr<24 * KK + 6>(q, cb);
-    aa[2] = q3_lut_addr<24 * KK + 12>(q, cb);
-    aa[3] = q3_lut_addr<24 * KK + 18>(q, cb);
-}
-
 template <int MODE>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr int kBF = bfmt<MODE>();
@@ -152,8 +156,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr int kSMX = TBM / 32;                  // 32-row groups per tile
 
     __shared__ u32x4 As[kStages][TBM * 8];
-    // Decode tables, replicated so that random indices spread over the banks:
-    // Q3 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
+    // Decode tables.  Q3S-256: the quad table, 12-bit index -> four fp16
+    // codebook values, one copy (a lookup decodes four weights; random
+    // 8-byte reads meet some bank conflicts, which cost less than the second
+    // address the pair table took).  The others replicated so that random
+    // indices spread over the banks:
+    // Q3K-256 pair (6-bit) -> (C3[lo], C3[hi]), 32 copies (entry * 32 + lane % 32);
     // NL4 byte -> (T4[lo], T4[hi]) (/ 8 for the down fold), 32 or 16 copies
     // (entry * copies + lane % copies);
     // Q2S nibble -> (C2[lo], C2[hi]) and Q2 nibble -> (lo - 2, hi - 2), 32
@@ -162,7 +170,9 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // that two blocks still fit a CU's LDS)
     constexpr int kNLCopies = kNLS ? 16 : 32;
     constexpr int kNLSh = kNLS ? 6 : 7;                        // log2(copies * 4)
-    constexpr int kTabDw = kNLTab ? 256 * kNLCopies : kLutDw;
+    // Q3S-256: the quad table (12-bit index -> four fp16 codebook values, one
+    // copy, 32 KB)
+    constexpr int kTabDw = kQ3 ? kQ3QuadDw : kNLTab ? 256 * kNLCopies : kLutDw;
     __shared__ __attribute__((aligned(kTabDw * 4))) uint32_t lut[kTabDw];
     constexpr int kPer = (kB256 || kSub) ? 4 : 2;   // quantized B: K steps per period
     // bytes of a weight row per period in LDS (Q3K-256: the 110-byte block
@@ -360,7 +370,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
 
     // LDS byte address of a table entry = cb | entry << 7 (32 copies) or
     // << kNLSh (NL4).
-    const uint32_t cb = lds_addr(lut) | (kNLTab ? (uint32_t)(lane & (kNLCopies - 1)) * 4u : (uint32_t)l32 * 4u);
+    const uint32_t cb = kQ3 ? lds_addr(lut)
+                      : lds_addr(lut) | (kNLTab ? (uint32_t)(lane & (kNLCopies - 1)) * 4u : (uint32_t)l32 * 4u);
     // NL4: table address of index byte B of the word nb
     auto nl_addr = [&](uint32_t nb, auto bc) {
         constexpr int B = decltype(bc)::value;
@@ -409,11 +420,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 const h2g s2 = {s, s};
                 if (kk == 0) F.dl[sn] = (float)d * 0.0078125f;
                 const uint32_t q[3] = {R[sn][0], R[sn][1], R[sn][2]};
-                uint32_t aa[4];
-                q3_chunk_addrs<kk>(q, cb, aa);
+                const u32x2 c0 = lds_ld2(q3_quad_addr<24 * kk>(q, cb));
+                const u32x2 c1 = lds_ld2(q3_quad_addr<24 * kk + 12>(q, cb));
+                const uint32_t cv[4] = {c0[0], c0[1], c1[0], c1[1]};
 #pragma unroll
                 for (int p = 0; p < 4; ++p)               // c * s, an exact fp16 integer
-                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * s2);
+                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, cv[p]) * s2);
             } else if constexpr (kNL) {
                 // h = 0: d in bytes 0-1, indices in bytes 2..17;
                 // h = 1: d in bytes 2-3, indices in bytes 4..19.
@@ -630,7 +642,18 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
         // 16-byte chunks: four copies of one entry each
         for (int i = tid; i < kTabDw / 4; i += 256) {
             uint32_t v;
-            if (kQ3 || kQ3K) {
+            if constexpr (kQ3) {                           // chunk i: quad entries 2i, 2i + 1
+                u32x4 qv;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int en = 2 * i + h;
+                    qv[2 * h] = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[(en >> 3) & 7]));
+                    qv[2 * h + 1] = pack2(f32_to_f16_bits((float)kC3[(en >> 6) & 7]), f32_to_f16_bits((float)kC3[en >> 9]));
+                }
+                reinterpret_cast<u32x4*>(lut)[i] = qv;
+                continue;
+            }
+            if (kQ3K) {
                 const int en = i >> 3;
                 v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
             } else if (kNat) {
