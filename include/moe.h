@@ -290,6 +290,28 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer
 moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, float* out,
                           void* stream);
 
+/* Helper, not the method: dequantize through the table decoders that the
+ * layer's kernels inline -- the same tables, lookup addresses and fp16
+ * multiplies, then the fp32 factor the kernel applies to its partial sums --
+ * so that a bit-exact comparison covers the decoders of the hot path (model
+ * card "Qwen3.8-Flash-Next - Avalon GGUF", "Files / Main model": the routed
+ * up/gate type with a scale per 256-weight block and sub-scales per 32
+ * weights, and the 4-bit non-linear down type).  fmt Q3S256 or NL4_32; path:
+ *   MOE_PATH_BANDWIDTH  the bandwidth-path kernels (T <= 16): Q3S256 from the
+ *                       pair table (6-bit index -> two codebook values) times
+ *                       s, then d/128; NL4_32 from its pair table, then d/128.
+ *                       Exact: the values of moe_dequantize.
+ *   MOE_PATH_GEMM       the grouped GEMM: Q3S256 from the quad table (12-bit
+ *                       index -> four values) times s, then d/128 (exact);
+ *                       NL4_32 as down weights, fp16_rne(16 d t / 128) / 16
+ *                       (the one rounding the grouped GEMM applies to them).
+ * Other formats or paths: MOE_ERR_FORMAT.  Blocks contiguous and 16-byte
+ * aligned, n_weights a positive multiple of the block size; out fp32. */
+#define MOE_PATH_BANDWIDTH 0
+#define MOE_PATH_GEMM 1
+moe_status moe_dequantize_path(int32_t fmt, int32_t path, const void* blocks, int64_t n_weights,
+                               float* out, void* stream);
+
 /* Helper for stacked layers (pre-norm residual): if delta is not NULL,
  * h += delta; then, if gamma and normed_bf16_out are not NULL,
  * normed[t] = bf16_rne(gamma * h[t] / sqrt(mean(h[t]^2) + eps)).  h fp32 [T][H]

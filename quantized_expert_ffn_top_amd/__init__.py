@@ -5,8 +5,9 @@ this package is its Python binding (ctypes) plus the build script.
 """
 
 from ._lib import (EXPORTS, LIB_PATH, MOE_FMT_BF16, MOE_FMT_NL4_32, MOE_FMT_NL4S256, MOE_FMT_Q2_32,
-                   MOE_FMT_Q2S256, MOE_FMT_Q3K256, MOE_FMT_Q3S256, LayerDesc,
-                   LayerWeights, MoeError, desc, load, moe_combine, moe_dequantize,
+                   MOE_FMT_Q2S256, MOE_FMT_Q3K256, MOE_FMT_Q3S256, MOE_PATH_BANDWIDTH, MOE_PATH_GEMM,
+                   LayerDesc, LayerWeights, MoeError, desc, load, moe_combine, moe_dequantize,
+                   moe_dequantize_path,
                    moe_expert_ffn, moe_layer_forward, moe_layer_forward_noalloc, moe_layer_forward_residual,
                    moe_layer_forward_timed,
                    moe_permute, moe_rmsnorm_residual,
@@ -14,8 +15,9 @@ from ._lib import (EXPORTS, LIB_PATH, MOE_FMT_BF16, MOE_FMT_NL4_32, MOE_FMT_NL4S
 
 __all__ = ["EXPORTS", "LIB_PATH", "MOE_FMT_BF16", "MOE_FMT_NL4_32", "MOE_FMT_Q2_32",
            "MOE_FMT_Q2S256", "MOE_FMT_Q3S256", "MOE_FMT_Q3K256", "MOE_FMT_NL4S256",
+           "MOE_PATH_BANDWIDTH", "MOE_PATH_GEMM",
            "LayerDesc", "LayerWeights", "MoeError", "desc", "load", "moe_combine",
-           "moe_dequantize", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_noalloc",
+           "moe_dequantize", "moe_dequantize_path", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_noalloc",
            "moe_layer_forward_residual",
            "moe_layer_forward_timed",
            "moe_permute",

@@ -21,6 +21,8 @@ MOE_FMT_Q2S256 = 4
 MOE_FMT_Q2_32 = 5
 MOE_FMT_Q3K256 = 6
 MOE_FMT_NL4S256 = 7
+MOE_PATH_BANDWIDTH = 0
+MOE_PATH_GEMM = 1
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_HIP"}
@@ -28,7 +30,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_FORMAT
 EXPORTS = ("moe_workspace_size", "moe_router_logits", "moe_route", "moe_permute",
            "moe_expert_ffn", "moe_combine", "moe_layer_forward", "moe_layer_forward_residual",
            "moe_layer_forward_timed",
-           "moe_layer_forward_noalloc", "moe_dequantize", "moe_rmsnorm_residual", "moe_status_string", "moe_last_error")
+           "moe_layer_forward_noalloc", "moe_dequantize", "moe_dequantize_path", "moe_rmsnorm_residual",
+           "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -82,6 +85,7 @@ def load():
         "moe_layer_forward_noalloc": (I32, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                             P, I32, P, P, P, P, P]),
         "moe_dequantize": (I32, [I32, P, I64, P, P]),
+        "moe_dequantize_path": (I32, [I32, I32, P, I64, P, P]),
         "moe_rmsnorm_residual": (I32, [P, P, P, F, I32, I32, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -229,6 +233,11 @@ def moe_layer_forward_noalloc(d, w, x, y, logits=None, topk_ids_out=None, topk_w
 def moe_dequantize(fmt, blocks, n_weights, out):
     _check(load().moe_dequantize(fmt, _ptr(blocks), n_weights, _ptr(out), _stream(blocks)),
            "moe_dequantize")
+
+
+def moe_dequantize_path(fmt, path, blocks, n_weights, out):
+    _check(load().moe_dequantize_path(fmt, path, _ptr(blocks), n_weights, _ptr(out), _stream(blocks)),
+           "moe_dequantize_path")
 
 
 def moe_rmsnorm_residual(h, delta, gamma, eps, normed):

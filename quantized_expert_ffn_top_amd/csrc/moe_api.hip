@@ -612,6 +612,24 @@ moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, fl
     return launched("moe_dequantize");
 }
 
+moe_status moe_dequantize_path(int32_t fmt, int32_t path, const void* blocks, int64_t n_weights,
+                               float* out, void* stream) {
+    g_last_error.clear();
+    if (!blocks || !out) return fail(MOE_ERR_NULL, "null argument");
+    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32)
+        return fail(MOE_ERR_FORMAT, "moe_dequantize_path supports Q3S256 and NL4_32");
+    if (path != MOE_PATH_BANDWIDTH && path != MOE_PATH_GEMM)
+        return fail(MOE_ERR_FORMAT, "path must be MOE_PATH_BANDWIDTH or MOE_PATH_GEMM");
+    const int64_t unit = fmt_block_weights(fmt);
+    if (n_weights < unit || n_weights % unit)
+        return fail(MOE_ERR_SHAPE, "n_weights must be a positive multiple of the block size");
+    if (!al16(blocks) || !al4(out)) return fail(MOE_ERR_ALIGN, "blocks must be 16-byte aligned");
+    moe_status s = check_device();
+    if (s != MOE_OK) return s;
+    launch_dequant_path(fmt, path, blocks, n_weights, out, (hipStream_t)stream);
+    return launched("moe_dequantize_path");
+}
+
 moe_status moe_rmsnorm_residual(float* h, const float* delta, const float* gamma, float eps,
                                 int32_t T, int32_t H, uint16_t* normed_bf16_out, void* stream) {
     g_last_error.clear();

@@ -18,6 +18,9 @@ constexpr int kGemmBK = 64;
 
 // ---- small kernels (moe_kernels_small.hip)
 void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, hipStream_t st);
+// through the table decoders of the layer's kernels: fmt Q3S256 or NL4_32,
+// path 0 (bandwidth-path kernels) or 1 (grouped GEMM)
+void launch_dequant_path(int fmt, int path, const void* blocks, int64_t n_weights, float* out, hipStream_t st);
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st);
 // with x16 (H a multiple of 256, at most 8192): also x16 = fp16(x), one row per token
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

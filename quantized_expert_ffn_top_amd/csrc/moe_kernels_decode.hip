@@ -17,6 +17,7 @@
 // down IQ4_NL; expert records packed up | gate | down).
 #include <algorithm>
 
+#include "moe_decoders.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -284,33 +285,9 @@ __device__ __forceinline__ void route_block(const float* __restrict__ logits, in
 }
 
 // ---------------------------------------------------------------- up|gate
-// Decode table: entry v = (fp16(C3[v & 7]), fp16(C3[v >> 3])) for an index
-// pair v (two 3-bit codes, the first in the low bits), in 32 copies
-// (copy = lane & 31) so that the random lookups of a half-wave fall in
-// distinct LDS banks.  Byte address v*128 + c*4: a pair's six index bits
-// reach it with one shift and one and-or.  The sub-scale s multiplies the
-// pair afterwards (v_pk_mul_f16; s*c is an exact fp16 integer, |s*c| <= 1016).
-constexpr int kQ3LutCopies = 32;
-constexpr int kQ3LutDw = 64 * kQ3LutCopies;       // 8 KB
-// C3 as int8 bytes (entry q in byte q): the table build needs no memory load.
-constexpr uint64_t kC3Bytes = 0x7F4E301700E1BD81ull;
-
-__device__ __forceinline__ float c3_entry(int q) {
-    return (float)(int8_t)(uint8_t)(kC3Bytes >> (8 * q));
-}
-
-// Byte address (bits 7..12) of the index pair starting at bit P of the
-// 96-bit index string w[0..2], or-ed onto `base`.
-template <int P>
-__device__ __forceinline__ uint32_t q3_pair_addr(const uint32_t* w, uint32_t base) {
-    constexpr int wd = P >> 5, lo = P & 31;
-    uint32_t v;
-    if constexpr (lo + 6 > 32) v = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], lo - 7);
-    else if constexpr (lo >= 7) v = w[wd] >> (lo - 7);
-    else if constexpr (wd > 0) v = __builtin_amdgcn_alignbit(w[wd], w[wd - 1], 25 + lo);
-    else v = w[wd] << (7 - lo);
-    return (v & 0x1f80u) | base;
-}
+// Decode table: the Q3S-256 pair table (moe_decoders.hpp).  The sub-scale s
+// multiplies each looked-up pair afterwards (s*c is an exact fp16 integer,
+// |s*c| <= 1016).
 
 // LDS budget of the up|gate kernel besides the table: the partial sums of
 // two items (WAVES x (up, gate) x 64 lanes x 4 floats each) and two staged
@@ -371,11 +348,7 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
     const int r = lane & 15, g = lane >> 4;
     // the decode table first, while the routing's logit loads are in flight
     // (the routing's barriers make it visible)
-    for (int i = tid; i < kQ3LutDw / 4; i += NT) {          // 16-byte chunk i: 8 per entry
-        const int v = i >> 3;
-        const uint32_t val = pack2(f32_to_f16_bits(c3_entry(v & 7)), f32_to_f16_bits(c3_entry(v >> 3)));
-        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
-    }
+    q3_pair_table_fill(lut, tid, NT);
     if (logits) {
         // routing (every block; block 0 publishes it), in the partial-sum space
         route_block<NT>(logits, np, lbias, T, E, k, dyn, s_tiles, s_perm, &s_nt, blockIdx.x == 0, ro.ids,
@@ -464,7 +437,7 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
         }
     };
 
-    const uint32_t cbase = lds_addr(lut) + (uint32_t)(lane & 31) * 4u;
+    const uint32_t cbase = lut_copy_base(lds_addr(lut), lane);
     const uint32_t kmag = (65536u + (uint32_t)k - 1u) / (uint32_t)k;   // t = (f * kmag) >> 16 for f < 512
     const __amdgpu_buffer_rsrc_t a_out =
         __builtin_amdgcn_make_buffer_rsrc(a16_perm, 0, (int)(T * k * I * 2), 0x00020000);
@@ -503,8 +476,8 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
         __builtin_amdgcn_sched_barrier(0);                                      \
         u32x4 bu[2], bg[2];                                                     \
         _Pragma("unroll") for (int i = 0; i < 8; ++i) {                         \
-            bu[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lu[i]) * su2); \
-            bg[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, lg[i]) * sg2); \
+            bu[i >> 2][i & 3] = mul_pair(lu[i], su2);                           \
+            bg[i >> 2][i & 3] = mul_pair(lg[i], sg2);                           \
         }                                                                       \
         _Pragma("unroll") for (int i = 0; i < 2; ++i) {                         \
             pu = mfma16_f16(av(gi, 2 * H_ + i), bu[i], pu);                     \
@@ -636,17 +609,8 @@ __global__ void __launch_bounds__(64 * (WAVES + kUgLoadWaves), 1) k_upgate_dec(
 }
 
 // ---------------------------------------------------------------- down
-// NL4 decode table: byte v -> (fp16(T4[v & 15]), fp16(T4[v >> 4])), the two
-// weights of one index byte (even weight in the low nibble), in 32 copies
-// (copy = lane & 31): byte address v*128 + c*4, so one shift and one and-or
-// per byte.  32 KB, built once per block.
-constexpr int kNl4LutDw = 256 * 32;
-// T4 as int8 bytes (entry q in byte q of the pair of words).
-constexpr uint64_t kT4Lo = 0x00F5E9DCCEBEA881ull, kT4Hi = 0x7F5B47382B1F140Aull;
-
-__device__ __forceinline__ float t4_entry(int q) {
-    return (float)(int8_t)(uint8_t)((q < 8 ? kT4Lo : kT4Hi) >> (8 * (q & 7)));
-}
+// Decode table: the NL4-32 pair table (moe_decoders.hpp), (T4[lo], T4[hi])
+// per index byte, built once per block.
 
 constexpr int kDnWaves = 8;
 constexpr int kDnChunkDw = 72;                    // 16 NL4 blocks of a row (288 bytes)
@@ -683,11 +647,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int nt = __builtin_amdgcn_readfirstlane(*ntiles);  // in flight during the table build
-    for (int i = tid; i < kNl4LutDw / 4; i += 64 * kDnWaves) {   // 16-byte chunk i: 8 per entry
-        const int v = i >> 3;
-        const uint32_t val = pack2(f32_to_f16_bits(t4_entry(v & 15)), f32_to_f16_bits(t4_entry(v >> 4)));
-        reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
-    }
+    nl4_pair_table_fill(lut, tid, 64 * kDnWaves);
     if (lane == 0) s_claim[w] = 0;
     __syncthreads();
 
@@ -809,7 +769,7 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
     const uint16_t* arow = a16_perm + (int64_t)(row0 + (r < rows ? r : 0)) * I + 8 * g;
     const __amdgpu_buffer_rsrc_t yo =
         __builtin_amdgcn_make_buffer_rsrc(y_perm, 0, (row0 + rows) * H * 4, 0x00020000);
-    const uint32_t cbase = lds_addr(lut) + (uint32_t)(lane & 31) * 4u;
+    const uint32_t cbase = lut_copy_base(lds_addr(lut), lane);
     uint32_t* st = stg[w];
 
     // whole chunks (16 NL4 blocks per row): the lane's 16-byte pieces,
@@ -906,10 +866,10 @@ __global__ void __launch_bounds__(64 * kDnWaves, 1) k_down_dec(
                 u32x4 bv[4];
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
-                    bv[k4][0] = lds_ld(((nib[k4] << 7) & 0x7f80u) | cbase);
-                    bv[k4][1] = lds_ld(((nib[k4] >> 1) & 0x7f80u) | cbase);
-                    bv[k4][2] = lds_ld(((nib[k4] >> 9) & 0x7f80u) | cbase);
-                    bv[k4][3] = lds_ld(((nib[k4] >> 17) & 0x7f80u) | cbase);
+                    bv[k4][0] = lds_ld(nl4_byte_addr<0>(nib[k4], cbase));
+                    bv[k4][1] = lds_ld(nl4_byte_addr<1>(nib[k4], cbase));
+                    bv[k4][2] = lds_ld(nl4_byte_addr<2>(nib[k4], cbase));
+                    bv[k4][3] = lds_ld(nl4_byte_addr<3>(nib[k4], cbase));
                 }
                 f32x4 part[4];
 #pragma unroll

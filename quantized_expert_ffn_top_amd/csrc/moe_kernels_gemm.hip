@@ -43,12 +43,12 @@
 //
 // Layer: "Avalon" README, opening paragraphs; model card "Qwen3.8-Flash-Next
 // - Avalon GGUF", "Files / Main model" (codecs, up | gate | down packing).
+#include "moe_decoders.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
 
 typedef _Float16 h2g __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int N> struct Cnt { static constexpr int value = N; };
 
@@ -98,29 +98,6 @@ struct GemmArgs {
 // that 16 consecutive rows read at one chunk hit 16 distinct bank groups.
 __device__ __forceinline__ int aslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// 8-byte LDS read (a must be a multiple of 8): one ds_read_b64.
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-__device__ __forceinline__ u32x2 lds_ld2(uint32_t a) {
-    return *(const lds_u32x2*)(uintptr_t)a;
-}
-
-// Q3S quad table: entry v (12 bits: four 3-bit codes, the first in the low
-// bits) holds the four codebook values (C3[v & 7], C3[v >> 3 & 7], C3[v >> 6
-// & 7], C3[v >> 9]) as fp16, 8 bytes, in one copy (4096 entries, 32 KB).  One
-// 8-byte read decodes four weights, so the index bits are moved into place
-// once per four weights, not once per two as with a pair table.
-constexpr int kQ3QuadDw = 4096 * 2;
-// Byte address of the entry for the four codes at bits P .. P + 11 of the
-// 96-bit index string q[0..2]: the field lands at address bits 3..14, or-ed
-// onto `base` (a 32 KB-aligned table).
-template <int P> __device__ __forceinline__ uint32_t q3_quad_addr(const uint32_t (&q)[3], uint32_t base) {
-    constexpr int wd = P >> 5, lo = P & 31;
-    uint32_t v;
-    if constexpr (lo + 12 > 32) v = __builtin_amdgcn_alignbit(q[wd + 1], q[wd], lo - 3);
-    else if constexpr (lo >= 3) v = q[wd] >> (lo - 3);
-    else v = q[wd] << (3 - lo);
-    return (v & 0x7ff8u) | base;
-}
 // LDS address of the nibble-table entry for the 4-bit field at bit P of a
 // 64-bit index word (two 2-bit indices): the field lands at address bits
 // 7..10, ORed into cb.
@@ -373,12 +350,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     const uint32_t cb = kQ3 ? lds_addr(lut)
                       : lds_addr(lut) | (kNLTab ? (uint32_t)(lane & (kNLCopies - 1)) * 4u : (uint32_t)l32 * 4u);
     // NL4: table address of index byte B of the word nb
-    auto nl_addr = [&](uint32_t nb, auto bc) {
-        constexpr int B = decltype(bc)::value;
-        constexpr uint32_t mask = 0xFFu << kNLSh;
-        const uint32_t v = B == 0 ? (nb << kNLSh) : (nb >> (8 * B - kNLSh));
-        return (v & mask) | cb;
-    };
+    auto nl_addr = [&](uint32_t nb, auto bc) { return nl4_byte_addr<decltype(bc)::value, kNLSh>(nb, cb); };
 
     // Fragments of one K step: f[sn][kk] = weights k = 32h + 8kk .. +7 of
     // column half sn; 256-weight blocks: dl[sn] = d / 128 of the lane's
@@ -420,12 +392,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 const h2g s2 = {s, s};
                 if (kk == 0) F.dl[sn] = (float)d * 0.0078125f;
                 const uint32_t q[3] = {R[sn][0], R[sn][1], R[sn][2]};
-                const u32x2 c0 = lds_ld2(q3_quad_addr<24 * kk>(q, cb));
-                const u32x2 c1 = lds_ld2(q3_quad_addr<24 * kk + 12>(q, cb));
-                const uint32_t cv[4] = {c0[0], c0[1], c1[0], c1[1]};
+                uint32_t fq[4];
+                q3_quad_decode8<kk>(q, cb, s2, fq);        // c * s, exact fp16 integers
 #pragma unroll
-                for (int p = 0; p < 4; ++p)               // c * s, an exact fp16 integer
-                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, cv[p]) * s2);
+                for (int p = 0; p < 4; ++p) F.f[sn][kk][p] = fq[p];
             } else if constexpr (kNL) {
                 // h = 0: d in bytes 0-1, indices in bytes 2..17;
                 // h = 1: d in bytes 2-3, indices in bytes 4..19.
@@ -436,8 +406,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 const uint32_t aa[4] = {nl_addr(nb, Cnt<0>{}), nl_addr(nb, Cnt<1>{}), nl_addr(nb, Cnt<2>{}),
                                         nl_addr(nb, Cnt<3>{})};
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * d2);
+                for (int p = 0; p < 4; ++p) F.f[sn][kk][p] = mul_pair(lds_ld(aa[p]), d2);
             } else {
                 // two 2-bit indices per table entry: chunk kk is bits 16 kk ..
                 // 16 kk + 15 of the 64-bit index word
@@ -639,33 +608,19 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // bytes.
     const int nk = g.K / BK;
     {
-        // 16-byte chunks: four copies of one entry each
-        for (int i = tid; i < kTabDw / 4; i += 256) {
+        // the Q3S quad table and the NL4 fold table (the down mode) are the
+        // shared decoders' (moe_decoders.hpp); the others: 16-byte chunks,
+        // four copies of one entry each
+        if constexpr (kQ3) q3_quad_table_fill(lut, tid, 256);
+        else if constexpr (kNL && !kNat) nl4_fold_table_fill(lut, tid, 256);
+        else for (int i = tid; i < kTabDw / 4; i += 256) {
             uint32_t v;
-            if constexpr (kQ3) {                           // chunk i: quad entries 2i, 2i + 1
-                u32x4 qv;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int en = 2 * i + h;
-                    qv[2 * h] = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[(en >> 3) & 7]));
-                    qv[2 * h + 1] = pack2(f32_to_f16_bits((float)kC3[(en >> 6) & 7]), f32_to_f16_bits((float)kC3[en >> 9]));
-                }
-                reinterpret_cast<u32x4*>(lut)[i] = qv;
-                continue;
-            }
             if (kQ3K) {
                 const int en = i >> 3;
                 v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
             } else if (kNat) {
                 const int en = i >> (kNLSh - 4);
                 v = pack2(f32_to_f16_bits((float)kT4[en & 15]), f32_to_f16_bits((float)kT4[en >> 4]));
-            } else if (kNL) {
-                // T4 / 8 (exact): the fragments hold 16 d T4 / 128, undone in
-                // the epilogue, so that d T4 / 128 stays in fp16's normal range
-                // for every normal d (|T4| >= 10) up to 4126
-                const int en = i >> (kNLSh - 4);
-                v = pack2(f32_to_f16_bits((float)kT4[en & 15] * 0.125f),
-                          f32_to_f16_bits((float)kT4[en >> 4] * 0.125f));
             } else {
                 const int en = (i >> 3) & 15;              // 16 entries; the rest repeats
                 const int lo = en & 3, hi = en >> 2;

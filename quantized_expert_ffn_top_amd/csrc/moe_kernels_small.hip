@@ -8,6 +8,7 @@
 // dropped ("Betelgeuse" post: every routed expert is computed).
 #include <type_traits>
 
+#include "moe_decoders.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -606,6 +607,91 @@ __global__ void __launch_bounds__(1024) k_combine_norm(const float* __restrict__
     norm_row<NV>(v, n4, H, gamma, eps, normed + (int64_t)t * H, s_red);
 }
 
+// ---------------------------------------------------------------- kernel-path dequant
+// Dequantization through the table decoders that the layer's kernels inline
+// (moe_decoders.hpp): the same table fill, the same lookup addresses, the
+// same fp16 multiply by the sub-scale (Q3S-256) or by d (the NL4-32 fold),
+// then the factor each kernel applies in fp32 afterwards (d / 128 on the
+// partial sums of a Q3S-256 block or of an NL4-32 block; the fold's 1 / 16).
+// One thread per 32 weights: a Q3S-256 sub-block (12 index bytes at 12 j,
+// the 8-byte tail at 96 of its block) or an NL4-32 block (18 bytes).
+enum { kDqpQ3Pair = 0, kDqpQ3Quad = 1, kDqpNl4Pair = 2, kDqpNl4Fold = 3 };
+
+// Weights 8 C .. 8 C + 7 of a sub-block from the pair table, times s.
+template <int C>
+__device__ __forceinline__ void q3_pair_decode8(const uint32_t* w, uint32_t base, f16x2_t s2, uint32_t (&f)[4]) {
+    f[0] = mul_pair(lds_ld(q3_pair_addr<24 * C + 0>(w, base)), s2);
+    f[1] = mul_pair(lds_ld(q3_pair_addr<24 * C + 6>(w, base)), s2);
+    f[2] = mul_pair(lds_ld(q3_pair_addr<24 * C + 12>(w, base)), s2);
+    f[3] = mul_pair(lds_ld(q3_pair_addr<24 * C + 18>(w, base)), s2);
+}
+
+template <int V>
+__global__ void __launch_bounds__(256) k_dequant_path(const uint8_t* __restrict__ blocks, int64_t n_units,
+                                                      float* __restrict__ out) {
+    constexpr bool kQ3 = V == kDqpQ3Pair || V == kDqpQ3Quad;
+    constexpr int kDw = V == kDqpQ3Pair ? kQ3LutDw : V == kDqpQ3Quad ? kQ3QuadDw : kNl4LutDw;
+    __shared__ __attribute__((aligned(32768))) uint32_t lut[kDw];
+    const int tid = threadIdx.x, lane = __lane_id();
+    if constexpr (V == kDqpQ3Pair) q3_pair_table_fill(lut, tid, 256);
+    else if constexpr (V == kDqpQ3Quad) q3_quad_table_fill(lut, tid, 256);
+    else if constexpr (V == kDqpNl4Pair) nl4_pair_table_fill(lut, tid, 256);
+    else nl4_fold_table_fill(lut, tid, 256);
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    if (i >= n_units) return;
+    float* o = out + i * 32;
+    uint32_t f[4][4];                                  // 4 groups of 8 weights, fp16 pairs
+    float scale;
+    if constexpr (kQ3) {
+        const uint8_t* b = blocks + (i >> 3) * kQ3Bytes;
+        const int j = (int)(i & 7);
+        const uint32_t* ip = reinterpret_cast<const uint32_t*>(b + 12 * j);
+        const uint32_t q[3] = {ip[0], ip[1], ip[2]};
+        const uint64_t tail = *reinterpret_cast<const uint64_t*>(b + 96);
+        const _Float16 s = (_Float16)(float)q3_tail_s(tail, j);
+        const f16x2_t s2 = {s, s};
+        scale = q3_tail_d(tail) * 0.0078125f;
+        if constexpr (V == kDqpQ3Pair) {
+            const uint32_t base = lut_copy_base(lds_addr(lut), lane);
+            q3_pair_decode8<0>(q, base, s2, f[0]);
+            q3_pair_decode8<1>(q, base, s2, f[1]);
+            q3_pair_decode8<2>(q, base, s2, f[2]);
+            q3_pair_decode8<3>(q, base, s2, f[3]);
+        } else {
+            const uint32_t base = lds_addr(lut);
+            q3_quad_decode8<0>(q, base, s2, f[0]);
+            q3_quad_decode8<1>(q, base, s2, f[1]);
+            q3_quad_decode8<2>(q, base, s2, f[2]);
+            q3_quad_decode8<3>(q, base, s2, f[3]);
+        }
+    } else {
+        // 18-byte blocks are 2-byte aligned: d and the index bytes as halves
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + i * kNL4Bytes);
+        const uint32_t dbits = h[0];
+        const uint32_t base = lut_copy_base(lds_addr(lut), lane);
+        const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
+        const f16x2_t d2 = {d, d};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t nb = (uint32_t)h[1 + 2 * c] | ((uint32_t)h[2 + 2 * c] << 16);
+            const uint32_t e[4] = {lds_ld(nl4_byte_addr<0>(nb, base)), lds_ld(nl4_byte_addr<1>(nb, base)),
+                                   lds_ld(nl4_byte_addr<2>(nb, base)), lds_ld(nl4_byte_addr<3>(nb, base))};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) f[c][p] = V == kDqpNl4Fold ? mul_pair(e[p], d2) : e[p];
+        }
+        scale = V == kDqpNl4Fold ? 0.0625f : f16_bits_to_f32(dbits) * 0.0078125f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const f16x2_t v = __builtin_bit_cast(f16x2_t, f[c][p]);
+            o[8 * c + 2 * p] = (float)v[0] * scale;
+            o[8 * c + 2 * p + 1] = (float)v[1] * scale;
+        }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
@@ -619,6 +705,19 @@ void launch_dequant(int fmt, const void* blocks, int64_t n_weights, float* out, 
     else if (fmt == kFmtQ3K256) k_dequant_q3k<<<cdiv(2 * n32, 256), 256, 0, st>>>(b, 2 * n32, out);
     else if (fmt == kFmtNL4S256) k_dequant_nl4s<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
     else k_dequant_q2<<<cdiv(n32, 256), 256, 0, st>>>(b, n32, out);
+}
+
+void launch_dequant_path(int fmt, int path, const void* blocks, int64_t n_weights, float* out, hipStream_t st) {
+    const int64_t n32 = n_weights / 32;
+    const uint8_t* b = (const uint8_t*)blocks;
+    const unsigned grid = cdiv(n32, 256);
+    if (fmt == kFmtQ3S256) {
+        if (path == 0) k_dequant_path<kDqpQ3Pair><<<grid, 256, 0, st>>>(b, n32, out);
+        else k_dequant_path<kDqpQ3Quad><<<grid, 256, 0, st>>>(b, n32, out);
+    } else {
+        if (path == 0) k_dequant_path<kDqpNl4Pair><<<grid, 256, 0, st>>>(b, n32, out);
+        else k_dequant_path<kDqpNl4Fold><<<grid, 256, 0, st>>>(b, n32, out);
+    }
 }
 
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st) {

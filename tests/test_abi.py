@@ -146,6 +146,11 @@ def test_stage_error_paths():
     assert lib.moe_dequantize(1, P, 256, P2, None) == 3
     assert lib.moe_dequantize(2, P, 100, P2, None) == 2
     assert lib.moe_dequantize(3, P + 8, 32, P2, None) == 4
+    assert lib.moe_dequantize_path(4, 0, P, 256, P2, None) == 3          # Q2S256: no kernel path
+    assert lib.moe_dequantize_path(2, 2, P, 256, P2, None) == 3          # no such path
+    assert lib.moe_dequantize_path(2, 1, P, 100, P2, None) == 2
+    assert lib.moe_dequantize_path(3, 0, P + 8, 32, P2, None) == 4
+    assert lib.moe_dequantize_path(3, 1, None, 32, P2, None) == 1
     assert lib.moe_rmsnorm_residual(P, None, P, 1e-6, 4, 256, None, None) == 1
     assert lib.moe_router_logits(P, 4, 250, 16, P, None, P2, P, 1 << 20, None) == 2
     assert lib.moe_router_logits(None, 4, 256, 16, P, None, P2, None, 0, None) == 1

@@ -166,6 +166,75 @@ def test_dequant_real_experts_bitexact(mode):
         assert np.array_equal(out2.cpu().numpy().view(np.uint32), ref2.view(np.uint32)), e
 
 
+# ---------------------------------------------------------------- the kernels' decoders
+# moe_dequantize_path decodes with the tables, lookup addresses and fp16
+# multiplies that the layer's kernels inline: the pair tables of the
+# bandwidth-path kernels, the quad table and the NL4 fold of the grouped GEMM.
+
+PATHS = [(Q.MOE_PATH_BANDWIDTH, "bandwidth"), (Q.MOE_PATH_GEMM, "gemm")]
+
+
+def _fold16(w):
+    """The grouped GEMM's NL4-32 down weights (its one rounding of weights):
+    16 w rounded once to binary16, round to nearest even, then / 16; w is the
+    oracle's exact value (16 w is exact in fp64)."""
+    with np.errstate(over="ignore"):
+        return (np.asarray(w, dtype=np.float64) * 16.0).astype(np.float16).astype(np.float32) * np.float32(0.0625)
+
+
+def _nl4_expected(w, path):
+    return _fold16(w) if path == Q.MOE_PATH_GEMM else np.asarray(w).astype(np.float32)
+
+
+def _path_dequant(fmt, path, src, n):
+    out = torch.empty(n, dtype=torch.float32, device=dev())
+    Q.moe_dequantize_path(fmt, path, src, n, out)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("path,name", PATHS, ids=[p[1] for p in PATHS])
+def test_kernel_decoders_hand_blocks_bitexact(path, name):
+    """Hand blocks through the kernels' decoders: d from the smallest subnormal
+    to the largest finite value, both signs; every sub-scale; every codebook
+    entry at every position."""
+    raw = _hand_q3s_blocks()
+    got = _path_dequant(Q.MOE_FMT_Q3S256, path, _u8(raw), raw.shape[0] * 256)
+    ref = OF.dequant_q3s(raw).reshape(-1).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+    blocks = []
+    for d_bits in (0x0001, 0x0155, 0x03FF, 0x0400, 0x1000, 0x3C00, 0x7BFF, 0xC000, 0x8001, 0x2800):
+        blocks.append(OF.pack_nl4_block(d_bits, list(range(16)) * 2))
+        blocks.append(OF.pack_nl4_block(d_bits, [15 - (i * 7) % 16 for i in range(32)]))
+    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, 18)
+    flat = raw.reshape(-1)
+    src = torch.zeros(((flat.size + 15) // 16) * 16, dtype=torch.uint8, device=dev())
+    src[:flat.size] = _u8(flat)
+    got = _path_dequant(Q.MOE_FMT_NL4_32, path, src, raw.shape[0] * 32)
+    ref = _nl4_expected(OF.dequant_nl4(raw).reshape(-1), path)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("mode", ["full", "wide", "small"])
+def test_kernel_decoders_real_experts_bitexact(mode):
+    """Every block of 8 real-shape experts (up|gate Q3S-256, down NL4-32) with
+    full-range fields (every sub-scale; d over four binades, subnormal or zero
+    included; or every d below 2^-11) through the decoders of both paths."""
+    sh = synth.REAL
+    nug = sh.upgate_bytes
+    for e in range(0, 512, 64):
+        rec_gpu = synth.expert_record(sh, 7, 0, e, device=dev(), mode=mode)
+        rec_cpu = synth.expert_record(sh, 7, 0, e, device="cpu", mode=mode).numpy()
+        assert np.array_equal(rec_gpu.cpu().numpy(), rec_cpu)
+        w_ug = OF.dequant_q3s(rec_cpu[:nug].reshape(-1, 104)).reshape(-1).astype(np.float32)
+        w_dn = OF.dequant_nl4(rec_cpu[nug:].reshape(-1, 18)).reshape(-1)
+        for path, name in PATHS:
+            got = _path_dequant(Q.MOE_FMT_Q3S256, path, rec_gpu[:nug], w_ug.size)
+            assert np.array_equal(got.view(np.uint32), w_ug.view(np.uint32)), (name, e)
+            got = _path_dequant(Q.MOE_FMT_NL4_32, path, rec_gpu[nug:], w_dn.size)
+            ref = _nl4_expected(w_dn, path)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (name, e)
+
+
 # ---------------------------------------------------------------- router
 
 @pytest.mark.parametrize("T,sh", [(1, synth.REAL), (3, synth.REAL), (8, synth.REAL), (16, synth.REAL),
