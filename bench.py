@@ -680,7 +680,7 @@ def counter_means(path, counter, count=False):
     return {k: (len(v) if count else sum(v) / len(v)) for k, v in out.items()}
 
 
-TRAFFIC_SOURCES = ["moe_common.hpp", "moe_kernels.hpp", "moe_kernels_decode.hip"]
+TRAFFIC_SOURCES = ["moe_common.hpp", "moe_decoders.hpp", "moe_kernels.hpp", "moe_kernels_decode.hip"]
 
 
 def write_traffic_json(fetch_csv, write_csv, cfetch_csv, cwrite_csv):

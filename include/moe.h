@@ -35,13 +35,15 @@
  *   - Element types: bf16 and fp16 are passed as uint16_t bit patterns.
  *   - Preconditions not checked on the device: expert ids given to
  *     moe_permute lie in [0, E) and are distinct within each token's row;
- *     logits are not NaN; weight scales d are finite; the activations x and
- *     the SwiGLU outputs a (below) satisfy |v| <= 65504.
+ *     logits are not NaN; weight scales d are finite, and |d| <= 32752 in
+ *     MOE_FMT_Q2_32 blocks (the grouped GEMM forms d (q - 2) in fp16); the
+ *     activations x and the SwiGLU outputs a (below) satisfy |v| <= 65504.
  *   - Numerics.  Accumulation is fp32 everywhere.  The matrix cores take x
  *     and a as fp16: a bf16 value v converts exactly when 2^-17 <= |v| <=
  *     65504 and with an absolute error <= 2^-25 below that (|v| > 65504
  *     would become inf).  Routed weights enter exactly (the quantized
- *     integers, with the scales applied in fp32 to partial sums), except the
+ *     integers, with the scales applied in fp32 to partial sums, or the
+ *     products d (q - 2) of Q2_32, exact in fp16 for |d| <= 32752), except the
  *     NL4_32 down weights of the grouped-GEMM path (T > 16 or the mixed
  *     formats), which enter as fp16_rne(16 d T4[q] / 128) / 16: relative
  *     error <= 2^-11 for every normal d up to 4126, absolute <= 2^-29 for a
@@ -295,18 +297,27 @@ moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, fl
  * multiplies, then the fp32 factor the kernel applies to its partial sums --
  * so that a bit-exact comparison covers the decoders of the hot path (model
  * card "Qwen3.8-Flash-Next - Avalon GGUF", "Files / Main model": the routed
- * up/gate type with a scale per 256-weight block and sub-scales per 32
- * weights, and the 4-bit non-linear down type).  fmt Q3S256 or NL4_32; path:
+ * up/gate types with a scale per 256-weight block and sub-scales, the 4-bit
+ * non-linear and 2-bit down types).  path:
  *   MOE_PATH_BANDWIDTH  the bandwidth-path kernels (T <= 16): Q3S256 from the
  *                       pair table (6-bit index -> two codebook values) times
- *                       s, then d/128; NL4_32 from its pair table, then d/128.
- *                       Exact: the values of moe_dequantize.
- *   MOE_PATH_GEMM       the grouped GEMM: Q3S256 from the quad table (12-bit
- *                       index -> four values) times s, then d/128 (exact);
- *                       NL4_32 as down weights, fp16_rne(16 d t / 128) / 16
- *                       (the one rounding the grouped GEMM applies to them).
- * Other formats or paths: MOE_ERR_FORMAT.  Blocks contiguous and 16-byte
- * aligned, n_weights a positive multiple of the block size; out fp32. */
+ *                       s, then d/128; NL4_32 from its pair table (index byte
+ *                       -> two values), then d/128 -- the decoder the grouped
+ *                       GEMM's NL4_32 up|gate mode runs too.  Exact.
+ *   MOE_PATH_GEMM       the grouped GEMM's down and up|gate modes: Q3S256 from
+ *                       the quad table (12-bit index -> four values) times s,
+ *                       then d/128; NL4_32 as down weights, fp16_rne(16 d t /
+ *                       128) / 16 (the one rounding that path applies to
+ *                       them); Q2S256 (nibble table times s, then d/128),
+ *                       Q2_32 (nibble table of q - 2 times d in fp16: exact
+ *                       for |d| <= 32752, +-inf for code 0 beyond), Q3K256 (pair
+ *                       table times the two exact parts of s, summed, then
+ *                       d/128), NL4S256 (the NL4 table in 16 copies, then
+ *                       d s/128).  Exact except the NL4_32 fold; a zero weight
+ *                       may carry either sign.
+ * Other formats (or Q2S256, Q2_32, Q3K256, NL4S256 on the bandwidth path):
+ * MOE_ERR_FORMAT.  Blocks contiguous and 16-byte aligned, n_weights a
+ * positive multiple of the block size; out fp32. */
 #define MOE_PATH_BANDWIDTH 0
 #define MOE_PATH_GEMM 1
 moe_status moe_dequantize_path(int32_t fmt, int32_t path, const void* blocks, int64_t n_weights,

@@ -616,10 +616,13 @@ moe_status moe_dequantize_path(int32_t fmt, int32_t path, const void* blocks, in
                                float* out, void* stream) {
     g_last_error.clear();
     if (!blocks || !out) return fail(MOE_ERR_NULL, "null argument");
-    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32)
-        return fail(MOE_ERR_FORMAT, "moe_dequantize_path supports Q3S256 and NL4_32");
     if (path != MOE_PATH_BANDWIDTH && path != MOE_PATH_GEMM)
         return fail(MOE_ERR_FORMAT, "path must be MOE_PATH_BANDWIDTH or MOE_PATH_GEMM");
+    if (path == MOE_PATH_BANDWIDTH && fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32)
+        return fail(MOE_ERR_FORMAT, "the bandwidth path decodes Q3S256 and NL4_32");
+    if (fmt != MOE_FMT_Q3S256 && fmt != MOE_FMT_NL4_32 && fmt != MOE_FMT_Q2S256 && fmt != MOE_FMT_Q2_32 &&
+        fmt != MOE_FMT_Q3K256 && fmt != MOE_FMT_NL4S256)
+        return fail(MOE_ERR_FORMAT, "moe_dequantize_path supports the six quantized formats");
     const int64_t unit = fmt_block_weights(fmt);
     if (n_weights < unit || n_weights % unit)
         return fail(MOE_ERR_SHAPE, "n_weights must be a positive multiple of the block size");

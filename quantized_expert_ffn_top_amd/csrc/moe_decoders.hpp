@@ -6,7 +6,8 @@
 //
 // Codecs: model card "Qwen3.8-Flash-Next - Avalon GGUF", "Files / Main model"
 // (routed up/gate at 3.25 bpw, a scale per 256-weight block and sub-scales
-// per 32 weights; routed down in the 4-bit non-linear 32-weight type).
+// per 32 weights; routed down in the 4-bit non-linear 32-weight type; the
+// other layers' 3.44-bpw, 2-bit and 4.25-bpw up/gate and 2-bit down types).
 #pragma once
 
 #include "moe_common.hpp"
@@ -123,20 +124,68 @@ __device__ __forceinline__ void q3_quad_decode8(const uint32_t (&q)[3], uint32_t
     f[3] = mul_pair(c1[1], s2);
 }
 
+// ---------------------------------------------------------------- Q3K-256 (3.44 bpw)
+// Grouped GEMM.  The Q3S pair table above, read with q3_pair_addr; s * c
+// (|s| <= 32) reaches 4064, past fp16's exact integers (2048), so a pair
+// enters as two exact fp16 parts, c (s mod 16) and c 16 floor(s / 16), summed
+// by two MFMAs; d / 128 goes on the block's fp32 partial sums.
+__device__ __forceinline__ void q3k_split(int s, f16x2_t& lo2, f16x2_t& hi2) {
+    const _Float16 lo = (_Float16)(float)(s & 15), hi = (_Float16)(float)(16 * (s >> 4));
+    lo2 = f16x2_t{lo, lo};
+    hi2 = f16x2_t{hi, hi};
+}
+
+// ---------------------------------------------------------------- 2-bit nibble tables
+// Grouped GEMM, the 2-bit codecs.  Entry v (4 bits: two 2-bit codes, the
+// first in the low bits) = two fp16 values, in 32 copies (byte address
+// v*128 + c*4), filled over 8 KB (entries 16..63 repeat the first 16 and are
+// never read).  Q2S-256: (C2[lo], C2[hi]), times the sub-scale s, then d /
+// 128 on the block's partial sums.  Q2-32: (lo - 2, hi - 2), times d (exact
+// in fp16).
+constexpr uint32_t kC2Bytes = 0x7F360081u;       // C2 = (-127, 0, 54, 127), entry q in byte q
+constexpr int kNibLutDw = 2048;
+
+__device__ __forceinline__ float c2_entry(int q) {
+    return (float)(int8_t)(uint8_t)(kC2Bytes >> (8 * q));
+}
+template <bool Q2S>
+__device__ __forceinline__ void nib_table_fill(uint32_t* lut, int tid, int nt) {
+    for (int i = tid; i < kNibLutDw / 4; i += nt) {
+        const int en = (i >> 3) & 15;
+        const int lo = en & 3, hi = en >> 2;
+        const uint32_t v = Q2S ? pack2(f32_to_f16_bits(c2_entry(lo)), f32_to_f16_bits(c2_entry(hi)))
+                               : pack2(f32_to_f16_bits((float)(lo - 2)), f32_to_f16_bits((float)(hi - 2)));
+        reinterpret_cast<u32x4*>(lut)[i] = u32x4{v, v, v, v};
+    }
+}
+// LDS address of the entry for the 4-bit field at bit P of a 64-bit index
+// word (two 2-bit codes): the field lands at address bits 7..10, or-ed onto
+// cb.
+template <int P> __device__ __forceinline__ uint32_t nib_lut_addr(const uint32_t (&q)[2], uint32_t cb) {
+    constexpr int w = P >> 5, b = P & 31;
+    uint32_t x;
+    if constexpr (b >= 7) x = q[w] >> (b - 7);
+    else x = q[w] << (7 - b);
+    return (x & 0x780u) | cb;
+}
+
 // ---------------------------------------------------------------- NL4-32 byte tables
 // Entry v = the two weights of one index byte (even weight in the low
 // nibble) as fp16, in 32 copies (copy = lane & 31): byte address v*128 + c*4.
-// 32 KB, 32 KB-aligned.  Bandwidth-path down: (T4[v & 15], T4[v >> 4]), d / 128
-// applied in fp32 to the partial sums.  Grouped-GEMM down (the fold):
+// 32 KB, 32 KB-aligned.  Bandwidth-path down and grouped-GEMM NL4-32 up|gate:
+// (T4[v & 15], T4[v >> 4]), d / 128 applied in fp32 to the partial sums (the
+// NL4S-256 up|gate the same table in 16 copies, d s / 128 per sub-block).  Grouped-GEMM down (the fold):
 // (T4[lo] / 8, T4[hi] / 8) (exact), multiplied by d in fp16, so that a
 // fragment holds fp16_rne(16 d T4 / 128) (one rounding; the factor 16 keeps
 // the small entries of small-d blocks out of fp16's subnormals) and the
 // epilogue divides by 16.
 constexpr int kNl4LutDw = 256 * 32;
 
+// (COPIES = 16: the NL4S-256 up|gate table, 16 KB, byte address v*64 + c*4.)
+template <int COPIES = 32>   // 32 or 16
 __device__ __forceinline__ void nl4_pair_table_fill(uint32_t* lut, int tid, int nt) {
-    for (int i = tid; i < kNl4LutDw / 4; i += nt) {          // 16-byte chunk i: 8 per entry
-        const int v = i >> 3;
+    for (int i = tid; i < 256 * COPIES / 4; i += nt) {        // 16-byte chunk i: COPIES / 4 per entry
+        const int v = i >> (COPIES == 32 ? 3 : 2);
         const uint32_t val = pack2(f32_to_f16_bits(t4_entry(v & 15)), f32_to_f16_bits(t4_entry(v >> 4)));
         reinterpret_cast<u32x4*>(lut)[i] = u32x4{val, val, val, val};
     }

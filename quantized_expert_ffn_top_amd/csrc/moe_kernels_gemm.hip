@@ -98,16 +98,6 @@ struct GemmArgs {
 // that 16 consecutive rows read at one chunk hit 16 distinct bank groups.
 __device__ __forceinline__ int aslot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-// LDS address of the nibble-table entry for the 4-bit field at bit P of a
-// 64-bit index word (two 2-bit indices): the field lands at address bits
-// 7..10, ORed into cb.
-template <int P> __device__ __forceinline__ uint32_t nib_lut_addr(const uint32_t (&q)[2], uint32_t cb) {
-    constexpr int w = P >> 5, b = P & 31;
-    uint32_t x;
-    if constexpr (b >= 7) x = q[w] >> (b - 7);
-    else x = q[w] << (7 - b);
-    return (x & 0x780u) | cb;
-}
 template <int MODE>
 __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     constexpr int kBF = bfmt<MODE>();
@@ -430,8 +420,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                 const uint32_t aa[4] = {nib_lut_addr<16 * kk + 0>(ix, cb), nib_lut_addr<16 * kk + 4>(ix, cb),
                                         nib_lut_addr<16 * kk + 8>(ix, cb), nib_lut_addr<16 * kk + 12>(ix, cb)};
 #pragma unroll
-                for (int p = 0; p < 4; ++p)               // exact: small integers times m
-                    F.f[sn][kk][p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, lds_ld(aa[p])) * m2);
+                for (int p = 0; p < 4; ++p) F.f[sn][kk][p] = mul_pair(lds_ld(aa[p]), m2);   // exact: small integers times m
             }
         }
     };
@@ -608,27 +597,13 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
     // bytes.
     const int nk = g.K / BK;
     {
-        // the Q3S quad table and the NL4 fold table (the down mode) are the
-        // shared decoders' (moe_decoders.hpp); the others: 16-byte chunks,
-        // four copies of one entry each
+        // the decode tables (moe_decoders.hpp)
         if constexpr (kQ3) q3_quad_table_fill(lut, tid, 256);
-        else if constexpr (kNL && !kNat) nl4_fold_table_fill(lut, tid, 256);
-        else for (int i = tid; i < kTabDw / 4; i += 256) {
-            uint32_t v;
-            if (kQ3K) {
-                const int en = i >> 3;
-                v = pack2(f32_to_f16_bits((float)kC3[en & 7]), f32_to_f16_bits((float)kC3[en >> 3]));
-            } else if (kNat) {
-                const int en = i >> (kNLSh - 4);
-                v = pack2(f32_to_f16_bits((float)kT4[en & 15]), f32_to_f16_bits((float)kT4[en >> 4]));
-            } else {
-                const int en = (i >> 3) & 15;              // 16 entries; the rest repeats
-                const int lo = en & 3, hi = en >> 2;
-                if (kBF == BF_Q2S) v = pack2(f32_to_f16_bits((float)kC2[lo]), f32_to_f16_bits((float)kC2[hi]));
-                else v = pack2(f32_to_f16_bits((float)(lo - 2)), f32_to_f16_bits((float)(hi - 2)));
-            }
-            reinterpret_cast<u32x4*>(lut)[i] = u32x4{v, v, v, v};
-        }
+        else if constexpr (kQ3K) q3_pair_table_fill(lut, tid, 256);
+        else if constexpr (kNLS) nl4_pair_table_fill<16>(lut, tid, 256);
+        else if constexpr (kNat) nl4_pair_table_fill<32>(lut, tid, 256);
+        else if constexpr (kNL) nl4_fold_table_fill(lut, tid, 256);
+        else nib_table_fill<kBF == BF_Q2S>(lut, tid, 256);
     }
     RawA A0, A1;
     load_a(0, A0);
@@ -783,19 +758,19 @@ __global__ void __launch_bounds__(256, 2) k_gemm(GemmArgs g) {
                         const uint32_t f = fq[sn][kk];
                         // a plain array: clang lowers __builtin_bit_cast of an
                         // ext_vector element as a read of element 0
+                        const uint32_t fw[1] = {f};
                         uint32_t fb[4];
-                        fb[0] = lds_ld(((f << 7) & 0x1F80u) | cb);
-                        fb[1] = lds_ld(((f << 1) & 0x1F80u) | cb);
-                        fb[2] = lds_ld(((f >> 5) & 0x1F80u) | cb);
-                        fb[3] = lds_ld(((f >> 11) & 0x1F80u) | cb);
-                        const int sv = sext6(f24[sn] >> (6 * kk));
-                        const _Float16 slo = (_Float16)(float)(sv & 15), shi = (_Float16)(float)(16 * (sv >> 4));
-                        const h2g slo2 = {slo, slo}, shi2 = {shi, shi};
+                        fb[0] = lds_ld(q3_pair_addr<0>(fw, cb));
+                        fb[1] = lds_ld(q3_pair_addr<6>(fw, cb));
+                        fb[2] = lds_ld(q3_pair_addr<12>(fw, cb));
+                        fb[3] = lds_ld(q3_pair_addr<18>(fw, cb));
+                        f16x2_t slo2, shi2;
+                        q3k_split(sext6(f24[sn] >> (6 * kk)), slo2, shi2);
                         u32x4 b1, b2;
 #pragma unroll
                         for (int pq = 0; pq < 4; ++pq) {
-                            b1[pq] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, fb[pq]) * slo2);
-                            b2[pq] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2g, fb[pq]) * shi2);
+                            b1[pq] = mul_pair(fb[pq], slo2);
+                            b2[pq] = mul_pair(fb[pq], shi2);
                         }
 #pragma unroll
                         for (int sm = 0; sm < SM; ++sm) {

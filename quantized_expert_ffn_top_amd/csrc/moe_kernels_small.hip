@@ -610,14 +610,15 @@ __global__ void __launch_bounds__(1024) k_combine_norm(const float* __restrict__
 // ---------------------------------------------------------------- kernel-path dequant
 // Dequantization through the table decoders that the layer's kernels inline
 // (moe_decoders.hpp): the same table fill, the same lookup addresses, the
-// same fp16 multiply by the sub-scale (Q3S-256) or by d (the NL4-32 fold),
-// then the factor each kernel applies in fp32 afterwards (d / 128 on the
-// partial sums of a Q3S-256 block or of an NL4-32 block; the fold's 1 / 16).
-// One thread per 32 weights: a Q3S-256 sub-block (12 index bytes at 12 j,
-// the 8-byte tail at 96 of its block) or an NL4-32 block (18 bytes).
-enum { kDqpQ3Pair = 0, kDqpQ3Quad = 1, kDqpNl4Pair = 2, kDqpNl4Fold = 3 };
+// same fp16 multiply by the sub-scale or by d, then the factor each kernel
+// applies in fp32 afterwards (d / 128, or d s / 128, on the partial sums of a
+// block or sub-block; the NL4 fold's 1 / 16).  One thread per 32 weights:
+// a 32-weight sub-block (Q3S-256, Q2S-256, NL4S-256), a 32-weight block
+// (NL4-32, Q2-32) or two 16-weight sub-blocks (Q3K-256), read from the block
+// bytes as the format lays them out.
+enum { kDqpQ3Pair, kDqpQ3Quad, kDqpNl4Pair, kDqpNl4Fold, kDqpQ2S, kDqpQ2, kDqpQ3K, kDqpNl4S };
 
-// Weights 8 C .. 8 C + 7 of a sub-block from the pair table, times s.
+// Weights 8 C .. 8 C + 7 of a Q3S sub-block from the pair table, times s.
 template <int C>
 __device__ __forceinline__ void q3_pair_decode8(const uint32_t* w, uint32_t base, f16x2_t s2, uint32_t (&f)[4]) {
     f[0] = mul_pair(lds_ld(q3_pair_addr<24 * C + 0>(w, base)), s2);
@@ -625,25 +626,51 @@ __device__ __forceinline__ void q3_pair_decode8(const uint32_t* w, uint32_t base
     f[2] = mul_pair(lds_ld(q3_pair_addr<24 * C + 12>(w, base)), s2);
     f[3] = mul_pair(lds_ld(q3_pair_addr<24 * C + 18>(w, base)), s2);
 }
+// Weights 8 C .. 8 C + 7 of a 2-bit index word pair from the nibble table, times m.
+template <int C>
+__device__ __forceinline__ void nib_decode8(const uint32_t (&ix)[2], uint32_t base, f16x2_t m2, uint32_t (&f)[4]) {
+    f[0] = mul_pair(lds_ld(nib_lut_addr<16 * C + 0>(ix, base)), m2);
+    f[1] = mul_pair(lds_ld(nib_lut_addr<16 * C + 4>(ix, base)), m2);
+    f[2] = mul_pair(lds_ld(nib_lut_addr<16 * C + 8>(ix, base)), m2);
+    f[3] = mul_pair(lds_ld(nib_lut_addr<16 * C + 12>(ix, base)), m2);
+}
+// The four pairs of one index word nb (8 NL4 weights), table entries SH apart.
+template <int SH>
+__device__ __forceinline__ void nl4_read8(uint32_t nb, uint32_t base, uint32_t (&f)[4]) {
+    f[0] = lds_ld(nl4_byte_addr<0, SH>(nb, base));
+    f[1] = lds_ld(nl4_byte_addr<1, SH>(nb, base));
+    f[2] = lds_ld(nl4_byte_addr<2, SH>(nb, base));
+    f[3] = lds_ld(nl4_byte_addr<3, SH>(nb, base));
+}
+// Sign-extended 6-bit field at bit b of a 96-bit little-endian string.
+__device__ __forceinline__ int field6(const uint32_t (&w)[3], int b) {
+    const int wd = b >> 5, o = b & 31;
+    uint32_t v = w[wd] >> o;
+    if (o > 26) v |= w[wd + 1] << (32 - o);
+    return sext6(v & 63u);
+}
 
 template <int V>
 __global__ void __launch_bounds__(256) k_dequant_path(const uint8_t* __restrict__ blocks, int64_t n_units,
                                                       float* __restrict__ out) {
-    constexpr bool kQ3 = V == kDqpQ3Pair || V == kDqpQ3Quad;
-    constexpr int kDw = V == kDqpQ3Pair ? kQ3LutDw : V == kDqpQ3Quad ? kQ3QuadDw : kNl4LutDw;
+    constexpr int kDw = (V == kDqpQ3Pair || V == kDqpQ3K) ? kQ3LutDw : V == kDqpQ3Quad ? kQ3QuadDw
+                        : (V == kDqpNl4Pair || V == kDqpNl4Fold) ? kNl4LutDw : V == kDqpNl4S ? 256 * 16 : kNibLutDw;
     __shared__ __attribute__((aligned(32768))) uint32_t lut[kDw];
     const int tid = threadIdx.x, lane = __lane_id();
-    if constexpr (V == kDqpQ3Pair) q3_pair_table_fill(lut, tid, 256);
+    if constexpr (V == kDqpQ3Pair || V == kDqpQ3K) q3_pair_table_fill(lut, tid, 256);
     else if constexpr (V == kDqpQ3Quad) q3_quad_table_fill(lut, tid, 256);
-    else if constexpr (V == kDqpNl4Pair) nl4_pair_table_fill(lut, tid, 256);
-    else nl4_fold_table_fill(lut, tid, 256);
+    else if constexpr (V == kDqpNl4Pair) nl4_pair_table_fill<32>(lut, tid, 256);
+    else if constexpr (V == kDqpNl4Fold) nl4_fold_table_fill(lut, tid, 256);
+    else if constexpr (V == kDqpNl4S) nl4_pair_table_fill<16>(lut, tid, 256);
+    else nib_table_fill<V == kDqpQ2S>(lut, tid, 256);
     __syncthreads();
     const int64_t i = (int64_t)blockIdx.x * 256 + tid;
     if (i >= n_units) return;
     float* o = out + i * 32;
-    uint32_t f[4][4];                                  // 4 groups of 8 weights, fp16 pairs
+    const uint32_t base32 = lut_copy_base(lds_addr(lut), lane);
+    uint32_t f[4][4];                                  // 4 groups of 8 weights as fp16 pairs
     float scale;
-    if constexpr (kQ3) {
+    if constexpr (V == kDqpQ3Pair || V == kDqpQ3Quad) {
         const uint8_t* b = blocks + (i >> 3) * kQ3Bytes;
         const int j = (int)(i & 7);
         const uint32_t* ip = reinterpret_cast<const uint32_t*>(b + 12 * j);
@@ -653,11 +680,10 @@ __global__ void __launch_bounds__(256) k_dequant_path(const uint8_t* __restrict_
         const f16x2_t s2 = {s, s};
         scale = q3_tail_d(tail) * 0.0078125f;
         if constexpr (V == kDqpQ3Pair) {
-            const uint32_t base = lut_copy_base(lds_addr(lut), lane);
-            q3_pair_decode8<0>(q, base, s2, f[0]);
-            q3_pair_decode8<1>(q, base, s2, f[1]);
-            q3_pair_decode8<2>(q, base, s2, f[2]);
-            q3_pair_decode8<3>(q, base, s2, f[3]);
+            q3_pair_decode8<0>(q, base32, s2, f[0]);
+            q3_pair_decode8<1>(q, base32, s2, f[1]);
+            q3_pair_decode8<2>(q, base32, s2, f[2]);
+            q3_pair_decode8<3>(q, base32, s2, f[3]);
         } else {
             const uint32_t base = lds_addr(lut);
             q3_quad_decode8<0>(q, base, s2, f[0]);
@@ -665,22 +691,89 @@ __global__ void __launch_bounds__(256) k_dequant_path(const uint8_t* __restrict_
             q3_quad_decode8<2>(q, base, s2, f[2]);
             q3_quad_decode8<3>(q, base, s2, f[3]);
         }
-    } else {
+    } else if constexpr (V == kDqpNl4Pair || V == kDqpNl4Fold) {
         // 18-byte blocks are 2-byte aligned: d and the index bytes as halves
         const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + i * kNL4Bytes);
         const uint32_t dbits = h[0];
-        const uint32_t base = lut_copy_base(lds_addr(lut), lane);
         const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)dbits);
         const f16x2_t d2 = {d, d};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t nb = (uint32_t)h[1 + 2 * c] | ((uint32_t)h[2 + 2 * c] << 16);
-            const uint32_t e[4] = {lds_ld(nl4_byte_addr<0>(nb, base)), lds_ld(nl4_byte_addr<1>(nb, base)),
-                                   lds_ld(nl4_byte_addr<2>(nb, base)), lds_ld(nl4_byte_addr<3>(nb, base))};
+            nl4_read8<7>((uint32_t)h[1 + 2 * c] | ((uint32_t)h[2 + 2 * c] << 16), base32, f[c]);
+            if constexpr (V == kDqpNl4Fold) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) f[c][p] = V == kDqpNl4Fold ? mul_pair(e[p], d2) : e[p];
+                for (int p = 0; p < 4; ++p) f[c][p] = mul_pair(f[c][p], d2);
+            }
         }
         scale = V == kDqpNl4Fold ? 0.0625f : f16_bits_to_f32(dbits) * 0.0078125f;
+    } else if constexpr (V == kDqpQ2S) {
+        const uint8_t* b = blocks + (i >> 3) * kQ2SBytes;
+        const int j = (int)(i & 7);
+        const uint32_t* ip = reinterpret_cast<const uint32_t*>(b + 8 * j);
+        const uint32_t ix[2] = {ip[0], ip[1]};
+        const uint64_t tail = *reinterpret_cast<const uint64_t*>(b + 64);
+        const _Float16 s = (_Float16)(float)q3_tail_s(tail, j);
+        const f16x2_t s2 = {s, s};
+        scale = q3_tail_d(tail) * 0.0078125f;
+        nib_decode8<0>(ix, base32, s2, f[0]);
+        nib_decode8<1>(ix, base32, s2, f[1]);
+        nib_decode8<2>(ix, base32, s2, f[2]);
+        nib_decode8<3>(ix, base32, s2, f[3]);
+    } else if constexpr (V == kDqpQ2) {
+        // 10-byte blocks are 2-byte aligned
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + i * kQ2Bytes);
+        const _Float16 d = __builtin_bit_cast(_Float16, h[0]);
+        const f16x2_t d2 = {d, d};
+        const uint32_t ix[2] = {(uint32_t)h[1] | ((uint32_t)h[2] << 16), (uint32_t)h[3] | ((uint32_t)h[4] << 16)};
+        scale = 1.0f;
+        nib_decode8<0>(ix, base32, d2, f[0]);
+        nib_decode8<1>(ix, base32, d2, f[1]);
+        nib_decode8<2>(ix, base32, d2, f[2]);
+        nib_decode8<3>(ix, base32, d2, f[3]);
+    } else if constexpr (V == kDqpQ3K) {
+        // 110-byte blocks are 2-byte aligned: read as halves.  This thread's
+        // sub-blocks j0, j0 + 1 (16 weights, 6 index bytes at 6 j each), d at
+        // byte 96, the 6-bit sub-scales at bits 6 j of the 96-bit field at 98
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(blocks + (i >> 3) * kQ3KBytes);
+        const int j0 = 2 * (int)(i & 7);
+        const float dl = f16_bits_to_f32(h[48]) * 0.0078125f;
+        const uint32_t sw[3] = {(uint32_t)h[49] | ((uint32_t)h[50] << 16), (uint32_t)h[51] | ((uint32_t)h[52] << 16),
+                                (uint32_t)h[53] | ((uint32_t)h[54] << 16)};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = j0 + u;
+            const uint64_t w48 = (uint64_t)h[3 * j] | ((uint64_t)h[3 * j + 1] << 16) | ((uint64_t)h[3 * j + 2] << 32);
+            f16x2_t lo2, hi2;
+            q3k_split(field6(sw, 6 * j), lo2, hi2);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const uint32_t fw[1] = {(uint32_t)(w48 >> (24 * g)) & 0xFFFFFFu};
+                const uint32_t fb[4] = {lds_ld(q3_pair_addr<0>(fw, base32)), lds_ld(q3_pair_addr<6>(fw, base32)),
+                                        lds_ld(q3_pair_addr<12>(fw, base32)), lds_ld(q3_pair_addr<18>(fw, base32))};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    // the two exact parts, as the two MFMAs sum them, then d / 128
+                    const f16x2_t b1 = __builtin_bit_cast(f16x2_t, mul_pair(fb[p], lo2));
+                    const f16x2_t b2 = __builtin_bit_cast(f16x2_t, mul_pair(fb[p], hi2));
+                    o[16 * u + 8 * g + 2 * p] = ((float)b1[0] + (float)b2[0]) * dl;
+                    o[16 * u + 8 * g + 2 * p + 1] = ((float)b1[1] + (float)b2[1]) * dl;
+                }
+            }
+        }
+        return;
+    } else {
+        // NL4S-256: 136-byte blocks, 8-byte aligned; sub-block j's 16 index
+        // bytes at 16 j, d at 128, the 6-bit sub-scales at bits 6 j of the
+        // 48-bit field at 130; table in 16 copies
+        const uint8_t* b = blocks + (i >> 3) * kNL4SBytes;
+        const int j = (int)(i & 7);
+        const uint32_t* ip = reinterpret_cast<const uint32_t*>(b + 16 * j);
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(b);
+        const uint32_t sw[3] = {(uint32_t)h[65] | ((uint32_t)h[66] << 16), (uint32_t)h[67], 0u};
+        scale = f16_bits_to_f32(h[64]) * 0.0078125f * (float)field6(sw, 6 * j);
+        const uint32_t base16 = lds_addr(lut) + (uint32_t)(lane & 15) * 4u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nl4_read8<6>(ip[c], base16, f[c]);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -711,13 +804,23 @@ void launch_dequant_path(int fmt, int path, const void* blocks, int64_t n_weight
     const int64_t n32 = n_weights / 32;
     const uint8_t* b = (const uint8_t*)blocks;
     const unsigned grid = cdiv(n32, 256);
+#define MOE_DQP(V) k_dequant_path<V><<<grid, 256, 0, st>>>(b, n32, out)
     if (fmt == kFmtQ3S256) {
-        if (path == 0) k_dequant_path<kDqpQ3Pair><<<grid, 256, 0, st>>>(b, n32, out);
-        else k_dequant_path<kDqpQ3Quad><<<grid, 256, 0, st>>>(b, n32, out);
+        if (path == 0) MOE_DQP(kDqpQ3Pair);
+        else MOE_DQP(kDqpQ3Quad);
+    } else if (fmt == kFmtNL4) {
+        if (path == 0) MOE_DQP(kDqpNl4Pair);
+        else MOE_DQP(kDqpNl4Fold);
+    } else if (fmt == kFmtQ2S256) {
+        MOE_DQP(kDqpQ2S);
+    } else if (fmt == kFmtQ2) {
+        MOE_DQP(kDqpQ2);
+    } else if (fmt == kFmtQ3K256) {
+        MOE_DQP(kDqpQ3K);
     } else {
-        if (path == 0) k_dequant_path<kDqpNl4Pair><<<grid, 256, 0, st>>>(b, n32, out);
-        else k_dequant_path<kDqpNl4Fold><<<grid, 256, 0, st>>>(b, n32, out);
+        MOE_DQP(kDqpNl4S);
     }
+#undef MOE_DQP
 }
 
 void launch_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t st) {

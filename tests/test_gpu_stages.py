@@ -235,6 +235,102 @@ def test_kernel_decoders_real_experts_bitexact(mode):
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (name, e)
 
 
+def _hand_blocks(fmt):
+    """Hand blocks of the other formats: d from the smallest subnormal to the
+    largest finite value, both signs; every sub-scale at every position;
+    every codebook entry."""
+    blocks = []
+    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
+        if fmt == Q.MOE_FMT_Q2S256:
+            for s in ([-8, -1, 0, 1, 7, 2, -3, 5], [7] * 8, [-8] * 8):
+                blocks.append(OF.pack_q2s_block(d_bits, s, [i % 4 for i in range(256)]))
+                blocks.append(OF.pack_q2s_block(d_bits, s, [3 - (i * 3) % 4 for i in range(256)]))
+        elif fmt == Q.MOE_FMT_Q2_32:
+            blocks.append(OF.pack_q2_block(d_bits, [i % 4 for i in range(32)]))
+            blocks.append(OF.pack_q2_block(d_bits, [3 - (i * 3) % 4 for i in range(32)]))
+        elif fmt == Q.MOE_FMT_Q3K256:
+            for base in (-32, -16, 0, 16):
+                s = [base + j for j in range(16)]
+                blocks.append(OF.pack_q3k_block(d_bits, s, [i % 8 for i in range(256)]))
+                blocks.append(OF.pack_q3k_block(d_bits, s[::-1], [7 - (i * 5) % 8 for i in range(256)]))
+        else:
+            for base in range(-32, 32, 8):
+                s = [base + j for j in range(8)]
+                blocks.append(OF.pack_nl4s_block(d_bits, s, [i % 16 for i in range(256)]))
+                blocks.append(OF.pack_nl4s_block(d_bits, s[::-1], [15 - (i * 7) % 16 for i in range(256)]))
+    return np.frombuffer(b"".join(blocks), dtype=np.uint8)
+
+
+def _padded(flat):
+    src = torch.zeros(((flat.size + 15) // 16) * 16, dtype=torch.uint8, device=dev())
+    src[:flat.size] = _u8(flat)
+    return src
+
+
+def _same(got, ref, fmt):
+    """Bit for bit; for Q3K-256 value for value (its two exact parts are
+    summed, so a zero weight can be +0 where the oracle's product is -0)."""
+    if fmt == Q.MOE_FMT_Q3K256:
+        return np.array_equal(got, ref) and not np.isnan(got).any()
+    return np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+MIXED_FMTS = [Q.MOE_FMT_Q2S256, Q.MOE_FMT_Q2_32, Q.MOE_FMT_Q3K256, Q.MOE_FMT_NL4S256]
+
+
+def _q2_fp16(w):
+    """The grouped GEMM's Q2-32 fragments: d (q - 2) formed in fp16, i.e. the
+    exact value rounded once to binary16 (equal to it for |d| <= 32752, the
+    stated bound; +-inf for code 0 beyond)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(w, dtype=np.float64).astype(np.float16).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", MIXED_FMTS, ids=["q2s", "q2", "q3k", "nl4s"])
+def test_kernel_decoders_mixed_hand_blocks(fmt):
+    """The grouped GEMM's decoders of the mixed-format and draft-head codecs
+    on hand blocks, against the oracle's exact values."""
+    flat = _hand_blocks(fmt)
+    n = flat.size // OF.CODECS[fmt][1] * OF.CODECS[fmt][0]
+    got = _path_dequant(fmt, Q.MOE_PATH_GEMM, _padded(flat), n)
+    w = OF.dequant_matrix(fmt, flat, 1, n).reshape(-1)
+    ref = _q2_fp16(w) if fmt == Q.MOE_FMT_Q2_32 else w.astype(np.float32)
+    assert _same(got, ref, fmt)
+    if fmt == Q.MOE_FMT_Q2_32:
+        # within the stated bound |d| <= 32752 the fragments are the exact values
+        inb = np.abs(w) <= 65504
+        assert np.array_equal(got[inb].view(np.uint32), w[inb].astype(np.float32).view(np.uint32))
+        assert np.isinf(got[~inb]).all() and (~inb).any()
+
+
+@pytest.mark.parametrize("ug,dn,mode", [(synth.FMT_Q2S256, synth.FMT_Q2_32, "full"),
+                                        (synth.FMT_NL4_32, synth.FMT_NL4_32, "wide"),
+                                        (synth.FMT_Q3K256, synth.FMT_NL4_32, "wide"),
+                                        (synth.FMT_Q3K256, synth.FMT_Q2_32, "small"),
+                                        (synth.FMT_NL4S256, synth.FMT_NL4_32, "small"),
+                                        (synth.FMT_NL4S256, synth.FMT_Q2_32, "full")])
+def test_kernel_decoders_mixed_experts(ug, dn, mode):
+    """Records of the mixed-format layers at real shape (every block of 4
+    experts) through the decoders their grouped-GEMM modes run: NL4-32 up|gate
+    through the pair table it shares with the bandwidth path's down kernel,
+    NL4-32 down through the fold, the others exact."""
+    sh = synth.Shape(3072, 512, 512, 10, 512, ug, dn)
+    nug = sh.upgate_bytes
+    for e in range(0, 512, 128):
+        rec_gpu = synth.expert_record(sh, 9, 2, e, device=dev(), mode=mode)
+        rec_cpu = synth.expert_record(sh, 9, 2, e, device="cpu", mode=mode).numpy()
+        assert np.array_equal(rec_gpu.cpu().numpy(), rec_cpu)
+        for fmt, lo, hi, n, path in (
+                (ug, 0, nug, 2 * sh.inter * sh.hidden,
+                 Q.MOE_PATH_BANDWIDTH if ug == synth.FMT_NL4_32 else Q.MOE_PATH_GEMM),
+                (dn, nug, sh.expert_bytes, sh.hidden * sh.inter, Q.MOE_PATH_GEMM)):
+            got = _path_dequant(fmt, path, _padded(rec_cpu[lo:hi]), n)
+            w = OF.dequant_matrix(fmt, rec_cpu[lo:hi], 1, n).reshape(-1)
+            ref = (_fold16(w) if (fmt == synth.FMT_NL4_32 and path == Q.MOE_PATH_GEMM)
+                   else _q2_fp16(w) if fmt == synth.FMT_Q2_32 else w.astype(np.float32))
+            assert _same(got, ref, fmt), (fmt, path, e)
+
+
 # ---------------------------------------------------------------- router
 
 @pytest.mark.parametrize("T,sh", [(1, synth.REAL), (3, synth.REAL), (8, synth.REAL), (16, synth.REAL),
