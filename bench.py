@@ -145,7 +145,7 @@ def main():
         write_traffic_json(*args.traffic_json)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); "
+        print("bench.py measures one GPU only (the library has no multi-GPU path); "
               "got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

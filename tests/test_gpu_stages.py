@@ -54,12 +54,7 @@ def test_dequant_nl4_hand_blocks_bitexact():
 
 
 def test_dequant_q2s_hand_blocks_bitexact():
-    blocks = []
-    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
-        for s in ([-8, -1, 0, 1, 7, 2, -3, 5], [7] * 8, [-8] * 8):
-            blocks.append(OF.pack_q2s_block(d_bits, s, [i % 4 for i in range(256)]))
-            blocks.append(OF.pack_q2s_block(d_bits, s, [3 - (i * 3) % 4 for i in range(256)]))
-    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, 80)
+    raw = _hand_blocks(Q.MOE_FMT_Q2S256).reshape(-1, 80)
     out = torch.empty(raw.shape[0] * 256, dtype=torch.float32, device=dev())
     Q.moe_dequantize(Q.MOE_FMT_Q2S256, _u8(raw), raw.shape[0] * 256, out)
     ref = OF.dequant_q2s(raw).reshape(-1).astype(np.float32)
@@ -67,16 +62,10 @@ def test_dequant_q2s_hand_blocks_bitexact():
 
 
 def test_dequant_q2_hand_blocks_bitexact():
-    blocks = []
-    for d_bits in (0x0001, 0x03FF, 0x3C00, 0x7BFF, 0xC000, 0x2400):
-        blocks.append(OF.pack_q2_block(d_bits, [i % 4 for i in range(32)]))
-        blocks.append(OF.pack_q2_block(d_bits, [3 - (i * 3) % 4 for i in range(32)]))
-    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, 10)
-    # 12 blocks = 120 bytes: pad the device copy to a 16-byte multiple
-    dev_raw = torch.zeros(128, dtype=torch.uint8, device=dev())
-    dev_raw[:120] = _u8(raw.reshape(-1))
+    raw = _hand_blocks(Q.MOE_FMT_Q2_32).reshape(-1, 10)
     out = torch.empty(raw.shape[0] * 32, dtype=torch.float32, device=dev())
-    Q.moe_dequantize(Q.MOE_FMT_Q2_32, dev_raw, raw.shape[0] * 32, out)
+    # 14 blocks = 140 bytes: the device copy padded to a 16-byte multiple
+    Q.moe_dequantize(Q.MOE_FMT_Q2_32, _padded(raw.reshape(-1)), raw.shape[0] * 32, out)
     ref = OF.dequant_q2(raw).reshape(-1).astype(np.float32)
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
@@ -94,13 +83,7 @@ def _dequant_padded(fmt, raw, n):
 def test_dequant_q3k_hand_blocks_bitexact():
     """Every 6-bit sub-scale (-32..31) at every one of the 16 positions, with
     d from subnormal to the largest finite and negative."""
-    blocks = []
-    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
-        for base in (-32, -16, 0, 16):
-            s = [base + j for j in range(16)]
-            blocks.append(OF.pack_q3k_block(d_bits, s, [i % 8 for i in range(256)]))
-            blocks.append(OF.pack_q3k_block(d_bits, s[::-1], [7 - (i * 5) % 8 for i in range(256)]))
-    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, OF.Q3K_BLOCK_BYTES)
+    raw = _hand_blocks(Q.MOE_FMT_Q3K256).reshape(-1, OF.Q3K_BLOCK_BYTES)
     got = _dequant_padded(Q.MOE_FMT_Q3K256, raw, raw.shape[0] * 256)
     ref = OF.dequant_q3k(raw).reshape(-1).astype(np.float32)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
@@ -108,13 +91,7 @@ def test_dequant_q3k_hand_blocks_bitexact():
 
 def test_dequant_nl4s_hand_blocks_bitexact():
     """Every 6-bit sub-scale at every one of the 8 positions, every table entry."""
-    blocks = []
-    for d_bits in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
-        for base in range(-32, 32, 8):
-            s = [base + j for j in range(8)]
-            blocks.append(OF.pack_nl4s_block(d_bits, s, [i % 16 for i in range(256)]))
-            blocks.append(OF.pack_nl4s_block(d_bits, s[::-1], [15 - (i * 7) % 16 for i in range(256)]))
-    raw = np.frombuffer(b"".join(blocks), dtype=np.uint8).reshape(-1, OF.NL4S_BLOCK_BYTES)
+    raw = _hand_blocks(Q.MOE_FMT_NL4S256).reshape(-1, OF.NL4S_BLOCK_BYTES)
     got = _dequant_padded(Q.MOE_FMT_NL4S256, raw, raw.shape[0] * 256)
     ref = OF.dequant_nl4s(raw).reshape(-1).astype(np.float32)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
