@@ -313,8 +313,8 @@ moe_status moe_dequantize(int32_t fmt, const void* blocks, int64_t n_weights, fl
  *                       for |d| <= 32752, +-inf for code 0 beyond), Q3K256 (pair
  *                       table times the two exact parts of s, summed, then
  *                       d/128), NL4S256 (the NL4 table in 16 copies, then
- *                       d s/128).  Exact except the NL4_32 fold; a zero weight
- *                       may carry either sign.
+ *                       d s/128).  Exact except the NL4_32 fold and Q2_32
+ *                       beyond its bound; a zero weight may carry either sign.
  * Other formats (or Q2S256, Q2_32, Q3K256, NL4S256 on the bandwidth path):
  * MOE_ERR_FORMAT.  Blocks contiguous and 16-byte aligned, n_weights a
  * positive multiple of the block size; out fp32. */
